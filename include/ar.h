@@ -1,0 +1,192 @@
+/*
+ * ar.h -- C-ABI of the MI355X (gfx950) multi-buffer all-reduce core.
+ *
+ * On one GPU, P simulated rank buffers of bf16 activations live in that GPU's
+ * HBM.  The library sums them element by element with binary32 accumulation
+ * in a fixed schedule order and writes bf16 results.  Every entry point
+ * launches hand-written HIP kernels on the caller's stream and returns at
+ * once; nothing here synchronises, allocates or copies between host and
+ * device.
+ *
+ * Pages cited (titles as printed on the pages):
+ *   [TBO-AR] "[DSV4] perf(tbo): overlap pure-TP all_reduce on TBO + Delay TP"
+ *   [CAR]    "fix(custom_all_reduce): use SYSTEM scope + ACQUIRE ordering for
+ *             cross-device signal loads"
+ *   [NVRAR]  "Technical Summary: Understanding and Improving Communication
+ *             Performance in Multi-node LLM Inference"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 data is passed as raw 16-bit patterns; payload words as uint64.
+ * - Every data pointer is a DEVICE pointer on the current HIP device and must
+ *   be 16-byte aligned (AR_ERR_ALIGN otherwise).  Pointer arrays (ins, outs,
+ *   in_words, ...) are HOST arrays of device pointers; the library copies the
+ *   pointers into kernel arguments, so the host arrays may be freed on return.
+ * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ * - The caller owns every buffer.  The library keeps no pointer after return.
+ * - All argument checks happen before any launch: an error return means no
+ *   work was queued.  n == 0 queues nothing and returns AR_OK.
+ * - Aliasing: an output may be exactly the same buffer as an input (in
+ *   place); any partial overlap between an output and another buffer, or
+ *   between two outputs, is AR_ERR_ALIAS.  Inputs may alias each other.
+ * - Numerics of every sum: binary32 round-to-nearest-even additions,
+ *   subnormals kept, no fused multiply-add, ranks added in order 0..P-1
+ *   starting from rank 0's value; one bf16 rounding (nearest, ties to even)
+ *   at the end; any NaN result is written as 0x7FC0.  The pages fix only
+ *   that the models run in bf16 ([NVRAR] Methodology 1, "Models"); this
+ *   accumulation order and rounding are this library's stated reading.
+ * - Thread safety: every entry point may be called concurrently from several
+ *   host threads on different streams.  The only global state is a per-device
+ *   attribute cache filled once under a lock (lazy initialisation raced by two
+ *   ubatch threads is the hazard [TBO-AR] review comments describe).
+ */
+#ifndef AR_H_
+#define AR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define AR_OK               0
+#define AR_ERR_INVALID     -1  /* NULL pointer, P out of range, bad size/split */
+#define AR_ERR_ALIGN       -2  /* a data pointer is not 16-byte aligned        */
+#define AR_ERR_ALIAS       -3  /* partial overlap between buffers              */
+#define AR_ERR_UNSUPPORTED -4  /* e.g. recursive doubling with P not 2^k       */
+#define AR_ERR_HIP         -5  /* a HIP runtime call or kernel launch failed   */
+
+#define AR_MAX_RANKS 8         /* simulated ranks per call: 1..8               */
+
+/* ubatch variants */
+#define AR_VARIANT_ONESHOT  0
+#define AR_VARIANT_2STAGE   1
+
+/* recursive-doubling flags */
+#define AR_RD_STAGED        1  /* one launch per exchange step via a mailbox   */
+#define AR_RD_FP32_CARRY    2  /* keep binary32 partials between steps (fused) */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* ar_status_str(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int ar_version(void);
+
+/*
+ * One-shot reduce.  out[i] = rn(((x_0[i] + x_1[i]) + ...) + x_{P-1}[i]).
+ * The single-stage counterpart of the two-stage kernel of [CAR] ("Root
+ * cause"/"Changes" 3): one rank reads every rank's buffer and sums; one
+ * output buffer.
+ *   ins    host array of P device pointers, each n bf16 values
+ *   P      1..AR_MAX_RANKS (P == 1 copies)
+ *   out    device buffer of n bf16; may equal one of ins[] exactly
+ *   n      elements per buffer (any n >= 0; no multiple-of-8 requirement)
+ * Errors: AR_ERR_INVALID, AR_ERR_ALIGN, AR_ERR_ALIAS, AR_ERR_HIP.
+ */
+int ar_reduce_oneshot(const void* const* ins, int P, void* out, size_t n, void* stream);
+
+/*
+ * Two-stage reduce ([CAR] "Changes" 3, the 2-stage write-mode kernel; [NVRAR]
+ * Methodology 3, phases 1 "Reduce-Scatter" and 3 "All-Gather").  All-reduce
+ * semantics: every outs[r] receives the same sum as ar_reduce_oneshot.
+ *   scratch == NULL  fused: each reduced group of 8 elements is stored
+ *                    straight into all P outputs (write mode).
+ *   scratch != NULL  staged: launch 1 reduces shard s (elements
+ *                    [s*S, min(n,(s+1)*S)), S = ceil(ceil(n/8)/P)*8) into
+ *                    scratch; launch 2 copies every shard to all P outputs.
+ *                    scratch holds n bf16, disjoint from every other buffer,
+ *                    and afterwards holds the reduced values.
+ *   outs   host array of P device pointers (n bf16 each); outs[r] may equal
+ *          an input exactly; outputs must be pairwise disjoint.
+ * Errors: as ar_reduce_oneshot.
+ */
+int ar_reduce_2stage(const void* const* ins, void* const* outs, int P, size_t n,
+                     void* scratch, void* stream);
+
+/*
+ * Pack bf16 data into fused 8-byte payload words ([NVRAR] Optimizations,
+ * "Fused Payloads"): words[j] = (uint64)seq << 32 | x[2j+1] << 16 | x[2j].
+ *   x      n bf16 (n must be even: AR_ERR_INVALID otherwise)
+ *   words  n/2 uint64, disjoint from x
+ */
+int ar_pack_fused(const void* x, uint64_t* words, size_t n, uint32_t seq, void* stream);
+
+/*
+ * Unpack payload words and validate their sequence numbers ([NVRAR]
+ * Optimizations, "Sequence-Number Synchronization").  x[2j] and x[2j+1] are
+ * always written from words[j].  Each wavefront checks its 64 lanes' words
+ * against expected_seq with one ballot and updates the counters once:
+ *   d_err[0] += number of words whose high 32 bits != expected_seq
+ *   d_err[1]  = min(d_err[1], index j of the first such word)
+ *   d_err    device array of 2 uint64, 8-byte aligned; initialise it with
+ *            ar_err_init (count 0, first UINT64_MAX).  The library only adds
+ *            and takes minima; read it after the stream has finished.
+ */
+int ar_unpack_fused(const uint64_t* words, void* x, size_t n, uint32_t expected_seq,
+                    uint64_t* d_err, void* stream);
+
+/*
+ * Recursive-doubling combine over P = 2, 4 or 8 payload buffers ([NVRAR]
+ * Methodology 3, phase 2 "Inter-node Recursive-Doubling", and Optimizations
+ * "Fused Payloads" / "Sequence-Number Synchronization").
+ * Step k = 0..L-1 (L = log2 P): rank r combines with partner r XOR 2^k.  The
+ * received payload must carry seq0 + k; the combined payload carries
+ * seq0 + k + 1 (uint32, wrapping).  Default (round each step): the exchanged
+ * partial is the bf16 payload, so each combine is rn(f(own) + f(partner)).
+ * All P outputs come out bitwise identical (binary32 addition commutes).
+ *   in_words, out_words  host arrays of P device pointers, n/2 words each;
+ *                        out_words[r] may equal in_words[q] exactly
+ *   n        bf16 elements per rank (even)
+ *   flags    0: fused -- one launch computes every step in registers.
+ *            AR_RD_STAGED: one launch per step; intermediate payloads go
+ *              through `mailbox`: P*(L-1)*Ws words with Ws = n/2 rounded up
+ *              to even (each rank's slot stays 16-byte aligned), disjoint
+ *              from all other buffers; may be NULL when P == 2.
+ *            AR_RD_FP32_CARRY (fused only): binary32 partials between steps,
+ *              one rounding at the end (the tree order, reordered relative
+ *              to the sequential sum).
+ *   d_err    as ar_unpack_fused: d_err[0] counts received words whose
+ *            sequence number is wrong; d_err[1] = min over them of
+ *            (k*P + q)*(n/2) + j, q the rank whose payload was received.
+ * Errors: AR_ERR_UNSUPPORTED for P not in {2,4,8} or FP32_CARRY with STAGED,
+ *         AR_ERR_INVALID for odd n or a missing mailbox, plus the common ones.
+ */
+int ar_rd_schedule(const uint64_t* const* in_words, uint64_t* const* out_words, int P,
+                   size_t n, uint32_t seq0, uint64_t* mailbox, int flags, uint64_t* d_err,
+                   void* stream);
+
+/*
+ * Two-stream chunked ubatch reduce ([TBO-AR] pull request overview: the TP
+ * all-reduce of each ubatch runs on its own stream so it overlaps the partner
+ * ubatch's compute; [NVRAR] Optimizations, "Chunked Non-blocking
+ * Communication").  Each rank buffer is a row-major [rows x hidden] bf16
+ * matrix.  Rows are split into n_ubatch ubatches (ubatch_rows == NULL: equal
+ * split, remainder to the last; otherwise the counts, which must sum to
+ * rows).  Ubatch u is reduced on streams[u] in ascending chunks of
+ * chunk_bytes of every rank buffer; a chunk is the unit that workgroups are
+ * assigned to, and chunks are dispatched in ascending order.
+ *   variant  AR_VARIANT_2STAGE: all P outputs; AR_VARIANT_ONESHOT: outs[0]
+ *            only (outs[1..] ignored, may be NULL).
+ *   chunk_bytes  > 0, a multiple of 16.
+ *   streams  host array of n_ubatch hipStream_t (entries may be NULL);
+ *            the caller orders them against other work with events.
+ *   n_ubatch 1..16.
+ * Results are identical to ar_reduce_oneshot for any split and chunk size.
+ */
+int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t rows,
+                     size_t hidden, int n_ubatch, const size_t* ubatch_rows,
+                     size_t chunk_bytes, int variant, void* const* streams);
+
+/*
+ * Initialise an error record for ar_unpack_fused / ar_rd_schedule on
+ * `stream`: d_err[0] = 0, d_err[1] = UINT64_MAX.  Uses a one-thread kernel,
+ * not a memset, so it may be recorded in a HIP graph.
+ */
+int ar_err_init(uint64_t* d_err, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AR_H_ */

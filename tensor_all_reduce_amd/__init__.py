@@ -1,0 +1,228 @@
+"""MI355X (gfx950) multi-buffer all-reduce core: Python binding of libarcore.
+
+A thin ctypes layer over the C-ABI in ``include/ar.h``.  Every function has
+the C name and only marshals arguments: torch tensors become device
+pointers and element counts, torch streams become ``hipStream_t`` handles.
+All arithmetic runs in the HIP kernels of ``libarcore.so``; there is no
+fallback of any kind.  If the library is missing, every call raises.
+
+bf16 buffers may be passed as ``torch.bfloat16`` or ``torch.int16`` /
+``torch.uint16`` tensors (only the 16-bit patterns matter); payload words as
+``torch.int64`` / ``torch.uint64`` tensors; error records as a 2-element
+64-bit tensor.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+__all__ = [
+    "ARError", "lib", "lib_path", "ar_status_str", "ar_version", "ar_reduce_oneshot",
+    "ar_reduce_2stage", "ar_pack_fused", "ar_unpack_fused", "ar_rd_schedule",
+    "ar_reduce_ubatch", "ar_err_init", "rd_mailbox_words",
+    "AR_OK", "AR_ERR_INVALID", "AR_ERR_ALIGN", "AR_ERR_ALIAS", "AR_ERR_UNSUPPORTED",
+    "AR_ERR_HIP", "AR_MAX_RANKS", "AR_VARIANT_ONESHOT", "AR_VARIANT_2STAGE",
+    "AR_RD_STAGED", "AR_RD_FP32_CARRY",
+]
+
+AR_OK = 0
+AR_ERR_INVALID = -1
+AR_ERR_ALIGN = -2
+AR_ERR_ALIAS = -3
+AR_ERR_UNSUPPORTED = -4
+AR_ERR_HIP = -5
+AR_MAX_RANKS = 8
+AR_VARIANT_ONESHOT = 0
+AR_VARIANT_2STAGE = 1
+AR_RD_STAGED = 1
+AR_RD_FP32_CARRY = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libarcore.so")
+_lib = None
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_u32 = ctypes.c_uint32
+
+
+class ARError(RuntimeError):
+    """A nonzero status from the C-ABI."""
+
+    def __init__(self, code: int, func: str):
+        self.code = code
+        super().__init__(f"{func}: {ar_status_str(code)} ({code})")
+
+
+def lib():
+    """Load libarcore.so from this package directory (raises if absent)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is not built; run __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950)")
+        L = ctypes.CDLL(lib_path)
+        L.ar_status_str.restype = ctypes.c_char_p
+        L.ar_status_str.argtypes = [ctypes.c_int]
+        L.ar_version.restype = ctypes.c_int
+        L.ar_version.argtypes = []
+        L.ar_reduce_oneshot.restype = ctypes.c_int
+        L.ar_reduce_oneshot.argtypes = [ctypes.POINTER(_vp), ctypes.c_int, _vp, _sz, _vp]
+        L.ar_reduce_2stage.restype = ctypes.c_int
+        L.ar_reduce_2stage.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz,
+                                       _vp, _vp]
+        L.ar_pack_fused.restype = ctypes.c_int
+        L.ar_pack_fused.argtypes = [_vp, _vp, _sz, _u32, _vp]
+        L.ar_unpack_fused.restype = ctypes.c_int
+        L.ar_unpack_fused.argtypes = [_vp, _vp, _sz, _u32, _vp, _vp]
+        L.ar_rd_schedule.restype = ctypes.c_int
+        L.ar_rd_schedule.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz,
+                                     _u32, _vp, ctypes.c_int, _vp, _vp]
+        L.ar_reduce_ubatch.restype = ctypes.c_int
+        L.ar_reduce_ubatch.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz,
+                                       _sz, ctypes.c_int, ctypes.POINTER(_sz), _sz, ctypes.c_int,
+                                       ctypes.POINTER(_vp)]
+        L.ar_err_init.restype = ctypes.c_int
+        L.ar_err_init.argtypes = [_vp, _vp]
+        _lib = L
+    return _lib
+
+
+def ar_status_str(code: int) -> str:
+    return lib().ar_status_str(int(code)).decode()
+
+
+def ar_version() -> int:
+    return int(lib().ar_version())
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _check(rc: int, func: str) -> None:
+    if rc != AR_OK:
+        raise ARError(rc, func)
+
+
+def _dev_ptr(t, elem_size: int, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.element_size() != elem_size:
+        raise ValueError(f"{name} must have {elem_size}-byte elements")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr_array(ptrs):
+    arr = (_vp * max(1, len(ptrs)))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def _bufs(ts, elem_size: int, name: str, count: int | None = None):
+    ptrs = []
+    for i, t in enumerate(ts):
+        if t is None:
+            ptrs.append(None)
+            continue
+        if count is not None and t.numel() < count:
+            raise ValueError(f"{name}[{i}] holds {t.numel()} elements, {count} needed")
+        ptrs.append(_dev_ptr(t, elem_size, f"{name}[{i}]"))
+    return ptrs
+
+
+def ar_reduce_oneshot(ins: Sequence, out, n: int | None = None, stream=None) -> None:
+    """out[:n] = sum of ins[p][:n] (binary32 accumulation in rank order, one bf16 rounding)."""
+    n = ins[0].numel() if n is None else int(n)
+    ip = _bufs(ins, 2, "ins", n)
+    (op,) = _bufs([out], 2, "out", n)
+    _check(lib().ar_reduce_oneshot(_ptr_array(ip), len(ip), op, n, _stream(stream)),
+           "ar_reduce_oneshot")
+
+
+def ar_reduce_2stage(ins: Sequence, outs: Sequence, scratch=None, n: int | None = None,
+                     stream=None) -> None:
+    """Every outs[r][:n] = the one-shot sum; scratch given -> staged RS/AG."""
+    n = ins[0].numel() if n is None else int(n)
+    ip = _bufs(ins, 2, "ins", n)
+    op = _bufs(outs, 2, "outs", n)
+    if len(op) != len(ip):
+        raise ValueError("need one output per rank")
+    sp = None if scratch is None else _bufs([scratch], 2, "scratch", n)[0]
+    _check(lib().ar_reduce_2stage(_ptr_array(ip), _ptr_array(op), len(ip), n, sp, _stream(stream)),
+           "ar_reduce_2stage")
+
+
+def ar_pack_fused(x, words, seq: int, n: int | None = None, stream=None) -> None:
+    n = x.numel() if n is None else int(n)
+    (xp,) = _bufs([x], 2, "x", n)
+    (wp,) = _bufs([words], 8, "words", n // 2)
+    _check(lib().ar_pack_fused(xp, wp, n, int(seq) & 0xFFFFFFFF, _stream(stream)), "ar_pack_fused")
+
+
+def ar_unpack_fused(words, x, expected_seq: int, d_err, n: int | None = None, stream=None) -> None:
+    n = x.numel() if n is None else int(n)
+    (wp,) = _bufs([words], 8, "words", n // 2)
+    (xp,) = _bufs([x], 2, "x", n)
+    (ep,) = _bufs([d_err], 8, "d_err", 2)
+    _check(lib().ar_unpack_fused(wp, xp, n, int(expected_seq) & 0xFFFFFFFF, ep, _stream(stream)),
+           "ar_unpack_fused")
+
+
+def rd_mailbox_words(P: int, n: int) -> int:
+    """Mailbox size in payload words for ar_rd_schedule(..., AR_RD_STAGED)."""
+    steps = {2: 1, 4: 2, 8: 3}[P]
+    W = n // 2
+    return P * (steps - 1) * (W + (W & 1))
+
+
+def ar_rd_schedule(in_words: Sequence, out_words: Sequence, seq0: int, d_err, mailbox=None,
+                   flags: int = 0, n: int | None = None, stream=None) -> None:
+    n = 2 * in_words[0].numel() if n is None else int(n)
+    ip = _bufs(in_words, 8, "in_words", n // 2)
+    op = _bufs(out_words, 8, "out_words", n // 2)
+    if len(op) != len(ip):
+        raise ValueError("need one output payload per rank")
+    mp = None
+    if mailbox is not None:
+        (mp,) = _bufs([mailbox], 8, "mailbox", rd_mailbox_words(len(ip), n) if len(ip) in (2, 4, 8) else 0)
+    (ep,) = _bufs([d_err], 8, "d_err", 2)
+    _check(lib().ar_rd_schedule(_ptr_array(ip), _ptr_array(op), len(ip), n, int(seq0) & 0xFFFFFFFF,
+                                mp, int(flags), ep, _stream(stream)), "ar_rd_schedule")
+
+
+def ar_reduce_ubatch(ins: Sequence, outs: Sequence, rows: int, hidden: int, n_ubatch: int = 2,
+                     ubatch_rows: Sequence[int] | None = None, chunk_bytes: int = 1 << 20,
+                     variant: int = AR_VARIANT_2STAGE, streams: Sequence | None = None) -> None:
+    n = int(rows) * int(hidden)
+    ip = _bufs(ins, 2, "ins", n)
+    op = _bufs(outs, 2, "outs", n)
+    if streams is None:
+        streams = [None] * n_ubatch
+    if len(streams) != n_ubatch:
+        raise ValueError("need one stream per ubatch")
+    sp = _ptr_array([_stream(s) for s in streams])
+    ub = None
+    if ubatch_rows is not None:
+        if len(ubatch_rows) != n_ubatch:
+            raise ValueError("need one row count per ubatch")
+        ub = (_sz * n_ubatch)(*[int(r) for r in ubatch_rows])
+    _check(lib().ar_reduce_ubatch(_ptr_array(ip), _ptr_array(op), len(ip), int(rows), int(hidden),
+                                  int(n_ubatch), ub, int(chunk_bytes), int(variant), sp),
+           "ar_reduce_ubatch")
+
+
+def ar_err_init(d_err, stream=None) -> None:
+    (ep,) = _bufs([d_err], 8, "d_err", 2)
+    _check(lib().ar_err_init(ep, _stream(stream)), "ar_err_init")

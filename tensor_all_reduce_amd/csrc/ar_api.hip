@@ -1,0 +1,320 @@
+// C-ABI of the all-reduce core (declared in include/ar.h): argument checks,
+// the per-device attribute cache, tuning knobs, and dispatch to the kernels.
+//
+// Every check runs before the first launch, so an error return never leaves
+// partial work queued.  The only global state is the device cache, filled
+// once per device under a mutex: two host threads (one per ubatch) racing the
+// first call must not both initialise it -- the lazy-initialisation race the
+// review of "[DSV4] perf(tbo): overlap pure-TP all_reduce on TBO + Delay TP"
+// flags for its per-ubatch communicators.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "ar.h"
+#include "ar_internal.hpp"
+
+namespace ar {
+size_t rd_mailbox_stride(size_t n);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxUbatch = 16;
+
+struct DevInfo {
+  bool ready = false;
+  int cus = 0;
+};
+
+struct Tuning {
+  int grid_mult = 4;
+  int nt_loads = 0;
+  int nt_stores = 0;
+};
+
+std::mutex g_mu;
+DevInfo g_dev[kMaxDevices];
+bool g_tuning_ready = false;
+Tuning g_tuning;
+
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  char* end = nullptr;
+  long v = std::strtol(s, &end, 10);
+  if (end == s || v < lo || v > hi) return dflt;
+  return (int)v;
+}
+
+// Resolve the launch policy for the current device: CU count (cached once per
+// device) and the tuning knobs (read once per process):
+//   AR_GRID_MULT   workgroups per CU for grid-stride kernels (1..64)
+//   AR_NT_LOADS    1: non-temporal loads of streamed inputs
+//   AR_NT_STORES   1: non-temporal stores of outputs
+int resolve(ar::Launch* L, void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_tuning_ready) {
+    g_tuning.grid_mult = env_int("AR_GRID_MULT", g_tuning.grid_mult, 1, 64);
+    g_tuning.nt_loads = env_int("AR_NT_LOADS", g_tuning.nt_loads, 0, 1);
+    g_tuning.nt_stores = env_int("AR_NT_STORES", g_tuning.nt_stores, 0, 1);
+    g_tuning_ready = true;
+  }
+  DevInfo& d = g_dev[dev];
+  if (!d.ready) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return AR_ERR_HIP;
+    d.cus = cus;
+    d.ready = true;
+  }
+  L->cus = d.cus;
+  L->grid_mult = g_tuning.grid_mult;
+  L->nt_loads = g_tuning.nt_loads;
+  L->nt_stores = g_tuning.nt_stores;
+  L->stream = static_cast<hipStream_t>(stream);
+  return AR_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+inline Span span_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+
+inline bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+inline bool same(Span a, Span b) { return a.lo == b.lo && a.hi == b.hi; }
+
+// An output may coincide exactly with an input; any other overlap with an
+// input is a partial alias.  Outputs may not overlap each other at all.
+int check_outputs(const Span* ins, int nin, const Span* outs, int nout) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlap(outs[o], ins[i]) && !same(outs[o], ins[i])) return AR_ERR_ALIAS;
+    for (int q = o + 1; q < nout; ++q)
+      if (overlap(outs[o], outs[q])) return AR_ERR_ALIAS;
+  }
+  return AR_OK;
+}
+
+int check_disjoint(Span s, const Span* others, int k) {
+  for (int i = 0; i < k; ++i)
+    if (overlap(s, others[i])) return AR_ERR_ALIAS;
+  return AR_OK;
+}
+
+bool mul_overflows(size_t a, size_t b) { return a != 0 && b > (~(size_t)0) / a; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? AR_OK : AR_ERR_HIP; }
+
+int check_ranks(const void* const* ins, int P, size_t n, ar::InPtrs* in, Span* spans) {
+  if (!ins || P < 1 || P > AR_MAX_RANKS) return AR_ERR_INVALID;
+  if (mul_overflows(n, 2)) return AR_ERR_INVALID;
+  for (int p = 0; p < P; ++p) {
+    if (!ins[p]) return AR_ERR_INVALID;
+    if (!aligned16(ins[p])) return AR_ERR_ALIGN;
+    in->p[p] = ins[p];
+    spans[p] = span_of(ins[p], n * 2);
+  }
+  return AR_OK;
+}
+
+int check_err(const uint64_t* d_err) {
+  if (!d_err) return AR_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(d_err) & 7u) return AR_ERR_ALIGN;
+  return AR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ar_status_str(int status) {
+  switch (status) {
+    case AR_OK: return "AR_OK";
+    case AR_ERR_INVALID: return "AR_ERR_INVALID: invalid argument";
+    case AR_ERR_ALIGN: return "AR_ERR_ALIGN: pointer not 16-byte aligned";
+    case AR_ERR_ALIAS: return "AR_ERR_ALIAS: buffers partially overlap";
+    case AR_ERR_UNSUPPORTED: return "AR_ERR_UNSUPPORTED: unsupported configuration";
+    case AR_ERR_HIP: return "AR_ERR_HIP: HIP runtime or launch failure";
+    default: return "AR_ERR_UNKNOWN";
+  }
+}
+
+int ar_version(void) { return 10000; }
+
+int ar_reduce_oneshot(const void* const* ins, int P, void* out, size_t n, void* stream) {
+  ar::InPtrs in{};
+  Span si[AR_MAX_RANKS];
+  int rc = check_ranks(ins, P, n, &in, si);
+  if (rc) return rc;
+  if (!out) return AR_ERR_INVALID;
+  if (!aligned16(out)) return AR_ERR_ALIGN;
+  const Span so = span_of(out, n * 2);
+  if ((rc = check_outputs(si, P, &so, 1))) return rc;
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  return hip_status(ar::launch_oneshot(L, in, P, out, n));
+}
+
+int ar_reduce_2stage(const void* const* ins, void* const* outs, int P, size_t n, void* scratch,
+                     void* stream) {
+  ar::InPtrs in{};
+  ar::OutPtrs out{};
+  Span si[AR_MAX_RANKS], so[AR_MAX_RANKS];
+  int rc = check_ranks(ins, P, n, &in, si);
+  if (rc) return rc;
+  if (!outs) return AR_ERR_INVALID;
+  for (int p = 0; p < P; ++p) {
+    if (!outs[p]) return AR_ERR_INVALID;
+    if (!aligned16(outs[p])) return AR_ERR_ALIGN;
+    out.p[p] = outs[p];
+    so[p] = span_of(outs[p], n * 2);
+  }
+  if ((rc = check_outputs(si, P, so, P))) return rc;
+  if (scratch) {
+    if (!aligned16(scratch)) return AR_ERR_ALIGN;
+    const Span ss = span_of(scratch, n * 2);
+    if ((rc = check_disjoint(ss, si, P)) || (rc = check_disjoint(ss, so, P))) return rc;
+  }
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  if (scratch) return hip_status(ar::launch_2stage_staged(L, in, out, P, n, scratch));
+  return hip_status(ar::launch_2stage_fused(L, in, out, P, n));
+}
+
+int ar_pack_fused(const void* x, uint64_t* words, size_t n, uint32_t seq, void* stream) {
+  if (!x || !words || (n & 1u) || mul_overflows(n, 4)) return AR_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(words)) return AR_ERR_ALIGN;
+  if (overlap(span_of(x, n * 2), span_of(words, n * 4))) return AR_ERR_ALIAS;
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  int rc = resolve(&L, stream);
+  if (rc) return rc;
+  return hip_status(ar::launch_pack(L, x, words, n, seq));
+}
+
+int ar_unpack_fused(const uint64_t* words, void* x, size_t n, uint32_t expected_seq, uint64_t* d_err,
+                    void* stream) {
+  if (!x || !words || (n & 1u) || mul_overflows(n, 4)) return AR_ERR_INVALID;
+  int rc = check_err(d_err);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(words)) return AR_ERR_ALIGN;
+  const Span sx = span_of(x, n * 2), sw = span_of(words, n * 4), se = span_of(d_err, 16);
+  if (overlap(sx, sw) || overlap(se, sx) || overlap(se, sw)) return AR_ERR_ALIAS;
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  return hip_status(ar::launch_unpack(L, words, x, n, expected_seq, d_err));
+}
+
+int ar_rd_schedule(const uint64_t* const* in_words, uint64_t* const* out_words, int P, size_t n,
+                   uint32_t seq0, uint64_t* mailbox, int flags, uint64_t* d_err, void* stream) {
+  if (!in_words || !out_words || (n & 1u) || mul_overflows(n, 4)) return AR_ERR_INVALID;
+  if (flags & ~(AR_RD_STAGED | AR_RD_FP32_CARRY)) return AR_ERR_INVALID;
+  if (P != 2 && P != 4 && P != 8) return AR_ERR_UNSUPPORTED;
+  const bool staged = (flags & AR_RD_STAGED) != 0;
+  if (staged && (flags & AR_RD_FP32_CARRY)) return AR_ERR_UNSUPPORTED;
+  int rc = check_err(d_err);
+  if (rc) return rc;
+  const int steps = P == 2 ? 1 : (P == 4 ? 2 : 3);
+  ar::WordIn in{};
+  ar::WordOut out{};
+  Span si[AR_MAX_RANKS], so[AR_MAX_RANKS];
+  for (int p = 0; p < P; ++p) {
+    if (!in_words[p] || !out_words[p]) return AR_ERR_INVALID;
+    if (!aligned16(in_words[p]) || !aligned16(out_words[p])) return AR_ERR_ALIGN;
+    in.p[p] = in_words[p];
+    out.p[p] = out_words[p];
+    si[p] = span_of(in_words[p], n * 4);
+    so[p] = span_of(out_words[p], n * 4);
+  }
+  if ((rc = check_outputs(si, P, so, P))) return rc;
+  const Span se = span_of(d_err, 16);
+  if ((rc = check_disjoint(se, si, P)) || (rc = check_disjoint(se, so, P))) return rc;
+  if (staged && steps > 1) {
+    if (!mailbox) return AR_ERR_INVALID;
+    if (!aligned16(mailbox)) return AR_ERR_ALIGN;
+    const size_t words = (size_t)P * (size_t)(steps - 1) * ar::rd_mailbox_stride(n);
+    const Span sm = span_of(mailbox, words * 8);
+    if ((rc = check_disjoint(sm, si, P)) || (rc = check_disjoint(sm, so, P)) ||
+        (rc = check_disjoint(sm, &se, 1)))
+      return rc;
+  }
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  if (staged) return hip_status(ar::launch_rd_staged(L, in, out, P, n, seq0, mailbox, d_err));
+  return hip_status(
+      ar::launch_rd_fused(L, in, out, P, n, seq0, (flags & AR_RD_FP32_CARRY) ? 1 : 0, d_err));
+}
+
+int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t rows, size_t hidden,
+                     int n_ubatch, const size_t* ubatch_rows, size_t chunk_bytes, int variant,
+                     void* const* streams) {
+  if (variant != AR_VARIANT_ONESHOT && variant != AR_VARIANT_2STAGE) return AR_ERR_INVALID;
+  if (n_ubatch < 1 || n_ubatch > kMaxUbatch || !streams) return AR_ERR_INVALID;
+  if (chunk_bytes == 0 || (chunk_bytes & 15u)) return AR_ERR_INVALID;
+  if (mul_overflows(rows, hidden)) return AR_ERR_INVALID;
+  const size_t n = rows * hidden;
+  ar::InPtrs in{};
+  ar::OutPtrs out{};
+  Span si[AR_MAX_RANKS], so[AR_MAX_RANKS];
+  int rc = check_ranks(ins, P, n, &in, si);
+  if (rc) return rc;
+  if (!outs) return AR_ERR_INVALID;
+  const int nout = variant == AR_VARIANT_2STAGE ? P : 1;
+  for (int p = 0; p < nout; ++p) {
+    if (!outs[p]) return AR_ERR_INVALID;
+    if (!aligned16(outs[p])) return AR_ERR_ALIGN;
+    out.p[p] = outs[p];
+    so[p] = span_of(outs[p], n * 2);
+  }
+  if ((rc = check_outputs(si, P, so, nout))) return rc;
+  size_t split[kMaxUbatch];
+  size_t total = 0;
+  for (int u = 0; u < n_ubatch; ++u) {
+    if (ubatch_rows) split[u] = ubatch_rows[u];
+    else split[u] = (u == n_ubatch - 1) ? rows - total : rows / (size_t)n_ubatch;
+    if (split[u] > rows - total) return AR_ERR_INVALID;
+    total += split[u];
+  }
+  if (total != rows) return AR_ERR_INVALID;
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, nullptr))) return rc;
+  const size_t chunk = chunk_bytes / 2;
+  size_t row0 = 0;
+  for (int u = 0; u < n_ubatch; ++u) {
+    const size_t e0 = row0 * hidden, e1 = (row0 + split[u]) * hidden;
+    row0 += split[u];
+    if (e1 == e0) continue;
+    L.stream = static_cast<hipStream_t>(streams[u]);
+    rc = hip_status(ar::launch_chunked(L, in, out, P, e0, e1, chunk, nout > 1 ? 1 : 0));
+    if (rc) return rc;
+  }
+  return AR_OK;
+}
+
+int ar_err_init(uint64_t* d_err, void* stream) {
+  int rc = check_err(d_err);
+  if (rc) return rc;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  return hip_status(ar::launch_err_init(L, d_err));
+}
+
+}  // extern "C"

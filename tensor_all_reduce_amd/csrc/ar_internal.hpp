@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI layer (ar_api.hip) and the kernel
+// translation units (ar_reduce.hip, ar_fused.hip).  Not installed; the public
+// boundary is include/ar.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ar.h"
+
+namespace ar {
+
+// Launch policy for one call, resolved by the API layer from the per-device
+// cache and the tuning environment (read once).
+struct Launch {
+  int cus;          // compute units on the current device
+  int grid_mult;    // persistent grid = cus * grid_mult workgroups (grid-stride kernels)
+  int nt_loads;     // 1: non-temporal vector loads for streamed inputs
+  int nt_stores;    // 1: non-temporal vector stores for outputs
+  hipStream_t stream;
+};
+
+// Pointer bundles passed to kernels by value (kernel arguments), so no
+// device-side pointer table and no host->device copy is needed per call.
+struct InPtrs { const void* p[AR_MAX_RANKS]; };
+struct OutPtrs { void* p[AR_MAX_RANKS]; };
+struct WordIn { const uint64_t* p[AR_MAX_RANKS]; };
+struct WordOut { uint64_t* p[AR_MAX_RANKS]; };
+
+hipError_t launch_oneshot(const Launch& L, const InPtrs& in, int P, void* out, size_t n);
+hipError_t launch_2stage_fused(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
+                               size_t n);
+hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
+                                size_t n, void* scratch);
+// Chunked reduce of elements [e0, e1) of every buffer, chunk-major workgroups.
+hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
+                          size_t e0, size_t e1, size_t chunk_elems, int two_stage);
+
+hipError_t launch_pack(const Launch& L, const void* x, uint64_t* w, size_t n, uint32_t seq);
+hipError_t launch_unpack(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,
+                         uint64_t* d_err);
+hipError_t launch_rd_fused(const Launch& L, const WordIn& in, const WordOut& out, int P,
+                           size_t n, uint32_t seq0, int fp32_carry, uint64_t* d_err);
+hipError_t launch_rd_staged(const Launch& L, const WordIn& in, const WordOut& out, int P,
+                            size_t n, uint32_t seq0, uint64_t* mailbox, uint64_t* d_err);
+hipError_t launch_err_init(const Launch& L, uint64_t* d_err);
+
+}  // namespace ar

@@ -1,0 +1,164 @@
+"""C-ABI host logic on the CPU: the library loads, exports every symbol that
+include/ar.h declares, and rejects bad arguments before any HIP call.
+
+No call here reaches a kernel launch: every call either fails validation or
+has n == 0, both of which return before the library touches the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tensor_all_reduce_amd as tar
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ar.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ar_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["ar_reduce_oneshot", "ar_reduce_2stage", "ar_pack_fused", "ar_unpack_fused",
+                 "ar_rd_schedule", "ar_reduce_ubatch", "ar_status_str", "ar_version", "ar_err_init"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(tar.lib_path), "build first: python __graft_entry__.py"
+    out = subprocess.run(["nm", "-D", "--defined-only", tar.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(ar_[a-z0-9_]+)$", out, flags=re.M))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    L = tar.lib()
+    for f in declared_functions():
+        assert hasattr(L, f)
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    for name, val in re.findall(r"#define\s+(AR_[A-Z0-9_]+)\s+(-?\d+)", src):
+        assert getattr(tar, name) == int(val), name
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-fsyntax-only", "-Wall", "-Werror", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings_and_version():
+    assert tar.ar_status_str(0) == "AR_OK"
+    for code in (-1, -2, -3, -4, -5):
+        assert tar.ar_status_str(code).startswith("AR_ERR_")
+    assert tar.ar_status_str(123) == "AR_ERR_UNKNOWN"
+    assert tar.ar_version() >= 10000
+
+
+# ---------------------------------------------------------------- validation (no device access)
+
+vp = ctypes.c_void_p
+A = 0x10000000          # fake, 16-byte aligned "device" addresses: never dereferenced
+B = 0x20000000
+C = 0x30000000
+
+
+def arr(*ptrs):
+    return (vp * len(ptrs))(*ptrs)
+
+
+def test_oneshot_validation():
+    L = tar.lib()
+    ins = arr(A, B)
+    assert L.ar_reduce_oneshot(None, 2, C, 8, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_oneshot(ins, 0, C, 8, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_oneshot(arr(*([A] * 9)), 9, C, 8, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_oneshot(ins, 2, None, 8, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_oneshot(arr(A + 2, B), 2, C, 8, None) == tar.AR_ERR_ALIGN
+    assert L.ar_reduce_oneshot(ins, 2, C + 8, 8, None) == tar.AR_ERR_ALIGN
+    # partial overlap of the output with an input
+    assert L.ar_reduce_oneshot(ins, 2, A + 16, 64, None) == tar.AR_ERR_ALIAS
+    # exact in place and n == 0 are accepted without touching the device
+    assert L.ar_reduce_oneshot(ins, 2, A, 0, None) == tar.AR_OK
+    assert L.ar_reduce_oneshot(arr(A, A), 2, C, 0, None) == tar.AR_OK
+
+
+def test_2stage_validation():
+    L = tar.lib()
+    ins = arr(A, B)
+    assert L.ar_reduce_2stage(ins, None, 2, 8, None, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_2stage(ins, arr(C, None), 2, 8, None, None) == tar.AR_ERR_INVALID
+    # two outputs overlapping each other
+    assert L.ar_reduce_2stage(ins, arr(C, C + 16), 2, 64, None, None) == tar.AR_ERR_ALIAS
+    assert L.ar_reduce_2stage(ins, arr(C, C), 2, 64, None, None) == tar.AR_ERR_ALIAS
+    # scratch overlapping an output or input
+    assert L.ar_reduce_2stage(ins, arr(C, C + 4096), 2, 64, C + 32, None) == tar.AR_ERR_ALIAS
+    assert L.ar_reduce_2stage(ins, arr(C, C + 4096), 2, 64, A, None) == tar.AR_ERR_ALIAS
+    assert L.ar_reduce_2stage(ins, arr(C, C + 4096), 2, 64, C + 8200, None) == tar.AR_ERR_ALIGN
+    # in place (outs == ins) is fine
+    assert L.ar_reduce_2stage(ins, arr(A, B), 2, 0, None, None) == tar.AR_OK
+
+
+def test_pack_unpack_validation():
+    L = tar.lib()
+    assert L.ar_pack_fused(A, B, 7, 1, None) == tar.AR_ERR_INVALID           # odd n
+    assert L.ar_pack_fused(A, A + 16, 64, 1, None) == tar.AR_ERR_ALIAS
+    assert L.ar_pack_fused(A + 4, B, 8, 1, None) == tar.AR_ERR_ALIGN
+    assert L.ar_pack_fused(A, B, 0, 1, None) == tar.AR_OK
+    assert L.ar_unpack_fused(A, B, 8, 1, None, None) == tar.AR_ERR_INVALID  # no error record
+    assert L.ar_unpack_fused(A, B, 8, 1, C + 4, None) == tar.AR_ERR_ALIGN
+    assert L.ar_unpack_fused(A, B, 8, 1, A + 8, None) == tar.AR_ERR_ALIAS
+    assert L.ar_unpack_fused(A, B, 0, 1, C, None) == tar.AR_OK
+
+
+def test_rd_validation():
+    L = tar.lib()
+    ins3 = arr(A, A + 0x1000, A + 0x2000)
+    outs3 = arr(B, B + 0x1000, B + 0x2000)
+    assert L.ar_rd_schedule(ins3, outs3, 3, 8, 0, None, 0, C, None) == tar.AR_ERR_UNSUPPORTED
+    ins = arr(*[A + 0x1000 * i for i in range(4)])
+    outs = arr(*[B + 0x1000 * i for i in range(4)])
+    assert L.ar_rd_schedule(ins, outs, 4, 7, 0, None, 0, C, None) == tar.AR_ERR_INVALID
+    assert L.ar_rd_schedule(ins, outs, 4, 8, 0, None, 3, C, None) == tar.AR_ERR_UNSUPPORTED
+    assert L.ar_rd_schedule(ins, outs, 4, 8, 0, None, 8, C, None) == tar.AR_ERR_INVALID
+    assert L.ar_rd_schedule(ins, outs, 4, 8, 0, None, tar.AR_RD_STAGED, C, None) == tar.AR_ERR_INVALID
+    assert L.ar_rd_schedule(ins, outs, 4, 8, 0, A, tar.AR_RD_STAGED, C, None) == tar.AR_ERR_ALIAS
+    assert L.ar_rd_schedule(ins, outs, 4, 8, 0, C - 64, tar.AR_RD_STAGED, C, None) == tar.AR_ERR_ALIAS
+    assert L.ar_rd_schedule(ins, outs, 4, 0, 0, C + 4096, tar.AR_RD_STAGED, C, None) == tar.AR_OK
+    assert L.ar_rd_schedule(ins, ins, 4, 0, 0, None, 0, C, None) == tar.AR_OK   # in place
+
+
+def test_ubatch_validation():
+    L = tar.lib()
+    ins = arr(A, B)
+    outs = arr(C, C + 0x100000)
+    streams = arr(None, None)
+    ub = (ctypes.c_size_t * 2)(3, 3)
+    assert L.ar_reduce_ubatch(ins, outs, 2, 4, 8, 2, ub, 4096, 1, streams) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch(ins, outs, 2, 4, 8, 2, None, 4008, 1, streams) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch(ins, outs, 2, 4, 8, 2, None, 0, 1, streams) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch(ins, outs, 2, 4, 8, 0, None, 4096, 1, streams) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch(ins, outs, 2, 4, 8, 2, None, 4096, 7, streams) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch(ins, outs, 2, 4, 8, 2, None, 4096, 1, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch(ins, arr(C, C + 16), 2, 4, 8, 2, None, 4096, 1, streams) == tar.AR_ERR_ALIAS
+    # one-shot ignores outs[1]
+    assert L.ar_reduce_ubatch(ins, arr(C, None), 2, 0, 8, 2, None, 4096, 0, streams) == tar.AR_OK
+
+
+def test_err_init_validation():
+    L = tar.lib()
+    assert L.ar_err_init(None, None) == tar.AR_ERR_INVALID
+    assert L.ar_err_init(C + 4, None) == tar.AR_ERR_ALIGN
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(tar.ARError) as ei:
+        tar._check(tar.AR_ERR_ALIAS, "ar_reduce_oneshot")
+    assert ei.value.code == tar.AR_ERR_ALIAS

@@ -1,0 +1,423 @@
+"""GPU parity of every hot-path call against the CPU oracle, through the C-ABI.
+
+Matched order (one-shot, two-stage, ubatch vs the sequential oracle; RD vs
+the oracle's RD): bit-exact.  Sequence numbers, mismatch counts and first
+indices: exact.  Small and medium sizes compare every element; the
+full-size configurations compare sampled elements (first/last 4096 plus
+random ones, each computed by the oracle from the gathered inputs) and check
+properties that hold at any size (all outputs identical, variants equal).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_all_reduce_amd as tar
+from tensor_all_reduce_amd import synth
+from gpu_util import (DEV, note, up16, down16, up64, down64, empty16, new_err, err_host, bits16,
+                      sample_indices, gather_ranks, gather)
+
+pytestmark = pytest.mark.gpu
+
+HIDDEN = 8192
+
+
+def check_full(got: torch.Tensor, want: np.ndarray, what: str):
+    g = down16(got)
+    bad = np.nonzero(g != want)[0]
+    assert bad.size == 0, (f"{what}: {bad.size} mismatches, first at {bad[0]}: "
+                           f"got 0x{int(g[bad[0]]):04X} want 0x{int(want[bad[0]]):04X}")
+
+
+# ------------------------------------------------------------ one-shot / two-stage
+
+@pytest.mark.parametrize("P,n", [(2, HIDDEN)] + [(8, T * HIDDEN) for T in (8, 32, 128)])
+def test_decode_configs(P, n):
+    """P=2 [1 x 8192] and P=8 [T x 8192], T in {8, 32, 128}: one-shot,
+    two-stage fused and staged, N(0,1) inputs."""
+    cfg, tag = (1, 0) if P == 2 else (2, n // HIDDEN)
+    xs = synth.rank_buffers("normal", P, n, cfg, tag)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    note(f"oneshot P={P} n={n}")
+    out = empty16(n)
+    tar.ar_reduce_oneshot(ins, out)
+    torch.cuda.synchronize()
+    check_full(out, ref, "oneshot")
+    note(f"2stage fused P={P} n={n}")
+    outs = [empty16(n) for _ in range(P)]
+    tar.ar_reduce_2stage(ins, outs)
+    torch.cuda.synchronize()
+    for o in outs:
+        check_full(o, ref, "2stage fused")
+    note(f"2stage staged P={P} n={n}")
+    outs2 = [empty16(n) for _ in range(P)]
+    scratch = empty16(n)
+    tar.ar_reduce_2stage(ins, outs2, scratch=scratch)
+    torch.cuda.synchronize()
+    check_full(scratch, ref, "staged scratch")
+    for o in outs2:
+        check_full(o, ref, "2stage staged")
+
+
+RAGGED = [1, 2, 7, 8, 9, 15, 17, 255, 1000, 2049, 65536 + 3, 300001, 4 * 1024 * 1024 + 5]
+
+
+@pytest.mark.parametrize("n", RAGGED)
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 8])
+def test_ragged_sizes(P, n):
+    """Sizes that are not multiples of the 8-element group, spanning one
+    partial group up to several grid-stride passes."""
+    xs = synth.rank_buffers("logmag", P, n, 20, n)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    note(f"ragged P={P} n={n}")
+    out = empty16(n)
+    tar.ar_reduce_oneshot(ins, out)
+    outs = [empty16(n) for _ in range(P)]
+    tar.ar_reduce_2stage(ins, outs)
+    outs2 = [empty16(n) for _ in range(P)]
+    tar.ar_reduce_2stage(ins, outs2, scratch=empty16(n))
+    torch.cuda.synchronize()
+    check_full(out, ref, "oneshot")
+    for o in outs + outs2:
+        check_full(o, ref, "2stage")
+
+
+SPECIALS = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80,
+                     0x7FC0, 0x7F81, 0xFFC1, 0x3F80, 0xBF80, 0x4B80, 0xCB80, 0x3B80, 0x3380],
+                    dtype=np.uint16)
+
+
+@pytest.mark.parametrize("P", [2, 3, 8])
+def test_special_values(P):
+    """NaN payloads, infinities, signed zeros, subnormals, values at the
+    overflow edge and absorption cases, densely mixed into the inputs."""
+    n = 200003
+    xs = synth.rank_buffers("logmag", P, n, 21, P)
+    g = np.random.default_rng([22, P])
+    for x in xs:
+        idx = g.choice(n, size=n // 3, replace=False)
+        x[idx] = g.choice(SPECIALS, size=idx.size)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    note(f"special values P={P}")
+    out = empty16(n)
+    tar.ar_reduce_oneshot(ins, out)
+    outs = [empty16(n) for _ in range(P)]
+    tar.ar_reduce_2stage(ins, outs, scratch=empty16(n))
+    torch.cuda.synchronize()
+    check_full(out, ref, "oneshot specials")
+    for o in outs:
+        check_full(o, ref, "2stage specials")
+
+
+def test_exhaustive_pairs_p2():
+    """P=2: every bf16 pattern against 19 special and 45 random partners."""
+    a = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    partners = np.concatenate([SPECIALS, synth.normal(45, 23)])
+    A = np.tile(a, partners.size)
+    Bv = np.repeat(partners, a.size)
+    ref = oracle.reduce_seq([A, Bv])
+    note("exhaustive pairs P=2")
+    out = empty16(A.size)
+    tar.ar_reduce_oneshot([up16(A), up16(Bv)], out)
+    torch.cuda.synchronize()
+    check_full(out, ref, "pairs")
+
+
+def test_in_place():
+    P, n = 8, 123457
+    xs = synth.rank_buffers("normal", P, n, 24)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    note("in-place 2stage fused")
+    tar.ar_reduce_2stage(ins, ins)
+    torch.cuda.synchronize()
+    for t in ins:
+        check_full(t, ref, "in-place fused")
+    ins = [up16(x) for x in xs]
+    note("in-place 2stage staged")
+    tar.ar_reduce_2stage(ins, ins, scratch=empty16(n))
+    torch.cuda.synchronize()
+    for t in ins:
+        check_full(t, ref, "in-place staged")
+    ins = [up16(x) for x in xs]
+    note("in-place oneshot")
+    tar.ar_reduce_oneshot(ins, ins[3])
+    torch.cuda.synchronize()
+    check_full(ins[3], ref, "in-place oneshot")
+
+
+def test_canaries_untouched():
+    """Outputs carved out of larger buffers: the guard bytes around them keep
+    their pattern, so no kernel writes outside [0, n)."""
+    P, n, G = 8, 50001, 4096
+    xs = synth.rank_buffers("normal", P, n, 25)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    pattern = np.int16(0x5A5A)
+    bigs = [torch.full((n + 2 * G,), int(pattern), dtype=torch.int16, device=DEV) for _ in range(P)]
+    outs = [b[G:G + n] for b in bigs]
+    sbig = torch.full((n + 2 * G,), int(pattern), dtype=torch.int16, device=DEV)
+    note("canaries")
+    tar.ar_reduce_2stage(ins, outs, scratch=sbig[G:G + n])
+    tar.ar_reduce_oneshot(ins, outs[0])
+    torch.cuda.synchronize()
+    for b in bigs + [sbig]:
+        h = down16(b)
+        assert np.all(h[:G] == np.uint16(0x5A5A)) and np.all(h[G + n:] == np.uint16(0x5A5A))
+        check_full(b[G:G + n], ref, "canary body")
+
+
+def test_n_zero_is_noop():
+    t = empty16(16)
+    t.fill_(7)
+    note("n=0")
+    tar.ar_reduce_oneshot([t, t], t, n=0)
+    torch.cuda.synchronize()
+    assert np.all(down16(t) == 7)
+
+
+# ------------------------------------------------------------ pack / RD / unpack
+
+def _rd_case(P, n, seq0, kind="normal", cfg=3):
+    xs = synth.rank_buffers(kind, P, n, cfg, P, seq0 & 0xFF)
+    return xs, [oracle.pack(x, seq0) for x in xs]
+
+
+@pytest.mark.parametrize("seq0", [1, 0xFFFFFFFE])
+@pytest.mark.parametrize("P,n", [(8, 128 * HIDDEN), (2, 20002), (4, 65538), (8, 6)])
+def test_pack_rd_unpack(P, n, seq0):
+    """Pack on the GPU, recursive doubling (fused R1, staged R1, fused R2),
+    unpack with validation; payload words, data and counts vs the oracle."""
+    xs, owords = _rd_case(P, n, seq0)
+    L = {2: 1, 4: 2, 8: 3}[P]
+    ins = [up16(x) for x in xs]
+    words = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+    note(f"pack P={P} n={n} seq0={seq0:#x}")
+    for i in range(P):
+        tar.ar_pack_fused(ins[i], words[i], seq0)
+    torch.cuda.synchronize()
+    for i in range(P):
+        assert np.array_equal(down64(words[i]), owords[i])
+    for flags, carry in ((0, False), (tar.AR_RD_STAGED, False), (tar.AR_RD_FP32_CARRY, True)):
+        ref_w, ref_e = oracle.rd(owords, seq0, carry)
+        out = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+        mb = None
+        if flags & tar.AR_RD_STAGED and P > 2:
+            mb = torch.empty(tar.rd_mailbox_words(P, n), dtype=torch.int64, device=DEV)
+        err = new_err()
+        note(f"rd P={P} n={n} flags={flags}")
+        tar.ar_rd_schedule(words, out, seq0, err, mailbox=mb, flags=flags)
+        torch.cuda.synchronize()
+        assert err_host(err) == (int(ref_e[0]), int(ref_e[1])) == (0, 2 ** 64 - 1)
+        for r in range(P):
+            got = down64(out[r])
+            bad = np.nonzero(got != ref_w[r])[0]
+            assert bad.size == 0, f"flags={flags} rank {r}: word {bad[0]} {got[bad[0]]:#x} vs {ref_w[r][bad[0]]:#x}"
+        x = empty16(n)
+        err2 = new_err()
+        note(f"unpack P={P} n={n}")
+        tar.ar_unpack_fused(out[P - 1], x, (seq0 + L) & 0xFFFFFFFF, err2)
+        torch.cuda.synchronize()
+        ox, oe = oracle.unpack(ref_w[P - 1], (seq0 + L) & 0xFFFFFFFF)
+        check_full(x, ox, "unpack")
+        assert err_host(err2) == (int(oe[0]), int(oe[1]))
+
+
+@pytest.mark.parametrize("staged", [False, True])
+def test_rd_error_counts(staged):
+    """Host-forced faults: corrupted sequence numbers in chosen words of
+    chosen ranks are counted exactly and the first index is exact; the data
+    is still combined from the payload bits, as in the oracle."""
+    P, n, seq0 = 8, 128 * HIDDEN, 40
+    xs, owords = _rd_case(P, n, seq0, cfg=31)
+    W = n // 2
+    hits = [(5, 7), (5, W - 1), (2, 1000), (7, 0), (0, W // 2)]
+    for r, j in hits:
+        owords[r][j] = (owords[r][j] & np.uint64(0xFFFFFFFF)) | (np.uint64(seq0 + 9) << np.uint64(32))
+    ref_w, ref_e = oracle.rd(owords, seq0)
+    words = [up64(w) for w in owords]
+    out = [torch.empty(W, dtype=torch.int64, device=DEV) for _ in range(P)]
+    mb = torch.empty(tar.rd_mailbox_words(P, n), dtype=torch.int64, device=DEV) if staged else None
+    err = new_err()
+    note(f"rd faults staged={staged}")
+    tar.ar_rd_schedule(words, out, seq0, err, mailbox=mb, flags=tar.AR_RD_STAGED if staged else 0)
+    torch.cuda.synchronize()
+    assert err_host(err) == (len(hits), min(r * W + j for r, j in hits))
+    assert (int(ref_e[0]), int(ref_e[1])) == err_host(err)
+    for r in range(P):
+        assert np.array_equal(down64(out[r]), ref_w[r])
+
+
+def test_unpack_faults():
+    """Stale payload (previous sequence number), a wrong expected number,
+    and k corrupted words: exact counts and first indices."""
+    n = 2 * HIDDEN * 64 + 6
+    x = synth.normal(n, 32)
+    w = oracle.pack(x, 100)
+    g = np.random.default_rng(33)
+    bad = np.sort(g.choice(w.size, size=77, replace=False))
+    wc = w.copy()
+    wc[bad] ^= np.uint64(1) << np.uint64(40)
+    for words, expect, count, first in ((w, 100, 0, 2 ** 64 - 1), (oracle.pack(x, 99), 100, w.size, 0),
+                                        (w, 101, w.size, 0), (wc, 100, 77, int(bad[0]))):
+        out = empty16(n)
+        err = new_err()
+        note(f"unpack fault expect={expect} count={count}")
+        tar.ar_unpack_fused(up64(words), out, expect, err)
+        torch.cuda.synchronize()
+        assert err_host(err) == (count, first)
+        check_full(out, x, "unpack data")
+    # counters accumulate across calls and keep the minimum index
+    err = new_err()
+    out = empty16(n)
+    tar.ar_unpack_fused(up64(wc), out, 100, err)
+    tar.ar_unpack_fused(up64(oracle.pack(x, 99)), out, 100, err)
+    torch.cuda.synchronize()
+    assert err_host(err) == (77 + w.size, 0)
+
+
+# ------------------------------------------------------------ ubatch
+
+@pytest.mark.parametrize("chunk_bytes", [1 << 20, 65536, 4096 + 16, 16])
+@pytest.mark.parametrize("split", [None, [3, 61], [64, 0]])
+def test_ubatch_small(chunk_bytes, split):
+    P, rows, hidden = 8, 64, 1000
+    n = rows * hidden
+    xs = synth.rank_buffers("logmag", P, n, 5, rows)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    outs = [empty16(n) for _ in range(P)]
+    s = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in s:
+        st.wait_stream(torch.cuda.current_stream())
+    note(f"ubatch rows={rows} hidden={hidden} chunk={chunk_bytes} split={split}")
+    tar.ar_reduce_ubatch(ins, outs, rows, hidden, 2, split, chunk_bytes, tar.AR_VARIANT_2STAGE, s)
+    one = [empty16(n)] + [None] * (P - 1)
+    tar.ar_reduce_ubatch(ins, one, rows, hidden, 2, split, chunk_bytes, tar.AR_VARIANT_ONESHOT, s)
+    torch.cuda.synchronize()
+    for o in outs:
+        check_full(o, ref, "ubatch 2stage")
+    check_full(one[0], ref, "ubatch oneshot")
+
+
+def test_ubatch_many_ubatches_hidden_not_multiple_of_8():
+    P, rows, hidden = 5, 37, 1001
+    n = rows * hidden
+    xs = synth.rank_buffers("normal", P, n, 6)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    outs = [empty16(n) for _ in range(P)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    note("ubatch 3 ubatches hidden=1001")
+    tar.ar_reduce_ubatch(ins, outs, rows, hidden, 3, None, 4096, tar.AR_VARIANT_2STAGE, streams)
+    torch.cuda.synchronize()
+    for o in outs:
+        check_full(o, ref, "ubatch odd hidden")
+
+
+# ------------------------------------------------------------ concurrency
+
+def test_two_threads_two_streams():
+    """Two host threads, each with its own stream, call concurrently (the
+    first calls race the library's one-time device initialisation)."""
+    import threading
+    P, n = 8, 333333
+    xs = synth.rank_buffers("normal", P, n, 7)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    results = {}
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [empty16(n) for _ in range(P)]
+                for _ in range(20):
+                    tar.ar_reduce_2stage(ins, outs, stream=s)
+                    tar.ar_reduce_oneshot(ins, outs[0], stream=s)
+                s.synchronize()
+                results[k] = [down16(o) for o in outs]
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    torch.cuda.synchronize()
+    note("two threads")
+    th = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    for k in range(2):
+        for o in results[k]:
+            assert np.array_equal(o, ref)
+
+
+# ------------------------------------------------------------ full-size configurations
+
+def _check_sampled(ins, outs, n, seed, what):
+    idx = sample_indices(n, 1 << 16, seed)
+    want = oracle.reduce_seq(gather_ranks(ins, idx))
+    for r, o in enumerate(outs):
+        got = gather(o, idx)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"{what} out {r}: element {idx[bad[0]]} got {got[bad[0]]:#x} want {want[bad[0]]:#x}"
+
+
+def test_prefill_2stage_full_size():
+    """P=8 [16384 x 8192] per rank (256 MiB per buffer), N(0,1): fused and
+    staged two-stage; sampled elements vs the oracle; all outputs identical;
+    staged == fused everywhere."""
+    P, n = 8, 16384 * HIDDEN
+    note("prefill full size: generate")
+    ins = [bits16(t) for t in synth.device_rank_buffers("normal", P, n, 4)]
+    outs = [empty16(n) for _ in range(P)]
+    note("prefill full size: 2stage fused")
+    tar.ar_reduce_2stage(ins, outs)
+    torch.cuda.synchronize()
+    _check_sampled(ins, outs[:1] + outs[-1:], n, 41, "prefill fused")
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    scratch = empty16(n)
+    outs2 = [empty16(n) for _ in range(P)]
+    note("prefill full size: 2stage staged")
+    tar.ar_reduce_2stage(ins, outs2, scratch=scratch)
+    torch.cuda.synchronize()
+    for o in outs2:
+        assert torch.equal(o, outs[0])
+    assert torch.equal(scratch, outs[0])
+    one = empty16(n)
+    note("prefill full size: oneshot")
+    tar.ar_reduce_oneshot(ins, one)
+    torch.cuda.synchronize()
+    assert torch.equal(one, outs[0])
+    del ins, outs, outs2, scratch, one
+    torch.cuda.empty_cache()
+
+
+def test_ubatch_full_size():
+    """P=8 [16384 x 16384] per rank split into two 8192-row ubatches on two
+    streams, 1 MiB chunks, log-uniform magnitudes in [2^-8, 2^8] with random
+    signs; sampled elements vs the oracle, all outputs identical."""
+    P, rows, hidden = 8, 16384, 16384
+    n = rows * hidden
+    note("ubatch full size: generate")
+    ins = [bits16(t) for t in synth.device_rank_buffers("logmag", P, n, 5)]
+    outs = [empty16(n) for _ in range(P)]
+    s = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in s:
+        st.wait_stream(torch.cuda.current_stream())
+    note("ubatch full size: reduce")
+    tar.ar_reduce_ubatch(ins, outs, rows, hidden, 2, None, 1 << 20, tar.AR_VARIANT_2STAGE, s)
+    torch.cuda.synchronize()
+    _check_sampled(ins, outs[:1] + outs[-1:], n, 51, "ubatch full")
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    del ins, outs
+    torch.cuda.empty_cache()
