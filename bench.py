@@ -1,0 +1,407 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X all-reduce core (one GPU).
+
+One step = one pass of every hot-path call over one batch: P = 8 simulated
+rank buffers of bf16 [16384 x 8192] (the 16k-token prefill hidden state,
+256 MiB per buffer), N(0,1) values drawn on the GPU from a seeded generator:
+
+  oneshot   ar_reduce_oneshot            reads 8 buffers, writes 1
+  2stage    ar_reduce_2stage (fused)     reads 8, writes 8
+  pack      ar_pack_fused x 8            bf16 -> fused payload words (seq s)
+  rd        ar_rd_schedule (fused, R1)   3 recursive-doubling steps, 8 payloads
+  unpack    ar_unpack_fused x 8          payload -> bf16, seq checked (s + 3)
+  ubatch    ar_reduce_ubatch             2 ubatches of 8192 rows, 2 streams, 1 MiB chunks
+
+`value` = credited bytes of the step / step time (GB/s, 1e9 B/s); credited
+bytes count each input read once and each output written once (no scratch).
+Inputs are resident in HBM before the timed region.
+
+Also reported (not part of `value`): per-call latency of one-shot and
+two-stage at 128 KiB / 512 KiB / 2 MiB per buffer (native timing loop, no
+Python in the loop), the staged two-stage at the prefill size, the ubatch
+reduce at its own [16384 x 16384] shape, attainable copy bandwidth, and the
+CPU oracle on a bounded sample of the same step (`cpu_baseline`).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0            # MI355X published HBM3E bandwidth, 8 TB/s
+P, ROWS, HIDDEN = 8, 16384, 8192
+UB_ROWS, UB_HIDDEN = 16384, 16384
+CHUNK_BYTES = 1 << 20
+METRIC = "achieved HBM GB/s (% of peak) per reduction; µs latency at 128KB–2MB"
+# the sources a kernel's counters depend on (code and launch shapes)
+KERNEL_SOURCES = ["tensor_all_reduce_amd/csrc/ar_device.hpp", "tensor_all_reduce_amd/csrc/ar_reduce.hip",
+                  "tensor_all_reduce_amd/csrc/ar_fused.hip", "tensor_all_reduce_amd/csrc/ar_api.hip"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps (for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after the steps, run 3 plain copies of exactly 1 GiB (counter calibration)")
+    return ap.parse_args()
+
+
+def sha256_files(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(row: str, sources):
+    """HBM bytes per launch of a row's kernel from the committed rocprofv3
+    counter summary (profiles/traffic_prefill_step.txt, "key: value" lines),
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_prefill_step.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != sha256_files(sources):
+        return None
+    try:
+        return float(rec[f"{row}.hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        msg = (f"bench.py measures one GPU only (got --gpus {args.gpus}): the simulated ranks live "
+               "in one GPU's HBM and this build runs no collective between GPUs")
+        print(msg, file=sys.stderr)
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tensor_all_reduce_amd as tar
+    from tensor_all_reduce_amd import synth
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible")
+    tar.lib()                                  # raises if the HIP library is missing
+    blib = ctypes.CDLL(os.path.join(ROOT, "tensor_all_reduce_amd", "libarbench.so"))
+    vp = ctypes.c_void_p
+    blib.arb_stream_us.restype = ctypes.c_double
+    blib.arb_stream_us.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                   ctypes.c_size_t, vp, ctypes.c_int, vp]
+    blib.arb_wall_us.restype = ctypes.c_int
+    blib.arb_wall_us.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                 ctypes.c_size_t, vp, ctypes.c_int, vp,
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double)]
+    blib.arb_copy.restype = ctypes.c_int
+    blib.arb_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    main_s = torch.cuda.current_stream()
+    n = ROWS * HIDDEN
+    B = 2 * n
+    W = n // 2
+
+    def e16(m):
+        return torch.empty(m, dtype=torch.int16, device=dev)
+
+    def e64(m):
+        return torch.empty(m, dtype=torch.int64, device=dev)
+
+    log(f"device {props.name}, {props.multi_processor_count} CUs; allocating the prefill batch")
+    ins = [t.view(torch.int16) for t in synth.device_rank_buffers("normal", P, n, 4, dev)]
+    out1 = e16(n)
+    outs = [e16(n) for _ in range(P)]
+    words = [e64(W) for _ in range(P)]
+    rdo = [e64(W) for _ in range(P)]
+    ux = [e16(n) for _ in range(P)]
+    ubo = [e16(n) for _ in range(P)]
+    err = e64(2)
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    rows = ["oneshot", "2stage", "pack", "rd", "unpack", "ubatch"]
+    credited = {
+        "oneshot": (P + 1) * B,
+        "2stage": 2 * P * B,
+        "pack": P * (B + 2 * B),
+        "rd": P * 2 * B * 2,
+        "unpack": P * (2 * B + B),
+        "ubatch": 2 * P * B,
+    }
+    launches = {"oneshot": 1, "2stage": 1, "pack": P, "rd": 1, "unpack": P, "ubatch": 2}
+    kernel_of = {"oneshot": "k_reduce<8,1>", "2stage": "k_reduce<8,8>", "pack": "k_pack",
+                 "rd": "k_rd_fused<8,R1>", "unpack": "k_unpack", "ubatch": "k_reduce<8,8> chunked"}
+    step_bytes = sum(credited.values())
+
+    def run_row(name, seq):
+        if name == "oneshot":
+            tar.ar_reduce_oneshot(ins, out1)
+        elif name == "2stage":
+            tar.ar_reduce_2stage(ins, outs)
+        elif name == "pack":
+            for r in range(P):
+                tar.ar_pack_fused(ins[r], words[r], seq)
+        elif name == "rd":
+            tar.ar_err_init(err)
+            tar.ar_rd_schedule(words, rdo, seq, err)
+        elif name == "unpack":
+            for r in range(P):
+                tar.ar_unpack_fused(rdo[r], ux[r], seq + 3, err)
+        elif name == "ubatch":
+            s0.wait_stream(main_s)
+            s1.wait_stream(main_s)
+            tar.ar_reduce_ubatch(ins, ubo, ROWS, HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE,
+                                 [s0, s1])
+            main_s.wait_stream(s0)
+            main_s.wait_stream(s1)
+
+    # ---------------------------------------------------------------- timed steps
+    log(f"warmup {args.warmup} steps")
+    for w in range(args.warmup):
+        for r in rows:
+            run_row(r, 1000 + w)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(main_s)
+        for i, r in enumerate(rows):
+            run_row(r, k + 1)
+            ev[k][i + 1].record(main_s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev[0][0].elapsed_time(ev[K - 1][len(rows)])
+    row_ms = {r: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)) / K for i, r in enumerate(rows)}
+    e = err.cpu().numpy().view(np.uint64)
+    assert int(e[0]) == 0, "sequence-number mismatches in the bench step"
+    # every output of the step agrees with the one-shot result on device
+    for o in outs + ubo:
+        assert torch.equal(o, out1), "two-stage/ubatch output differs from one-shot"
+    ms_per_step = gpu_ms / K
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{ms_per_step:.3f} ms/step (wall {1e3 * wall / K:.3f}), {value:.1f} GB/s")
+
+    per_row = {}
+    for r in rows:
+        gbps = credited[r] / (row_ms[r] * 1e-3) / 1e9
+        per_row[r] = {"kernel": kernel_of[r], "launches": launches[r], "ms": round(row_ms[r], 4),
+                      "credited_bytes": credited[r], "GBps": round(gbps, 1),
+                      "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+    dom = max(rows, key=lambda r: row_ms[r])
+    dom_launch_ms = row_ms[dom] / launches[dom]
+    dom_bytes = credited[dom] / launches[dom]
+    achieved = dom_bytes / (dom_launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": load_traffic(dom, KERNEL_SOURCES),
+                "kernel": kernel_of[dom], "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_ms": round(dom_launch_ms, 4)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "P=8 simulated ranks, bf16 [16384 x 8192] per rank (16k-token prefill "
+                               "hidden state, 256 MiB/buffer), N(0,1); step = one-shot + two-stage + "
+                               "pack + recursive doubling + unpack + 2-ubatch chunked reduce",
+                   "P": P, "shape_per_rank": [ROWS, HIDDEN], "accumulate": "f32",
+                   "step_credited_bytes": step_bytes, "parallelism": "none (one GPU)"},
+        "roofline": roofline,
+        "rows": per_row,
+    }
+
+    if args.copy_calib:
+        cb = 1 << 30
+        src = torch.empty(cb // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty(cb // 2, dtype=torch.int16, device=dev)
+        src.fill_(1)
+        for _ in range(3):
+            if blib.arb_copy(src.data_ptr(), dst.data_ptr(), cb, 64, main_s.cuda_stream) != 0:
+                raise RuntimeError("arb_copy failed")
+        torch.cuda.synchronize()
+        result["copy_calib_bytes"] = cb
+        del src, dst
+
+    if not args.no_extras:
+        result.update(extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1))
+        del ins, outs, words, rdo, ux, ubo, out1
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args, np)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1):
+    vp = ctypes.c_void_p
+    sh = main_s.cuda_stream
+    res = {}
+
+    def parr(ts):
+        a = (vp * len(ts))()
+        for i, t in enumerate(ts):
+            a[i] = t.data_ptr()
+        return a
+
+    # staged two-stage at the prefill size (scratch round trip not credited)
+    n = ROWS * HIDDEN
+    scratch = e16(n)
+    us = blib.arb_stream_us(2, parr(ins), parr(outs), P, n, scratch.data_ptr(), 20, sh)
+    res["2stage_staged_prefill"] = {"us": round(us, 2),
+                                    "GBps_credited": round(2 * P * 2 * n / (us * 1e-6) / 1e9, 1)}
+    us = blib.arb_stream_us(1, parr(ins), parr(outs), P, n, None, 20, sh)
+    res["2stage_fused_prefill"] = {"us": round(us, 2),
+                                   "GBps_credited": round(2 * P * 2 * n / (us * 1e-6) / 1e9, 1),
+                                   "frac_of_peak": round(2 * P * 2 * n / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+    del scratch
+    log("prefill staged/fused two-stage timed")
+
+    # attainable bandwidth: plain copy of 2 GiB
+    cb = 1 << 31
+    src = torch.empty(cb // 2, dtype=torch.int16, device=dev)
+    dst = torch.empty(cb // 2, dtype=torch.int16, device=dev)
+    src.fill_(1)
+    best = 0.0
+    for block in (64, 128, 256):
+        for _ in range(3):
+            blib.arb_copy(src.data_ptr(), dst.data_ptr(), cb, block, sh)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(10):
+            blib.arb_copy(src.data_ptr(), dst.data_ptr(), cb, block, sh)
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        gbps = 2 * cb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        best = max(best, gbps)
+    res["copy_GBps"] = round(best, 1)
+    del src, dst
+    log(f"copy bandwidth {best:.0f} GB/s")
+
+    # latency at decode sizes, 128 KiB .. 2 MiB per buffer
+    lat = {}
+    for T in (8, 32, 128):
+        m = T * HIDDEN
+        xi = [x[:m] for x in ins]
+        xo = [o[:m] for o in outs]
+        sc = e16(m)
+        key = f"{2 * m // 1024}KiB"
+        lat[key] = {}
+        for which, name in ((0, "oneshot"), (1, "2stage_fused"), (2, "2stage_staged")):
+            us = blib.arb_stream_us(which, parr(xi), parr(xo), P, m, sc.data_ptr(), 5000, sh)
+            p50, p10, p90 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+            rc = blib.arb_wall_us(which, parr(xi), parr(xo), P, m, sc.data_ptr(), 2000, sh,
+                                  ctypes.byref(p50), ctypes.byref(p10), ctypes.byref(p90))
+            if rc != 0:
+                raise RuntimeError(f"arb_wall_us failed: {rc}")
+            cred = (P + 1) * 2 * m if which == 0 else 2 * P * 2 * m
+            lat[key][name] = {"stream_us": round(us, 2), "wall_us_p50": round(p50.value, 2),
+                              "wall_us_p90": round(p90.value, 2),
+                              "GBps_hot": round(cred / (us * 1e-6) / 1e9, 1)}
+    res["latency"] = lat
+    log("latency measured")
+
+    # ubatch reduce at its own shape: [16384 x 16384] per rank, 2 streams, 1 MiB chunks
+    from tensor_all_reduce_amd import synth
+    m = UB_ROWS * UB_HIDDEN
+    uin = [t.view(torch.int16) for t in synth.device_rank_buffers("logmag", P, m, 5, dev)]
+    uout = [e16(m) for _ in range(P)]
+
+    def ub():
+        s0.wait_stream(main_s)
+        s1.wait_stream(main_s)
+        tar.ar_reduce_ubatch(uin, uout, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE,
+                             [s0, s1])
+        main_s.wait_stream(s0)
+        main_s.wait_stream(s1)
+
+    for _ in range(3):
+        ub()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(main_s)
+    for _ in range(reps):
+        ub()
+    e1.record(main_s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = 2 * P * 2 * m / (ms * 1e-3) / 1e9
+    res["ubatch_16384x16384"] = {"ms": round(ms, 4), "GBps_credited": round(gbps, 1),
+                                 "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                                 "streams": 2, "chunk_bytes": CHUNK_BYTES}
+    log(f"ubatch [16384x16384]: {ms:.3f} ms, {gbps:.0f} GB/s")
+    del uin, uout
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, np):
+    """The oracle (single-threaded C, as it stands) on a bounded sample of the
+    same step: the first `rows_s` rows of the [16384 x 8192] workload."""
+    import oracle
+    from tensor_all_reduce_amd import synth
+
+    def step(rows_s):
+        m = rows_s * HIDDEN
+        xs = [synth.normal(m, 4, 0, p) for p in range(P)]
+        t0 = time.perf_counter()
+        oracle.reduce_seq(xs)
+        oracle.reduce_2stage(xs)
+        ws = [oracle.pack(x, 1) for x in xs]
+        rw, _ = oracle.rd(ws, 1)
+        for w in rw:
+            oracle.unpack(w, 4)
+        oracle.reduce_ubatch(xs, rows_s, HIDDEN, 2, None, CHUNK_BYTES // 2, oracle.TWOSTAGE)
+        dt = time.perf_counter() - t0
+        b = 2 * m
+        cred = (P + 1) * b + 2 * P * b + 3 * P * b + 4 * P * b + 3 * P * b + 2 * P * b
+        return dt, cred
+
+    dt, _ = step(16)
+    rows_s = int(min(ROWS, max(16, 16 * args.cpu_seconds / max(dt, 1e-3))))
+    rows_s -= rows_s % 2
+    log(f"cpu oracle: calibration 16 rows took {dt:.2f} s; timing {rows_s} rows")
+    dt, cred = step(rows_s)
+    gbps = cred / dt / 1e9
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full step (all six rows) of the oracle on the first {rows_s} of 16384 rows "
+                      f"(P=8, hidden 8192, N(0,1)); {dt:.1f} s on one host core; credited bytes as the GPU step",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

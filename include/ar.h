@@ -180,6 +180,29 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
                      size_t chunk_bytes, int variant, void* const* streams);
 
 /*
+ * Launch-shape control (tuning; not a step of the reduction).  Every kernel
+ * kind runs on a flat grid of `block`-lane workgroups (64, 128 or 256), each
+ * lane handling `vec` 16-byte groups per buffer (1 or 2), with optional
+ * non-temporal loads/stores, and at most `wg_per_cu` workgroups per compute
+ * unit (0 = no cap; enforced by requesting unused LDS).  Defaults are the
+ * fastest shapes measured on MI355X.  A new shape applies to launches made
+ * after the call, process-wide; the call is thread-safe.
+ * Returns AR_ERR_INVALID for an unknown kind or out-of-range field.
+ */
+#define AR_KERNEL_ONESHOT  0   /* ar_reduce_oneshot                         */
+#define AR_KERNEL_2STAGE   1   /* ar_reduce_2stage, fused                    */
+#define AR_KERNEL_UBATCH   2   /* ar_reduce_ubatch, two-stage variant        */
+#define AR_KERNEL_RS       3   /* ar_reduce_2stage, staged: reduce-scatter   */
+#define AR_KERNEL_AG       4   /* ar_reduce_2stage, staged: all-gather       */
+#define AR_KERNEL_PACK     5   /* ar_pack_fused                              */
+#define AR_KERNEL_UNPACK   6   /* ar_unpack_fused                            */
+#define AR_KERNEL_RD       7   /* ar_rd_schedule, fused                      */
+#define AR_KERNEL_RDSTEP   8   /* ar_rd_schedule, staged (per step)          */
+int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu);
+int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
+                        int* wg_per_cu);
+
+/*
  * Initialise an error record for ar_unpack_fused / ar_rd_schedule on
  * `stream`: d_err[0] = 0, d_err[1] = UINT64_MAX.  Uses a one-thread kernel,
  * not a memset, so it may be recorded in a HIP graph.

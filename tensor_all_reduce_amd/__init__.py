@@ -23,7 +23,9 @@ __all__ = [
     "ar_reduce_ubatch", "ar_err_init", "rd_mailbox_words",
     "AR_OK", "AR_ERR_INVALID", "AR_ERR_ALIGN", "AR_ERR_ALIAS", "AR_ERR_UNSUPPORTED",
     "AR_ERR_HIP", "AR_MAX_RANKS", "AR_VARIANT_ONESHOT", "AR_VARIANT_2STAGE",
-    "AR_RD_STAGED", "AR_RD_FP32_CARRY",
+    "AR_RD_STAGED", "AR_RD_FP32_CARRY", "ar_set_launch_shape", "ar_get_launch_shape",
+    "AR_KERNEL_ONESHOT", "AR_KERNEL_2STAGE", "AR_KERNEL_UBATCH", "AR_KERNEL_RS", "AR_KERNEL_AG",
+    "AR_KERNEL_PACK", "AR_KERNEL_UNPACK", "AR_KERNEL_RD", "AR_KERNEL_RDSTEP",
 ]
 
 AR_OK = 0
@@ -37,6 +39,15 @@ AR_VARIANT_ONESHOT = 0
 AR_VARIANT_2STAGE = 1
 AR_RD_STAGED = 1
 AR_RD_FP32_CARRY = 2
+AR_KERNEL_ONESHOT = 0
+AR_KERNEL_2STAGE = 1
+AR_KERNEL_UBATCH = 2
+AR_KERNEL_RS = 3
+AR_KERNEL_AG = 4
+AR_KERNEL_PACK = 5
+AR_KERNEL_UNPACK = 6
+AR_KERNEL_RD = 7
+AR_KERNEL_RDSTEP = 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libarcore.so")
@@ -85,6 +96,11 @@ def lib():
                                        ctypes.POINTER(_vp)]
         L.ar_err_init.restype = ctypes.c_int
         L.ar_err_init.argtypes = [_vp, _vp]
+        L.ar_set_launch_shape.restype = ctypes.c_int
+        L.ar_set_launch_shape.argtypes = [ctypes.c_int] * 6
+        ip = ctypes.POINTER(ctypes.c_int)
+        L.ar_get_launch_shape.restype = ctypes.c_int
+        L.ar_get_launch_shape.argtypes = [ctypes.c_int, ip, ip, ip, ip, ip]
         _lib = L
     return _lib
 
@@ -226,3 +242,17 @@ def ar_reduce_ubatch(ins: Sequence, outs: Sequence, rows: int, hidden: int, n_ub
 def ar_err_init(d_err, stream=None) -> None:
     (ep,) = _bufs([d_err], 8, "d_err", 2)
     _check(lib().ar_err_init(ep, _stream(stream)), "ar_err_init")
+
+
+def ar_set_launch_shape(kind: int, block: int, vec: int, nt_loads: int, nt_stores: int,
+                        wg_per_cu: int) -> None:
+    """Set the launch shape of one kernel kind (tuning; process-wide)."""
+    _check(lib().ar_set_launch_shape(int(kind), int(block), int(vec), int(nt_loads),
+                                     int(nt_stores), int(wg_per_cu)), "ar_set_launch_shape")
+
+
+def ar_get_launch_shape(kind: int) -> tuple:
+    """(block, vec, nt_loads, nt_stores, wg_per_cu) of one kernel kind."""
+    v = [ctypes.c_int() for _ in range(5)]
+    _check(lib().ar_get_launch_shape(int(kind), *[ctypes.byref(x) for x in v]), "ar_get_launch_shape")
+    return tuple(x.value for x in v)

@@ -14,7 +14,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libarcore.so")
+BENCH_LIB = os.path.join(HERE, "libarbench.so")
 SOURCES = ["ar_api.hip", "ar_reduce.hip", "ar_fused.hip"]
+BENCH_SOURCES = ["ar_bench.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -30,10 +32,9 @@ HIP_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    objs = []
-    procs = []
-    for src in SOURCES:
+def _compile(sources, verbose, jobs):
+    objs, procs = [], []
+    for src in sources:
         obj = os.path.join(CSRC, src.replace(".hip", ".o"))
         cmd = [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -47,12 +48,24 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for p, c in procs:
         if p.wait() != 0:
             raise RuntimeError("hipcc failed: " + " ".join(c))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    return objs
+
+
+def _link(objs, out, extra, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, *extra]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile libarcore.so (the library) and libarbench.so (timing helpers
+    and a copy kernel used only by bench.py; linked against libarcore.so)."""
+    objs = _compile(SOURCES + BENCH_SOURCES, verbose, jobs)
+    _link(objs[: len(SOURCES)], LIB, [], verbose)
+    _link(objs[len(SOURCES):], BENCH_LIB, ["-L", HERE, "-larcore", "-Wl,-rpath,$ORIGIN"], verbose)
     return LIB
 
 

@@ -9,6 +9,7 @@
 // flags for its per-ubatch communicators.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -28,56 +29,90 @@ constexpr int kMaxUbatch = 16;
 struct DevInfo {
   bool ready = false;
   int cus = 0;
+  int lds_per_cu = 0;
+  int lds_per_block = 0;
 };
 
-struct Tuning {
-  int grid_mult = 4;
-  int nt_loads = 0;
-  int nt_stores = 0;
+// Default launch shapes: the fastest settings measured on MI355X for each
+// kernel's stream pattern (block, vec, nt_loads, nt_stores, wg_per_cu).
+constexpr ar::Shape kDefaultShape[ar::kKinds] = {
+    {256, 1, 1, 1, 2, 0},   // one-shot, 8 -> 1
+    {64, 2, 1, 1, 4, 0},    // fused two-stage, 8 -> 8
+    {64, 1, 1, 1, 6, 0},    // ubatch, 8 -> 8 on two streams
+    {256, 1, 1, 1, 5, 0},   // staged reduce-scatter, 8 -> 1
+    {64, 1, 1, 1, 3, 0},    // staged all-gather, 1 -> 8
+    {256, 1, 1, 0, 6, 0},   // pack, 1 -> 2
+    {128, 1, 0, 1, 12, 0},  // unpack, 2 -> 1
+    {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
+    {64, 1, 1, 1, 8, 0},    // staged recursive-doubling step, 8 -> 8
 };
+constexpr const char* kShapeEnv[ar::kKinds] = {
+    "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
+    "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP"};
 
 std::mutex g_mu;
 DevInfo g_dev[kMaxDevices];
-bool g_tuning_ready = false;
-Tuning g_tuning;
+bool g_shapes_ready = false;
+ar::Shape g_shape[ar::kKinds];
 
-int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* s = std::getenv(name);
-  if (!s || !*s) return dflt;
-  char* end = nullptr;
-  long v = std::strtol(s, &end, 10);
-  if (end == s || v < lo || v > hi) return dflt;
-  return (int)v;
+bool shape_ok(int block, int vec, int ntl, int nts, int wg) {
+  return (block == 64 || block == 128 || block == 256) && vec >= 1 && vec <= 2 && ntl >= 0 &&
+         ntl <= 1 && nts >= 0 && nts <= 1 && wg >= 0 && wg <= 64;
 }
 
-// Resolve the launch policy for the current device: CU count (cached once per
-// device) and the tuning knobs (read once per process):
-//   AR_GRID_MULT   workgroups per CU for grid-stride kernels (1..64)
-//   AR_NT_LOADS    1: non-temporal loads of streamed inputs
-//   AR_NT_STORES   1: non-temporal stores of outputs
+// "block,vec,nt_loads,nt_stores,wg_per_cu"; an invalid string keeps the default.
+void parse_shape(const char* name, ar::Shape* s) {
+  const char* e = std::getenv(name);
+  if (!e || !*e) return;
+  int v[5];
+  if (std::sscanf(e, "%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4]) != 5) return;
+  if (!shape_ok(v[0], v[1], v[2], v[3], v[4])) return;
+  *s = ar::Shape{v[0], v[1], v[2], v[3], v[4], 0};
+}
+
+// Caller holds g_mu.
+void init_shapes_locked() {
+  if (g_shapes_ready) return;
+  for (int k = 0; k < ar::kKinds; ++k) {
+    g_shape[k] = kDefaultShape[k];
+    parse_shape(kShapeEnv[k], &g_shape[k]);
+  }
+  g_shapes_ready = true;
+}
+
+// Resolve the launch policy for the current device: CU count and LDS sizes
+// (cached once per device) and the per-kernel shapes (defaults above,
+// overridable once per process through AR_SHAPE_<KIND> for A/B measurement).
 int resolve(ar::Launch* L, void* stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AR_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_tuning_ready) {
-    g_tuning.grid_mult = env_int("AR_GRID_MULT", g_tuning.grid_mult, 1, 64);
-    g_tuning.nt_loads = env_int("AR_NT_LOADS", g_tuning.nt_loads, 0, 1);
-    g_tuning.nt_stores = env_int("AR_NT_STORES", g_tuning.nt_stores, 0, 1);
-    g_tuning_ready = true;
-  }
+  init_shapes_locked();
   DevInfo& d = g_dev[dev];
   if (!d.ready) {
-    int cus = 0;
+    int cus = 0, lcu = 0, lblk = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lcu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&lblk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
         cus <= 0)
       return AR_ERR_HIP;
     d.cus = cus;
+    d.lds_per_cu = lcu;
+    d.lds_per_block = lblk;
     d.ready = true;
   }
   L->cus = d.cus;
-  L->grid_mult = g_tuning.grid_mult;
-  L->nt_loads = g_tuning.nt_loads;
-  L->nt_stores = g_tuning.nt_stores;
+  for (int k = 0; k < ar::kKinds; ++k) {
+    ar::Shape s = g_shape[k];
+    unsigned lds = 0;
+    if (s.wg_per_cu > 0 && d.lds_per_cu > 0) {
+      lds = ((unsigned)d.lds_per_cu / (unsigned)s.wg_per_cu) & ~255u;
+      if (lds > (unsigned)d.lds_per_block) lds = (unsigned)d.lds_per_block;
+    }
+    s.lds = lds;
+    L->shape[k] = s;
+  }
   L->stream = static_cast<hipStream_t>(stream);
   return AR_OK;
 }
@@ -306,6 +341,30 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
     rc = hip_status(ar::launch_chunked(L, in, out, P, e0, e1, chunk, nout > 1 ? 1 : 0));
     if (rc) return rc;
   }
+  return AR_OK;
+}
+
+int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu) {
+  if (kind < 0 || kind >= ar::kKinds || !shape_ok(block, vec, nt_loads, nt_stores, wg_per_cu))
+    return AR_ERR_INVALID;
+  std::lock_guard<std::mutex> lock(g_mu);
+  init_shapes_locked();
+  g_shape[kind] = ar::Shape{block, vec, nt_loads, nt_stores, wg_per_cu, 0};
+  return AR_OK;
+}
+
+int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
+                        int* wg_per_cu) {
+  if (kind < 0 || kind >= ar::kKinds || !block || !vec || !nt_loads || !nt_stores || !wg_per_cu)
+    return AR_ERR_INVALID;
+  std::lock_guard<std::mutex> lock(g_mu);
+  init_shapes_locked();
+  const ar::Shape& s = g_shape[kind];
+  *block = s.block;
+  *vec = s.vec;
+  *nt_loads = s.nt_loads;
+  *nt_stores = s.nt_stores;
+  *wg_per_cu = s.wg_per_cu;
   return AR_OK;
 }
 

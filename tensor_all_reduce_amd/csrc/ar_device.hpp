@@ -17,8 +17,8 @@ namespace ar {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 256;   // workgroup size used by the streaming kernels
-constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kMaxBlock = 256;  // largest workgroup the kernels are compiled for
+constexpr int kWave = 64;       // CDNA wavefront width
 
 template <bool NT>
 __device__ __forceinline__ u32x4 ld4(const u32x4* p) {
@@ -93,11 +93,13 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // instead of being read back from the thread's sticky last-error slot.
 template <typename T> struct id { using type = T; };
 
+// `lds` bytes of dynamic LDS per workgroup are requested only to cap how many
+// workgroups share a CU (an occupancy knob); no kernel reads them.
 template <typename... KArgs>
-inline hipError_t launch_k(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+inline hipError_t launch_k(void (*k)(KArgs...), dim3 grid, dim3 block, unsigned lds, hipStream_t s,
                            typename id<KArgs>::type... args) {
   void* argv[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, lds, s);
 }
 
 inline size_t cdiv(size_t a, size_t b) { return (a + b - 1) / b; }

@@ -13,10 +13,10 @@
 // {data_j, seq, data_j+1, seq}.
 //
 // Validation: every lane checks its words' sequence numbers; a wavefront
-// folds its 64 lanes' verdicts with one ballot per word slot.  When the whole
-// wavefront is clean (the normal case) that is the only cost; otherwise the
-// wave-uniform count and first index are accumulated in scalar registers and
-// one lane issues two atomics when the wavefront retires.
+// folds its 64 lanes' verdicts with one ballot.  When the whole wavefront is
+// clean (the normal case) that is the only cost; otherwise one ballot per
+// word slot gives the wave-uniform count and first index, and one lane
+// issues two atomics.
 #include "ar_device.hpp"
 #include "ar_internal.hpp"
 
@@ -50,34 +50,31 @@ __device__ __forceinline__ void wave_flush(const WaveErr& e, uint64_t* err) {
   }
 }
 
-// Base of this lane's wavefront in a grid-stride loop whose stride is a
-// multiple of 64: every lane of a wavefront runs the same trip count, so the
-// ballots always see the whole wavefront.
-__device__ __forceinline__ size_t wave_base() {
-  return (size_t)blockIdx.x * blockDim.x + (threadIdx.x & ~(kWave - 1));
-}
-
 }  // namespace
 
 // ----------------------------------------------------------------------------
+// All kernels below use a flat grid: lane (blockIdx.x * blockDim.x + tid)
+// owns one 16-byte group, workgroups dispatched in address order (the launch
+// shape that measured fastest for streaming on MI355X).  The ragged end (the
+// data words past the last whole group) is done by the last workgroup.
+
 // Pack: 16 bytes of bf16 (4 data words) -> 32 bytes of payload.
 template <bool NTL, bool NTS>
-__global__ __launch_bounds__(kBlock) void k_pack(const void* x, uint64_t* w, size_t n, uint32_t seq) {
+__global__ __launch_bounds__(kMaxBlock) void k_pack(const void* x, uint64_t* w, size_t n, uint32_t seq) {
   const size_t nvec = n >> 3;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  const u32x4* src = static_cast<const u32x4*>(x);
-  u32x4* dst = reinterpret_cast<u32x4*>(w);
-  for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    const u32x4 d = ld4<NTL>(src + v);
+  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < nvec) {
+    const u32x4 d = ld4<NTL>(static_cast<const u32x4*>(x) + v);
     u32x4 a, b;
     a[0] = d[0]; a[1] = seq; a[2] = d[1]; a[3] = seq;
     b[0] = d[2]; b[1] = seq; b[2] = d[3]; b[3] = seq;
+    u32x4* dst = reinterpret_cast<u32x4*>(w);
     st4<NTS>(dst + 2 * v, a);
     st4<NTS>(dst + 2 * v + 1, b);
   }
   // tail: n is even, so 0..3 whole data words remain
   const size_t j = (nvec << 2) + threadIdx.x;
-  if (blockIdx.x == 0 && j < (n >> 1)) {
+  if (blockIdx.x == gridDim.x - 1 && j < (n >> 1)) {
     const uint32_t d = static_cast<const uint32_t*>(x)[j];
     w[j] = ((uint64_t)seq << 32) | (uint64_t)d;
   }
@@ -85,36 +82,32 @@ __global__ __launch_bounds__(kBlock) void k_pack(const void* x, uint64_t* w, siz
 
 // Unpack + validate: 32 bytes of payload -> 16 bytes of bf16.
 template <bool NTL, bool NTS>
-__global__ __launch_bounds__(kBlock) void k_unpack(const uint64_t* w, void* x, size_t n, uint32_t seq,
-                                                   uint64_t* err) {
+__global__ __launch_bounds__(kMaxBlock) void k_unpack(const uint64_t* w, void* x, size_t n, uint32_t seq,
+                                                     uint64_t* err) {
   const size_t nvec = n >> 3;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  const u32x4* src = reinterpret_cast<const u32x4*>(w);
-  u32x4* dst = static_cast<u32x4*>(x);
+  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool act = v < nvec;
+  u32x4 a = {0u, seq, 0u, seq}, b = {0u, seq, 0u, seq};
+  if (act) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(w);
+    a = ld4<NTL>(src + 2 * v);
+    b = ld4<NTL>(src + 2 * v + 1);
+    u32x4 d;
+    d[0] = a[0]; d[1] = a[2]; d[2] = b[0]; d[3] = b[2];
+    st4<NTS>(static_cast<u32x4*>(x) + v, d);
+  }
+  const bool b0 = a[1] != seq, b1 = a[3] != seq, b2 = b[1] != seq, b3 = b[3] != seq;
   WaveErr e;
-  for (size_t base = wave_base(); base < nvec; base += stride) {
-    const size_t v = base + lane_id();
-    const bool act = v < nvec;
-    u32x4 a = {0u, seq, 0u, seq}, b = {0u, seq, 0u, seq};
-    if (act) {
-      a = ld4<NTL>(src + 2 * v);
-      b = ld4<NTL>(src + 2 * v + 1);
-      u32x4 d;
-      d[0] = a[0]; d[1] = a[2]; d[2] = b[0]; d[3] = b[2];
-      st4<NTS>(dst + v, d);
-    }
-    const bool b0 = a[1] != seq, b1 = a[3] != seq, b2 = b[1] != seq, b3 = b[3] != seq;
-    if (__ballot(b0 | b1 | b2 | b3)) {
-      const uint64_t j = 4 * (uint64_t)v;
-      wave_note(e, b0, j);
-      wave_note(e, b1, j + 1);
-      wave_note(e, b2, j + 2);
-      wave_note(e, b3, j + 3);
-    }
+  if (__ballot(b0 | b1 | b2 | b3)) {
+    const uint64_t j = 4 * (uint64_t)v;
+    wave_note(e, b0, j);
+    wave_note(e, b1, j + 1);
+    wave_note(e, b2, j + 2);
+    wave_note(e, b3, j + 3);
   }
   wave_flush(e, err);
   const size_t j = (nvec << 2) + threadIdx.x;
-  if (blockIdx.x == 0 && j < (n >> 1)) {
+  if (blockIdx.x == gridDim.x - 1 && j < (n >> 1)) {
     const uint64_t wj = w[j];
     static_cast<uint32_t*>(x)[j] = (uint32_t)wj;
     if ((uint32_t)(wj >> 32) != seq) {
@@ -134,65 +127,62 @@ __global__ __launch_bounds__(kBlock) void k_unpack(const uint64_t* w, void* x, s
 // node is rounded to bf16, as the exchanged payload is bf16; otherwise the
 // partials stay binary32 and are rounded once.
 template <int P, bool ROUND_EACH, bool NTL, bool NTS>
-__global__ __launch_bounds__(kBlock) void k_rd_fused(WordIn in, WordOut out, size_t W, uint32_t seq0,
-                                                     uint64_t* err) {
+__global__ __launch_bounds__(kMaxBlock) void k_rd_fused(WordIn in, WordOut out, size_t W, uint32_t seq0,
+                                                       uint64_t* err) {
   constexpr uint32_t L = P == 2 ? 1 : (P == 4 ? 2 : 3);
   const uint32_t seq_out = seq0 + L;
   const size_t nvec = W >> 1;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool act = v < nvec;
+  u32x4 a[P];
+  bool any = false;
+  bool bad[P][2];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    a[p] = act ? ld4<NTL>(reinterpret_cast<const u32x4*>(in.p[p]) + v) : u32x4{0u, seq0, 0u, seq0};
+    bad[p][0] = a[p][1] != seq0;
+    bad[p][1] = a[p][3] != seq0;
+    any |= bad[p][0] | bad[p][1];
+  }
   WaveErr e;
-  for (size_t base = wave_base(); base < nvec; base += stride) {
-    const size_t v = base + lane_id();
-    const bool act = v < nvec;
-    u32x4 a[P];
-    bool any = false;
-    bool bad[P][2];
+  if (__ballot(any)) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      a[p] = act ? ld4<NTL>(reinterpret_cast<const u32x4*>(in.p[p]) + v) : u32x4{0u, seq0, 0u, seq0};
-      bad[p][0] = a[p][1] != seq0;
-      bad[p][1] = a[p][3] != seq0;
-      any |= bad[p][0] | bad[p][1];
-    }
-    if (__ballot(any)) {
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        wave_note(e, bad[p][0], (uint64_t)p * W + 2 * (uint64_t)v);
-        wave_note(e, bad[p][1], (uint64_t)p * W + 2 * (uint64_t)v + 1);
-      }
-    }
-    if (act) {
-      float f[P][4];
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        f[p][0] = lo_f32(a[p][0]);
-        f[p][1] = hi_f32(a[p][0]);
-        f[p][2] = lo_f32(a[p][2]);
-        f[p][3] = hi_f32(a[p][2]);
-      }
-#pragma unroll
-      for (int h = 1; h < P; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < P; i += 2 * h) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float s = f[i][k] + f[i + h][k];
-            f[i][k] = ROUND_EACH ? round_bf16(s) : s;
-          }
-        }
-      }
-      u32x4 o;
-      o[0] = pack_bf16x2(f[0][0], f[0][1]);
-      o[1] = seq_out;
-      o[2] = pack_bf16x2(f[0][2], f[0][3]);
-      o[3] = seq_out;
-#pragma unroll
-      for (int p = 0; p < P; ++p) st4<NTS>(reinterpret_cast<u32x4*>(out.p[p]) + v, o);
+      wave_note(e, bad[p][0], (uint64_t)p * W + 2 * (uint64_t)v);
+      wave_note(e, bad[p][1], (uint64_t)p * W + 2 * (uint64_t)v + 1);
     }
   }
   wave_flush(e, err);
+  if (act) {
+    float f[P][4];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      f[p][0] = lo_f32(a[p][0]);
+      f[p][1] = hi_f32(a[p][0]);
+      f[p][2] = lo_f32(a[p][2]);
+      f[p][3] = hi_f32(a[p][2]);
+    }
+#pragma unroll
+    for (int h = 1; h < P; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < P; i += 2 * h) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float s = f[i][k] + f[i + h][k];
+          f[i][k] = ROUND_EACH ? round_bf16(s) : s;
+        }
+      }
+    }
+    u32x4 o;
+    o[0] = pack_bf16x2(f[0][0], f[0][1]);
+    o[1] = seq_out;
+    o[2] = pack_bf16x2(f[0][2], f[0][3]);
+    o[3] = seq_out;
+#pragma unroll
+    for (int p = 0; p < P; ++p) st4<NTS>(reinterpret_cast<u32x4*>(out.p[p]) + v, o);
+  }
   // odd word count: the last word, one lane
-  if (blockIdx.x == 0 && threadIdx.x == 0 && (W & 1)) {
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0 && (W & 1)) {
     const size_t j = W - 1;
     float f[P][2];
     for (int p = 0; p < P; ++p) {
@@ -215,56 +205,54 @@ __global__ __launch_bounds__(kBlock) void k_rd_fused(WordIn in, WordOut out, siz
   }
 }
 
-// Staged recursive doubling, one launch per step k.  blockIdx.y picks the
-// pair (r, q = r | 2^k) with bit k of r clear; a lane reads both payload
+// Staged recursive doubling, one launch per step k.  Workgroup b works on
+// tile b / (P/2) of pair b % (P/2), so consecutive workgroups cover every
+// pair at the same offset and all P payload streams advance together.  The
+// pair (r, q = r | 2^k) has bit k of r clear; a lane reads both payload
 // groups, checks both sequence numbers (each payload of the step is received
 // by exactly one partner, so each is checked once), adds, rounds, and writes
 // the new payload to both ranks' destinations.  One lane per pair makes
 // exact in-place aliasing safe.
 template <bool NTL, bool NTS>
-__global__ __launch_bounds__(kBlock) void k_rd_step(WordIn src, WordOut dst, int P, int k, size_t W,
-                                                    uint32_t seq_in, uint64_t* err) {
-  const int i = blockIdx.y;
+__global__ __launch_bounds__(kMaxBlock) void k_rd_step(WordIn src, WordOut dst, int P, int k, size_t W,
+                                                      uint32_t seq_in, uint64_t* err) {
+  const unsigned npairs = (unsigned)P >> 1;
+  const int i = (int)(blockIdx.x % npairs);
+  const size_t tile = blockIdx.x / npairs;
+  const size_t ntiles = gridDim.x / npairs;
   const int low = i & ((1 << k) - 1);
   const int r = ((i >> k) << (k + 1)) | low;
   const int q = r | (1 << k);
   const uint32_t seq_out = seq_in + 1u;
   const size_t nvec = W >> 1;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
   const uint64_t base_r = ((uint64_t)k * P + r) * W;
   const uint64_t base_q = ((uint64_t)k * P + q) * W;
-  const u32x4* sr = reinterpret_cast<const u32x4*>(src.p[r]);
-  const u32x4* sq = reinterpret_cast<const u32x4*>(src.p[q]);
-  u32x4* dr = reinterpret_cast<u32x4*>(dst.p[r]);
-  u32x4* dq = reinterpret_cast<u32x4*>(dst.p[q]);
+  const size_t v = tile * blockDim.x + threadIdx.x;
+  const bool act = v < nvec;
+  u32x4 a = {0u, seq_in, 0u, seq_in}, b = a;
+  if (act) {
+    a = ld4<NTL>(reinterpret_cast<const u32x4*>(src.p[r]) + v);
+    b = ld4<NTL>(reinterpret_cast<const u32x4*>(src.p[q]) + v);
+  }
+  const bool ba0 = a[1] != seq_in, ba1 = a[3] != seq_in, bb0 = b[1] != seq_in, bb1 = b[3] != seq_in;
   WaveErr e;
-  for (size_t base = wave_base(); base < nvec; base += stride) {
-    const size_t v = base + lane_id();
-    const bool act = v < nvec;
-    u32x4 a = {0u, seq_in, 0u, seq_in}, b = a;
-    if (act) {
-      a = ld4<NTL>(sr + v);
-      b = ld4<NTL>(sq + v);
-    }
-    const bool ba0 = a[1] != seq_in, ba1 = a[3] != seq_in, bb0 = b[1] != seq_in, bb1 = b[3] != seq_in;
-    if (__ballot(ba0 | ba1 | bb0 | bb1)) {
-      wave_note(e, ba0, base_r + 2 * (uint64_t)v);
-      wave_note(e, ba1, base_r + 2 * (uint64_t)v + 1);
-      wave_note(e, bb0, base_q + 2 * (uint64_t)v);
-      wave_note(e, bb1, base_q + 2 * (uint64_t)v + 1);
-    }
-    if (act) {
-      u32x4 o;
-      o[0] = pack_bf16x2(lo_f32(a[0]) + lo_f32(b[0]), hi_f32(a[0]) + hi_f32(b[0]));
-      o[1] = seq_out;
-      o[2] = pack_bf16x2(lo_f32(a[2]) + lo_f32(b[2]), hi_f32(a[2]) + hi_f32(b[2]));
-      o[3] = seq_out;
-      st4<NTS>(dr + v, o);
-      st4<NTS>(dq + v, o);
-    }
+  if (__ballot(ba0 | ba1 | bb0 | bb1)) {
+    wave_note(e, ba0, base_r + 2 * (uint64_t)v);
+    wave_note(e, ba1, base_r + 2 * (uint64_t)v + 1);
+    wave_note(e, bb0, base_q + 2 * (uint64_t)v);
+    wave_note(e, bb1, base_q + 2 * (uint64_t)v + 1);
   }
   wave_flush(e, err);
-  if (blockIdx.x == 0 && threadIdx.x == 0 && (W & 1)) {
+  if (act) {
+    u32x4 o;
+    o[0] = pack_bf16x2(lo_f32(a[0]) + lo_f32(b[0]), hi_f32(a[0]) + hi_f32(b[0]));
+    o[1] = seq_out;
+    o[2] = pack_bf16x2(lo_f32(a[2]) + lo_f32(b[2]), hi_f32(a[2]) + hi_f32(b[2]));
+    o[3] = seq_out;
+    st4<NTS>(reinterpret_cast<u32x4*>(dst.p[r]) + v, o);
+    st4<NTS>(reinterpret_cast<u32x4*>(dst.p[q]) + v, o);
+  }
+  if (tile == ntiles - 1 && threadIdx.x == 0 && (W & 1)) {
     const size_t j = W - 1;
     const uint64_t wa = src.p[r][j], wb = src.p[q][j];
     if ((uint32_t)(wa >> 32) != seq_in) {
@@ -293,53 +281,60 @@ __global__ void k_err_init(uint64_t* err) {
 // ----------------------------------------------------------------------------
 namespace {
 
-inline unsigned grid_for(const Launch& L, size_t items) {
-  const size_t want = cdiv(items, kBlock);
-  const size_t cap = (size_t)L.cus * (size_t)L.grid_mult;
-  const size_t g = want < cap ? want : cap;
+// Flat grid: one lane per 16-byte group, at least one workgroup (the last
+// workgroup also does the ragged end).
+inline unsigned flat_grid(const Shape& sh, size_t items) {
+  const size_t g = cdiv(items, (size_t)sh.block);
   return (unsigned)(g ? g : 1);
 }
 
-inline int nt_mode(const Launch& L) { return (L.nt_loads ? 1 : 0) | (L.nt_stores ? 2 : 0); }
+inline bool grid_fits(const Shape& sh, size_t items) {
+  return cdiv(items, (size_t)sh.block) <= 0x7FFFFFFFull;
+}
 
 template <int P, bool RE>
 hipError_t rd_fused_p(const Launch& L, const WordIn& in, const WordOut& out, size_t W, uint32_t seq0,
                       uint64_t* err) {
-  const unsigned g = grid_for(L, W >> 1);
-  switch (nt_mode(L)) {
-    case 0: return launch_k(k_rd_fused<P, RE, false, false>, g, kBlock, L.stream, in, out, W, seq0, err);
-    case 1: return launch_k(k_rd_fused<P, RE, true, false>, g, kBlock, L.stream, in, out, W, seq0, err);
-    case 2: return launch_k(k_rd_fused<P, RE, false, true>, g, kBlock, L.stream, in, out, W, seq0, err);
-    default: return launch_k(k_rd_fused<P, RE, true, true>, g, kBlock, L.stream, in, out, W, seq0, err);
-  }
+  const Shape& sh = L.shape[kRD];
+  const unsigned g = flat_grid(sh, W >> 1);
+  const dim3 b(sh.block);
+  if (sh.nt_loads && sh.nt_stores)
+    return launch_k(k_rd_fused<P, RE, true, true>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
+  if (sh.nt_loads) return launch_k(k_rd_fused<P, RE, true, false>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
+  if (sh.nt_stores) return launch_k(k_rd_fused<P, RE, false, true>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
+  return launch_k(k_rd_fused<P, RE, false, false>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
 }
 
 }  // namespace
 
 hipError_t launch_pack(const Launch& L, const void* x, uint64_t* w, size_t n, uint32_t seq) {
-  const unsigned g = grid_for(L, n >> 3);
-  switch (nt_mode(L)) {
-    case 0: return launch_k(k_pack<false, false>, g, kBlock, L.stream, x, w, n, seq);
-    case 1: return launch_k(k_pack<true, false>, g, kBlock, L.stream, x, w, n, seq);
-    case 2: return launch_k(k_pack<false, true>, g, kBlock, L.stream, x, w, n, seq);
-    default: return launch_k(k_pack<true, true>, g, kBlock, L.stream, x, w, n, seq);
-  }
+  const Shape& sh = L.shape[kPack];
+  if (!grid_fits(sh, n >> 3)) return hipErrorInvalidConfiguration;
+  const unsigned g = flat_grid(sh, n >> 3);
+  const dim3 b(sh.block);
+  if (sh.nt_loads && sh.nt_stores) return launch_k(k_pack<true, true>, g, b, sh.lds, L.stream, x, w, n, seq);
+  if (sh.nt_loads) return launch_k(k_pack<true, false>, g, b, sh.lds, L.stream, x, w, n, seq);
+  if (sh.nt_stores) return launch_k(k_pack<false, true>, g, b, sh.lds, L.stream, x, w, n, seq);
+  return launch_k(k_pack<false, false>, g, b, sh.lds, L.stream, x, w, n, seq);
 }
 
 hipError_t launch_unpack(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,
                          uint64_t* d_err) {
-  const unsigned g = grid_for(L, n >> 3);
-  switch (nt_mode(L)) {
-    case 0: return launch_k(k_unpack<false, false>, g, kBlock, L.stream, w, x, n, seq, d_err);
-    case 1: return launch_k(k_unpack<true, false>, g, kBlock, L.stream, w, x, n, seq, d_err);
-    case 2: return launch_k(k_unpack<false, true>, g, kBlock, L.stream, w, x, n, seq, d_err);
-    default: return launch_k(k_unpack<true, true>, g, kBlock, L.stream, w, x, n, seq, d_err);
-  }
+  const Shape& sh = L.shape[kUnpack];
+  if (!grid_fits(sh, n >> 3)) return hipErrorInvalidConfiguration;
+  const unsigned g = flat_grid(sh, n >> 3);
+  const dim3 b(sh.block);
+  if (sh.nt_loads && sh.nt_stores)
+    return launch_k(k_unpack<true, true>, g, b, sh.lds, L.stream, w, x, n, seq, d_err);
+  if (sh.nt_loads) return launch_k(k_unpack<true, false>, g, b, sh.lds, L.stream, w, x, n, seq, d_err);
+  if (sh.nt_stores) return launch_k(k_unpack<false, true>, g, b, sh.lds, L.stream, w, x, n, seq, d_err);
+  return launch_k(k_unpack<false, false>, g, b, sh.lds, L.stream, w, x, n, seq, d_err);
 }
 
 hipError_t launch_rd_fused(const Launch& L, const WordIn& in, const WordOut& out, int P, size_t n,
                            uint32_t seq0, int fp32_carry, uint64_t* d_err) {
   const size_t W = n >> 1;
+  if (!grid_fits(L.shape[kRD], W >> 1)) return hipErrorInvalidConfiguration;
   if (fp32_carry) {
     switch (P) {
       case 2: return rd_fused_p<2, false>(L, in, out, W, seq0, d_err);
@@ -366,8 +361,11 @@ hipError_t launch_rd_staged(const Launch& L, const WordIn& in, const WordOut& ou
   const size_t W = n >> 1;
   const size_t Ws = rd_mailbox_stride(n);
   const int steps = P == 2 ? 1 : (P == 4 ? 2 : 3);
-  const unsigned gx = grid_for(L, W >> 1);
-  const dim3 grid(gx > 0 ? (gx + (unsigned)(P / 2) - 1) / (unsigned)(P / 2) : 1, (unsigned)(P / 2));
+  const Shape& sh = L.shape[kRDStep];
+  const size_t tiles = flat_grid(sh, W >> 1);
+  if (tiles * (size_t)(P / 2) > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(tiles * (size_t)(P / 2)));
+  const dim3 b(sh.block);
   for (int k = 0; k < steps; ++k) {
     WordIn s{};
     WordOut d{};
@@ -377,19 +375,17 @@ hipError_t launch_rd_staged(const Launch& L, const WordIn& in, const WordOut& ou
     }
     const uint32_t sk = seq0 + (uint32_t)k;
     hipError_t e;
-    switch (nt_mode(L)) {
-      case 0: e = launch_k(k_rd_step<false, false>, grid, kBlock, L.stream, s, d, P, k, W, sk, d_err); break;
-      case 1: e = launch_k(k_rd_step<true, false>, grid, kBlock, L.stream, s, d, P, k, W, sk, d_err); break;
-      case 2: e = launch_k(k_rd_step<false, true>, grid, kBlock, L.stream, s, d, P, k, W, sk, d_err); break;
-      default: e = launch_k(k_rd_step<true, true>, grid, kBlock, L.stream, s, d, P, k, W, sk, d_err); break;
-    }
+    if (sh.nt_loads && sh.nt_stores) e = launch_k(k_rd_step<true, true>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
+    else if (sh.nt_loads) e = launch_k(k_rd_step<true, false>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
+    else if (sh.nt_stores) e = launch_k(k_rd_step<false, true>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
+    else e = launch_k(k_rd_step<false, false>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_err_init(const Launch& L, uint64_t* d_err) {
-  return launch_k(k_err_init, dim3(1), dim3(kWave), L.stream, d_err);
+  return launch_k(k_err_init, dim3(1), dim3(kWave), 0, L.stream, d_err);
 }
 
 }  // namespace ar

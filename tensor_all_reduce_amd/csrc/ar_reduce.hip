@@ -1,5 +1,5 @@
 // Reduce kernels for gfx950: one-shot, two-stage (fused write mode and
-// staged reduce-scatter / all-gather), and the chunk-major ubatch kernel.
+// staged reduce-scatter / all-gather) and the chunked ubatch reduce.
 //
 // Pages cited (titles as printed):
 //   [CAR]    "fix(custom_all_reduce): use SYSTEM scope + ACQUIRE ordering for
@@ -14,160 +14,36 @@
 //             stream.
 //
 // The work is elementwise and HBM-bound: each 16-byte group of 8 bf16 is read
-// once from each of the P buffers and written once to each output.  Nothing
-// is a contraction, so no MFMA; the kernels aim at bytes in flight: 128-bit
-// loads, two groups per lane per iteration (2*P loads issued before the first
-// add), grid-stride loops over a grid sized from the CU count.
+// once from each of the P buffers and written once to each output; no MFMA.
+// Launch shape (chosen by measurement on MI355X; the per-kernel table lives
+// in the API layer): a flat grid of small workgroups, each owning one
+// contiguous tile of V * blockDim groups, one group per lane per pass.
+// Workgroups are dispatched in index order, so the tiles in flight form a
+// compact, advancing window of each buffer; a persistent grid-stride loop
+// spreads the in-flight accesses over the whole buffer and measured up to
+// 20% slower.  Workgroups per CU are capped per kernel (see Shape).
 #include "ar_device.hpp"
 #include "ar_internal.hpp"
 
 namespace ar {
 
 // ----------------------------------------------------------------------------
-// One-shot (NOUT == 1) and fused two-stage (NOUT == P): grid-stride over the
-// 16-byte groups, every group reduced by exactly one lane, so an output that
-// is exactly an input buffer is safe (each lane reads its group from every
-// input before it writes that group).
-template <int P, int NOUT, bool NTL, bool NTS>
-__global__ __launch_bounds__(kBlock) void k_reduce(InPtrs in, OutPtrs out, size_t n) {
-  const size_t nvec = n >> 3;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const u32x4* src[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) src[p] = static_cast<const u32x4*>(in.p[p]);
-  u32x4* dst[NOUT];
-#pragma unroll
-  for (int o = 0; o < NOUT; ++o) dst[o] = static_cast<u32x4*>(out.p[o]);
-
-  for (; v + stride < nvec; v += 2 * stride) {
-    u32x4 a[P], b[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(src[p] + v);
-#pragma unroll
-    for (int p = 0; p < P; ++p) b[p] = ld4<NTL>(src[p] + v + stride);
-    const u32x4 ra = reduce8<P>(a);
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) st4<NTS>(dst[o] + v, ra);
-    const u32x4 rb = reduce8<P>(b);
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) st4<NTS>(dst[o] + v + stride, rb);
-  }
-  if (v < nvec) {
-    u32x4 a[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(src[p] + v);
-    const u32x4 ra = reduce8<P>(a);
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) st4<NTS>(dst[o] + v, ra);
-  }
-  // ragged tail: the last n % 8 elements, one lane each, scalar
-  const size_t t0 = nvec << 3;
-  if (blockIdx.x == 0 && t0 + threadIdx.x < n) {
-    const size_t i = t0 + threadIdx.x;
-    const uint16_t* in16[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) in16[p] = static_cast<const uint16_t*>(in.p[p]);
-    const uint16_t r = reduce1<P>(in16, i);
-#pragma unroll
-    for (int o = 0; o < NOUT; ++o) static_cast<uint16_t*>(out.p[o])[i] = r;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Staged two-stage.  Shard s = elements [s*S, min(n, (s+1)*S)), S a multiple
-// of 8.  Workgroup b works on shard b % P: workgroups are dispatched to the
-// 8 XCDs round-robin, so with P = 8 shard s is reduced (and later gathered)
-// by XCD s alone, the one-GPU picture of "rank s owns shard s", and the
-// gather re-reads scratch lines through the L2 that wrote them.
-template <int P, bool NTL>
-__global__ __launch_bounds__(kBlock) void k_rs(InPtrs in, void* scratch, size_t n, size_t S) {
-  const unsigned s = blockIdx.x % P;
-  const unsigned j = blockIdx.x / P;
-  const unsigned bps = gridDim.x / P;
-  const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
-  const size_t hi = lo + S < n ? lo + S : n;
-  const size_t vlo = lo >> 3, vhi = hi >> 3;
-  const size_t stride = (size_t)bps * blockDim.x;
-  const u32x4* src[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) src[p] = static_cast<const u32x4*>(in.p[p]);
-  u32x4* dst = static_cast<u32x4*>(scratch);
-  size_t v = vlo + (size_t)j * blockDim.x + threadIdx.x;
-  for (; v + stride < vhi; v += 2 * stride) {
-    u32x4 a[P], b[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(src[p] + v);
-#pragma unroll
-    for (int p = 0; p < P; ++p) b[p] = ld4<NTL>(src[p] + v + stride);
-    dst[v] = reduce8<P>(a);
-    dst[v + stride] = reduce8<P>(b);
-  }
-  if (v < vhi) {
-    u32x4 a[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(src[p] + v);
-    dst[v] = reduce8<P>(a);
-  }
-  if (j == 0 && (vhi << 3) + threadIdx.x < hi) {
-    const size_t i = (vhi << 3) + threadIdx.x;
-    const uint16_t* in16[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) in16[p] = static_cast<const uint16_t*>(in.p[p]);
-    static_cast<uint16_t*>(scratch)[i] = reduce1<P>(in16, i);
-  }
-}
-
-template <int P, bool NTS>
-__global__ __launch_bounds__(kBlock) void k_ag(const void* scratch, OutPtrs out, size_t n, size_t S) {
-  const unsigned s = blockIdx.x % P;
-  const unsigned j = blockIdx.x / P;
-  const unsigned bps = gridDim.x / P;
-  const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
-  const size_t hi = lo + S < n ? lo + S : n;
-  const size_t vlo = lo >> 3, vhi = hi >> 3;
-  const size_t stride = (size_t)bps * blockDim.x;
-  const u32x4* src = static_cast<const u32x4*>(scratch);
-  u32x4* dst[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) dst[p] = static_cast<u32x4*>(out.p[p]);
-  size_t v = vlo + (size_t)j * blockDim.x + threadIdx.x;
-  for (; v + stride < vhi; v += 2 * stride) {
-    const u32x4 a = src[v];
-    const u32x4 b = src[v + stride];
-#pragma unroll
-    for (int p = 0; p < P; ++p) st4<NTS>(dst[p] + v, a);
-#pragma unroll
-    for (int p = 0; p < P; ++p) st4<NTS>(dst[p] + v + stride, b);
-  }
-  if (v < vhi) {
-    const u32x4 a = src[v];
-#pragma unroll
-    for (int p = 0; p < P; ++p) st4<NTS>(dst[p] + v, a);
-  }
-  if (j == 0 && (vhi << 3) + threadIdx.x < hi) {
-    const size_t i = (vhi << 3) + threadIdx.x;
-    const uint16_t r = static_cast<const uint16_t*>(scratch)[i];
-#pragma unroll
-    for (int p = 0; p < P; ++p) static_cast<uint16_t*>(out.p[p])[i] = r;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Chunk-major reduce of elements [e0, e1).  Chunk c covers
-// [e0 + c*chunk, min(e0 + (c+1)*chunk, e1)); workgroup b handles slice
-// b % bpc of chunk b / bpc, so workgroups are dispatched in ascending chunk
-// order and no workgroup straddles a chunk boundary.  Each slice is up to
-// kChunkU * blockDim * 8 elements; misaligned slice ends (when e0 or the
-// chunk length is not a multiple of 8) are done element by element.
-constexpr int kChunkU = 2;
-
-template <int P, int NOUT, bool NTL, bool NTS>
-__global__ __launch_bounds__(kBlock) void k_chunk(InPtrs in, OutPtrs out, size_t e0, size_t e1,
-                                                  size_t chunk, unsigned bpc) {
+// Range reduce over elements [e0, e1) of every buffer, chunk-major.
+// Chunk c covers [e0 + c*chunk, min(e0 + (c+1)*chunk, e1)); workgroup b works
+// on tile b % bpc of chunk b / bpc, so tiles never straddle a chunk boundary
+// and chunks are dispatched in ascending order.  A whole-buffer reduce is the
+// single-chunk case.  Tiles are V * blockDim groups of 8 elements; groups are
+// aligned to the buffer base, and a tile end that falls inside a group (e0 or
+// the chunk length not a multiple of 8, or the ragged end of the buffer) is
+// done element by element.  NOUT == 1: one-shot; NOUT == P: fused two-stage
+// (write mode).  Every group is reduced by exactly one lane, which reads it
+// from every input before writing it, so an output equal to an input is safe.
+template <int P, int NOUT, int V, bool NTL, bool NTS>
+__global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, size_t e0, size_t e1,
+                                                     size_t chunk, unsigned bpc) {
+  const size_t span = (size_t)V * blockDim.x * 8;
   const size_t c = blockIdx.x / bpc;
   const unsigned t = blockIdx.x % bpc;
-  const size_t span = (size_t)kChunkU * blockDim.x * 8;
   const size_t c0 = e0 + c * chunk;
   const size_t c1 = c0 + chunk < e1 ? c0 + chunk : e1;
   const size_t b0 = c0 + (size_t)t * span;
@@ -175,24 +51,19 @@ __global__ __launch_bounds__(kBlock) void k_chunk(InPtrs in, OutPtrs out, size_t
   const size_t b1 = b0 + span < c1 ? b0 + span : c1;
   const size_t vb0 = (b0 + 7) >> 3, vb1 = b1 >> 3;
 
-  const u32x4* src[P];
+  u32x4 x[V][P];
 #pragma unroll
-  for (int p = 0; p < P; ++p) src[p] = static_cast<const u32x4*>(in.p[p]);
-  u32x4 x[kChunkU][P];
-  bool ok[kChunkU];
-#pragma unroll
-  for (int u = 0; u < kChunkU; ++u) {
+  for (int u = 0; u < V; ++u) {
     const size_t v = vb0 + threadIdx.x + (size_t)u * blockDim.x;
-    ok[u] = v < vb1;
-    if (ok[u]) {
+    if (v < vb1) {
 #pragma unroll
-      for (int p = 0; p < P; ++p) x[u][p] = ld4<NTL>(src[p] + v);
+      for (int p = 0; p < P; ++p) x[u][p] = ld4<NTL>(static_cast<const u32x4*>(in.p[p]) + v);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kChunkU; ++u) {
-    if (ok[u]) {
-      const size_t v = vb0 + threadIdx.x + (size_t)u * blockDim.x;
+  for (int u = 0; u < V; ++u) {
+    const size_t v = vb0 + threadIdx.x + (size_t)u * blockDim.x;
+    if (v < vb1) {
       const u32x4 r = reduce8<P>(x[u]);
 #pragma unroll
       for (int o = 0; o < NOUT; ++o) st4<NTS>(static_cast<u32x4*>(out.p[o]) + v, r);
@@ -214,66 +85,98 @@ __global__ __launch_bounds__(kBlock) void k_chunk(InPtrs in, OutPtrs out, size_t
 }
 
 // ----------------------------------------------------------------------------
-// Host-side dispatch: P and the non-temporal choices are template
-// parameters, so every instantiation has straight-line per-rank code.
+// Staged two-stage.  Shard s = elements [s*S, min(n, (s+1)*S)), S a multiple
+// of 8.  Workgroup b works on tile b / P of shard b % P: workgroups go to the
+// 8 XCDs round-robin, so with P = 8 shard s is reduced (and later gathered)
+// by XCD s alone -- the one-GPU picture of "rank s owns shard s" -- and the
+// gather re-reads scratch lines through the L2 that wrote them.
+template <int P, bool NTL>
+__global__ __launch_bounds__(kMaxBlock) void k_rs(InPtrs in, void* scratch, size_t n, size_t S) {
+  const unsigned s = blockIdx.x % P;
+  const size_t j = blockIdx.x / P;
+  const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
+  const size_t hi = lo + S < n ? lo + S : n;
+  const size_t v = (lo >> 3) + j * blockDim.x + threadIdx.x;
+  if (v < (hi >> 3)) {
+    u32x4 a[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(static_cast<const u32x4*>(in.p[p]) + v);
+    static_cast<u32x4*>(scratch)[v] = reduce8<P>(a);
+  }
+  if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
+    const size_t i = ((hi >> 3) << 3) + threadIdx.x;
+    const uint16_t* in16[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) in16[p] = static_cast<const uint16_t*>(in.p[p]);
+    static_cast<uint16_t*>(scratch)[i] = reduce1<P>(in16, i);
+  }
+}
 
+template <int P, bool NTS>
+__global__ __launch_bounds__(kMaxBlock) void k_ag(const void* scratch, OutPtrs out, size_t n, size_t S) {
+  const unsigned s = blockIdx.x % P;
+  const size_t j = blockIdx.x / P;
+  const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
+  const size_t hi = lo + S < n ? lo + S : n;
+  const size_t v = (lo >> 3) + j * blockDim.x + threadIdx.x;
+  if (v < (hi >> 3)) {
+    const u32x4 a = static_cast<const u32x4*>(scratch)[v];
+#pragma unroll
+    for (int p = 0; p < P; ++p) st4<NTS>(static_cast<u32x4*>(out.p[p]) + v, a);
+  }
+  if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
+    const size_t i = ((hi >> 3) << 3) + threadIdx.x;
+    const uint16_t r = static_cast<const uint16_t*>(scratch)[i];
+#pragma unroll
+    for (int p = 0; p < P; ++p) static_cast<uint16_t*>(out.p[p])[i] = r;
+  }
+}
+
+// ----------------------------------------------------------------------------
 namespace {
 
-// Grid for the grid-stride kernels: enough workgroups to give every lane one
-// group when the message is small (latency regime), capped at cus*grid_mult
-// for large messages (each lane then loops).
-inline unsigned stream_grid(const Launch& L, size_t nvec) {
-  const size_t want = cdiv(nvec, kBlock);
-  const size_t cap = (size_t)L.cus * (size_t)L.grid_mult;
-  size_t g = want < cap ? want : cap;
-  return (unsigned)(g ? g : 1);
+template <int P, int NOUT, int V>
+hipError_t range_v(const Shape& sh, hipStream_t st, const InPtrs& in, const OutPtrs& out, size_t e0,
+                   size_t e1, size_t chunk) {
+  const size_t span = (size_t)V * sh.block * 8;
+  const size_t bpc = cdiv(chunk, span);
+  const size_t nchunks = cdiv(e1 - e0, chunk);
+  const size_t blocks = nchunks * bpc;
+  if (blocks > 0x7FFFFFFFull || bpc > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
+  const unsigned g = (unsigned)blocks, b = (unsigned)bpc;
+  const dim3 blk(sh.block);
+  if (sh.nt_loads && sh.nt_stores)
+    return launch_k(k_reduce<P, NOUT, V, true, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
+  if (sh.nt_loads)
+    return launch_k(k_reduce<P, NOUT, V, true, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
+  if (sh.nt_stores)
+    return launch_k(k_reduce<P, NOUT, V, false, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
+  return launch_k(k_reduce<P, NOUT, V, false, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
 }
 
 template <int P, int NOUT>
-hipError_t reduce_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_t n) {
-  const unsigned g = stream_grid(L, n >> 3);
-  const int m = (L.nt_loads ? 1 : 0) | (L.nt_stores ? 2 : 0);
-  switch (m) {
-    case 0: return launch_k(k_reduce<P, NOUT, false, false>, g, kBlock, L.stream, in, out, n);
-    case 1: return launch_k(k_reduce<P, NOUT, true, false>, g, kBlock, L.stream, in, out, n);
-    case 2: return launch_k(k_reduce<P, NOUT, false, true>, g, kBlock, L.stream, in, out, n);
-    default: return launch_k(k_reduce<P, NOUT, true, true>, g, kBlock, L.stream, in, out, n);
-  }
+hipError_t range_p(const Shape& sh, hipStream_t st, const InPtrs& in, const OutPtrs& out, size_t e0,
+                   size_t e1, size_t chunk) {
+  if (sh.vec == 2) return range_v<P, NOUT, 2>(sh, st, in, out, e0, e1, chunk);
+  return range_v<P, NOUT, 1>(sh, st, in, out, e0, e1, chunk);
 }
 
 template <int P>
 hipError_t staged_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_t n, void* scratch) {
-  const size_t groups = cdiv(n, 8);
-  const size_t S = cdiv(groups, P) * 8;
-  const size_t shard_vec = S / 8;
-  size_t bps = cdiv(shard_vec, kBlock);
-  const size_t cap = cdiv((size_t)L.cus * (size_t)L.grid_mult, P);
-  if (bps > cap) bps = cap;
-  if (bps == 0) bps = 1;
-  const unsigned g = (unsigned)(bps * P);
-  hipError_t e = L.nt_loads ? launch_k(k_rs<P, true>, g, kBlock, L.stream, in, scratch, n, S)
-                            : launch_k(k_rs<P, false>, g, kBlock, L.stream, in, scratch, n, S);
+  const size_t S = cdiv(cdiv(n, 8), P) * 8;
+  const Shape& rs = L.shape[kRS];
+  const Shape& ag = L.shape[kAG];
+  const size_t bps_rs = cdiv(S / 8, (size_t)rs.block), bps_ag = cdiv(S / 8, (size_t)ag.block);
+  if (bps_rs * P > 0x7FFFFFFFull || bps_ag * P > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+  const unsigned g_rs = (unsigned)(bps_rs * P), g_ag = (unsigned)(bps_ag * P);
+  hipError_t e = rs.nt_loads
+                     ? launch_k(k_rs<P, true>, g_rs, dim3(rs.block), rs.lds, L.stream, in, scratch, n, S)
+                     : launch_k(k_rs<P, false>, g_rs, dim3(rs.block), rs.lds, L.stream, in, scratch, n, S);
   if (e != hipSuccess) return e;
-  return L.nt_stores ? launch_k(k_ag<P, true>, g, kBlock, L.stream, (const void*)scratch, out, n, S)
-                     : launch_k(k_ag<P, false>, g, kBlock, L.stream, (const void*)scratch, out, n, S);
-}
-
-template <int P, int NOUT>
-hipError_t chunk_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_t e0, size_t e1,
-                   size_t chunk) {
-  const size_t span = (size_t)kChunkU * kBlock * 8;
-  const size_t bpc = cdiv(chunk, span);
-  const size_t nchunks = cdiv(e1 - e0, chunk);
-  const size_t blocks = nchunks * bpc;
-  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
-  const int m = (L.nt_loads ? 1 : 0) | (L.nt_stores ? 2 : 0);
-  const unsigned g = (unsigned)blocks, b = (unsigned)bpc;
-  switch (m) {
-    case 0: return launch_k(k_chunk<P, NOUT, false, false>, g, kBlock, L.stream, in, out, e0, e1, chunk, b);
-    case 1: return launch_k(k_chunk<P, NOUT, true, false>, g, kBlock, L.stream, in, out, e0, e1, chunk, b);
-    case 2: return launch_k(k_chunk<P, NOUT, false, true>, g, kBlock, L.stream, in, out, e0, e1, chunk, b);
-    default: return launch_k(k_chunk<P, NOUT, true, true>, g, kBlock, L.stream, in, out, e0, e1, chunk, b);
-  }
+  return ag.nt_stores ? launch_k(k_ag<P, true>, g_ag, dim3(ag.block), ag.lds, L.stream,
+                                 (const void*)scratch, out, n, S)
+                      : launch_k(k_ag<P, false>, g_ag, dim3(ag.block), ag.lds, L.stream,
+                                 (const void*)scratch, out, n, S);
 }
 
 }  // namespace
@@ -294,12 +197,12 @@ hipError_t chunk_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_t
 hipError_t launch_oneshot(const Launch& L, const InPtrs& in, int P, void* out, size_t n) {
   OutPtrs o{};
   o.p[0] = out;
-  AR_DISPATCH_P(P, (reduce_p<PP, 1>(L, in, o, n)))
+  AR_DISPATCH_P(P, (range_p<PP, 1>(L.shape[kOneshot], L.stream, in, o, 0, n, n)))
 }
 
 hipError_t launch_2stage_fused(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                                size_t n) {
-  AR_DISPATCH_P(P, (reduce_p<PP, PP>(L, in, out, n)))
+  AR_DISPATCH_P(P, (range_p<PP, PP>(L.shape[k2Stage], L.stream, in, out, 0, n, n)))
 }
 
 hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
@@ -310,9 +213,9 @@ hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                           size_t e0, size_t e1, size_t chunk_elems, int two_stage) {
   if (two_stage) {
-    AR_DISPATCH_P(P, (chunk_p<PP, PP>(L, in, out, e0, e1, chunk_elems)))
+    AR_DISPATCH_P(P, (range_p<PP, PP>(L.shape[kUbatch], L.stream, in, out, e0, e1, chunk_elems)))
   }
-  AR_DISPATCH_P(P, (chunk_p<PP, 1>(L, in, out, e0, e1, chunk_elems)))
+  AR_DISPATCH_P(P, (range_p<PP, 1>(L.shape[kOneshot], L.stream, in, out, e0, e1, chunk_elems)))
 }
 
 }  // namespace ar

@@ -1,0 +1,170 @@
+"""Summarise rocprofv3 CSV output of bench.py into short text files.
+
+  stats    kernel durations from a --kernel-trace --stats run: per hot-path
+           row, the rocprofv3 average over all dispatches and the average
+           over the timed steps only (warmup steps dropped), next to the
+           rocprofv3 kernel_stats line.
+  traffic  HBM bytes per launch from two --pmc runs (FETCH_SIZE, then
+           WRITE_SIZE; KiB per dispatch), each scaled by what the same
+           counter reads for the plain 1 GiB copies that bench.py
+           --copy-calib appends (known bytes / counted bytes).
+
+Dispatches are labelled by position: every bench step launches the same
+sequence of library kernels (STEP below), so the n-th library dispatch of a
+step is that row's kernel whatever its template arguments.
+
+Usage:
+  python -m tensor_all_reduce_amd.profsum stats DIR --warmup W --command "..."
+  python -m tensor_all_reduce_amd.profsum traffic FETCH_DIR WRITE_DIR --calib-bytes B \
+      --command-fetch "..." --command-write "..."
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 8
+# library kernels launched by one bench step, in launch order
+STEP = (["oneshot", "2stage"] + ["pack"] * P + ["err_init", "rd"] + ["unpack"] * P + ["ubatch"] * 2)
+ROWS = ["oneshot", "2stage", "pack", "rd", "unpack", "ubatch"]
+LAUNCHES = {"oneshot": 1, "2stage": 1, "pack": P, "rd": 1, "unpack": P, "ubatch": 2}
+PREFIX = {"oneshot": "k_reduce", "2stage": "k_reduce", "pack": "k_pack", "err_init": "k_err_init",
+          "rd": "k_rd_fused", "unpack": "k_unpack", "ubatch": "k_reduce"}
+# algorithmic bytes per launch, [16384 x 8192] bf16 per rank buffer
+B = 2 * 16384 * 8192
+ALGO = {"oneshot": (P + 1) * B, "2stage": 2 * P * B, "pack": 3 * B, "rd": 4 * P * B,
+        "unpack": 3 * B, "ubatch": P * B}
+SOURCES = ["tensor_all_reduce_amd/csrc/ar_device.hpp", "tensor_all_reduce_amd/csrc/ar_reduce.hip",
+           "tensor_all_reduce_amd/csrc/ar_fused.hip", "tensor_all_reduce_amd/csrc/ar_api.hip"]
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    for p in SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def one(pattern: str) -> str:
+    hits = glob.glob(pattern)
+    if len(hits) != 1:
+        raise SystemExit(f"expected one file for {pattern}, found {hits}")
+    return hits[0]
+
+
+def label(rows, name_key, order_key):
+    """Library dispatches in launch order, each tagged with its row."""
+    lib = [r for r in rows if "ar::k_" in r[name_key]]
+    lib.sort(key=lambda r: int(r[order_key]))
+    steps = len(lib) // len(STEP)
+    out = []
+    for s in range(steps):
+        for i, row in enumerate(STEP):
+            r = lib[s * len(STEP) + i]
+            if PREFIX[row] not in r[name_key]:
+                raise SystemExit(f"dispatch {s}/{i}: expected {PREFIX[row]}, found {r[name_key][:60]}")
+            out.append((s, row, r))
+    return out, steps
+
+
+def cmd_stats(a):
+    trace = one(os.path.join(a.dir, "*kernel_trace.csv"))
+    stats = one(os.path.join(a.dir, "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(trace)))
+    lab, steps = label(rows, "Kernel_Name", "Dispatch_Id")
+    dur = {r: [] for r in ROWS}
+    dur_all = {r: [] for r in ROWS}
+    span = {}                         # (step) -> [start, end] of the two concurrent ubatch launches
+    for s, row, r in lab:
+        if row not in dur:
+            continue
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        d = (t1 - t0) * 1e-6
+        dur_all[row].append(d)
+        if s >= a.warmup:
+            dur[row].append(d)
+            if row == "ubatch":
+                lo, hi = span.get(s, (t0, t1))
+                span[s] = (min(lo, t0), max(hi, t1))
+    print(f"# rocprofv3 kernel trace of the bench step: P=8, bf16 [16384 x 8192] per rank")
+    print(f"# command: {a.command}")
+    print(f"# {steps} steps traced, first {a.warmup} are warmup; durations in ms per dispatch")
+    print(f"# row      launches/step  mean(timed)  median(timed)  mean(all)  algorithmic GB/s per launch")
+    for row in ROWS:
+        m = statistics.mean(dur[row])
+        gbps = ALGO[row] / (m * 1e-3) / 1e9
+        print(f"{row:9s} {LAUNCHES[row]:3d}  {m:10.4f}  {statistics.median(dur[row]):10.4f}  "
+              f"{statistics.mean(dur_all[row]):10.4f}  {gbps:8.1f}")
+    mk = statistics.mean([(hi - lo) * 1e-6 for lo, hi in span.values()])
+    print(f"# ubatch: the two launches run concurrently on two streams; mean makespan per step "
+          f"{mk:.4f} ms = {2 * ALGO['ubatch'] / (mk * 1e-3) / 1e9:.1f} GB/s for both ubatches")
+    print("#")
+    print("# rocprofv3 --stats kernel_stats.csv (library kernels), all dispatches of the run:")
+    for r in csv.DictReader(open(stats)):
+        if "ar::k_" in r["Name"] or "k_copy" in r["Name"]:
+            name = r["Name"].split("(")[0].replace("void ", "")
+            print(f"#   {name:48s} calls {int(r['Calls']):4d}  avg {float(r['AverageNs']) * 1e-6:.4f} ms  "
+                  f"min {float(r['MinNs']) * 1e-6:.4f}  max {float(r['MaxNs']) * 1e-6:.4f}")
+
+
+def counters(d):
+    f = one(os.path.join(d, "*counter_collection.csv"))
+    rows = list(csv.DictReader(open(f)))
+    lab, _ = label(rows, "Kernel_Name", "Dispatch_Id")
+    per = {r: [] for r in ROWS}
+    for _, row, r in lab:
+        if row in per:
+            per[row].append(float(r["Counter_Value"]) * 1024.0)
+    copy = [float(r["Counter_Value"]) * 1024.0 for r in rows if "k_copy" in r["Kernel_Name"]]
+    if not copy:
+        raise SystemExit(f"{f}: no calibration copy dispatches")
+    return {k: statistics.mean(v) for k, v in per.items()}, statistics.mean(copy), rows[0]["Counter_Name"]
+
+
+def cmd_traffic(a):
+    fetch, fcopy, fname = counters(a.fetch_dir)
+    write, wcopy, wname = counters(a.write_dir)
+    fs, ws = a.calib_bytes / fcopy, a.calib_bytes / wcopy
+    print("# HBM traffic per launch of the bench step kernels (P=8, bf16 [16384 x 8192] per rank)")
+    print(f"# fetch command: {a.command_fetch}")
+    print(f"# write command: {a.command_write}")
+    print(f"# counters: {fname} and {wname}, KiB per dispatch, averaged over every dispatch of the run;")
+    print(f"# scaled by the plain copy of {a.calib_bytes} B: fetch x{fs:.5f}, write x{ws:.5f}")
+    print(f"source_sha256: {sources_sha256()}")
+    print(f"fetch_scale: {fs:.6f}")
+    print(f"write_scale: {ws:.6f}")
+    for row in ROWS:
+        fb, wb = fetch[row] * fs, write[row] * ws
+        print(f"{row}.fetch_bytes_per_launch: {fb:.0f}")
+        print(f"{row}.write_bytes_per_launch: {wb:.0f}")
+        print(f"{row}.hbm_bytes_per_launch: {fb + wb:.0f}")
+        print(f"{row}.algorithmic_bytes_per_launch: {ALGO[row]}")
+        print(f"{row}.traffic_over_algorithmic: {(fb + wb) / ALGO[row]:.4f}")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--warmup", type=int, default=2)
+    s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--calib-bytes", type=float, default=float(1 << 30))
+    t.add_argument("--command-fetch", default="")
+    t.add_argument("--command-write", default="")
+    a = ap.parse_args(argv)
+    return cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

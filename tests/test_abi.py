@@ -162,3 +162,19 @@ def test_binding_raises_on_error():
     with pytest.raises(tar.ARError) as ei:
         tar._check(tar.AR_ERR_ALIAS, "ar_reduce_oneshot")
     assert ei.value.code == tar.AR_ERR_ALIAS
+
+
+def test_launch_shape_roundtrip_and_validation():
+    L = tar.lib()
+    for kind in range(9):
+        before = tar.ar_get_launch_shape(kind)
+        tar.ar_set_launch_shape(kind, 128, 2, 0, 1, 7)
+        assert tar.ar_get_launch_shape(kind) == (128, 2, 0, 1, 7)
+        tar.ar_set_launch_shape(kind, *before)
+        assert tar.ar_get_launch_shape(kind) == before
+    assert L.ar_set_launch_shape(9, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(0, 96, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(0, 64, 3, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(0, 64, 1, 2, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(0, 64, 1, 1, 1, 65) == tar.AR_ERR_INVALID
+    assert L.ar_get_launch_shape(0, None, None, None, None, None) == tar.AR_ERR_INVALID
