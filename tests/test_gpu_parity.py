@@ -421,3 +421,91 @@ def test_ubatch_full_size():
         assert torch.equal(o, outs[0])
     del ins, outs
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ reordered variants (tolerance)
+
+def _f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _within(got_bits, ref_bits, xs, floor_coef):
+    """max relative error 2^-7 (one bf16 ulp) per element, with an absolute
+    floor floor_coef * sum_p |x_p| for elements whose exact sum cancels."""
+    a, b = _f64(got_bits), _f64(ref_bits)
+    absum = sum(np.abs(_f64(x)) for x in xs)
+    rel = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b))
+    floor = floor_coef * absum
+    ok = np.abs(a - b) <= np.maximum(rel, floor)
+    by_floor = int(np.count_nonzero((np.abs(a - b) > rel) & ok))
+    return bool(ok.all()), by_floor
+
+
+P8_GAMMA = 7 * 2.0 ** -24 / (1 - 7 * 2.0 ** -24)
+
+
+@pytest.mark.parametrize("kind", ["normal", "logmag"])
+def test_rd_fp32_carry_vs_sequential(kind):
+    """Tree order with binary32 partials vs the sequential schedule: within
+    one bf16 ulp, floor 2*gamma_7*sum|x| (two binary32 summation orders)."""
+    P, n, seq0 = 8, 128 * HIDDEN, 3
+    xs = synth.rank_buffers(kind, P, n, 3, 71)
+    ref = oracle.reduce_seq(xs)
+    words = [up64(oracle.pack(x, seq0)) for x in xs]
+    out = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+    err = new_err()
+    note(f"rd fp32-carry vs sequential {kind}")
+    tar.ar_rd_schedule(words, out, seq0, err, flags=tar.AR_RD_FP32_CARRY)
+    x = empty16(n)
+    tar.ar_unpack_fused(out[0], x, seq0 + 3, err)
+    torch.cuda.synchronize()
+    assert err_host(err)[0] == 0
+    ok, by_floor = _within(down16(x), ref, xs, 2 * P8_GAMMA)
+    print(f"[gpu] fp32-carry {kind}: {by_floor} of {n} elements judged by the cancellation floor")
+    assert ok
+
+
+@pytest.mark.parametrize("kind", ["normal", "logmag"])
+def test_rd_round_each_step_vs_sequential(kind):
+    """Per-step bf16 rounding vs the sequential schedule: within one bf16 ulp,
+    or the absolute floor (4*2^-8 + 2*gamma_7)*sum|x|: three tree levels each
+    round partials whose magnitudes sum to at most sum|x|, plus the
+    sequential result's own final rounding and binary32 accumulation."""
+    P, n, seq0 = 8, 128 * HIDDEN, 5
+    xs = synth.rank_buffers(kind, P, n, 3, 72)
+    ref = oracle.reduce_seq(xs)
+    words = [up64(oracle.pack(x, seq0)) for x in xs]
+    out = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+    err = new_err()
+    note(f"rd round-each-step vs sequential {kind}")
+    tar.ar_rd_schedule(words, out, seq0, err)
+    x = empty16(n)
+    tar.ar_unpack_fused(out[5], x, seq0 + 3, err)
+    torch.cuda.synchronize()
+    ok, by_floor = _within(down16(x), ref, xs, 4 * 2.0 ** -8 + 2 * P8_GAMMA)
+    print(f"[gpu] round-each-step {kind}: {by_floor} of {n} elements judged by the floor")
+    assert ok
+
+
+def test_permuted_ranks_within_tolerance():
+    """The rank order is part of the schedule: permuting the inputs gives a
+    reordered sum, within one bf16 ulp of the sequential oracle (floor
+    2*gamma_7*sum|x|); integer data is exact in any order."""
+    P, n = 8, 32 * HIDDEN
+    xs = synth.rank_buffers("normal", P, n, 2, 73)
+    ref = oracle.reduce_seq(xs)
+    g = np.random.default_rng(74)
+    for _ in range(3):
+        perm = g.permutation(P)
+        out = empty16(n)
+        note(f"permuted ranks {perm.tolist()}")
+        tar.ar_reduce_oneshot([up16(xs[p]) for p in perm], out)
+        torch.cuda.synchronize()
+        ok, _ = _within(down16(out), ref, xs, 2 * P8_GAMMA)
+        assert ok
+    ints = synth.rank_buffers("integers", P, n, 2, 75)
+    iref = oracle.reduce_seq(ints)
+    out = empty16(n)
+    tar.ar_reduce_oneshot([up16(ints[p]) for p in g.permutation(P)], out)
+    torch.cuda.synchronize()
+    check_full(out, iref, "permuted integers")
