@@ -1,0 +1,149 @@
+"""The oracle's pins catch plausible mistakes: each mutant below is a copy of
+oracle/ar_oracle.c with one planted error (on the CPU, never on a GPU), built
+into its own library and checked with the same kinds of pins as
+test_oracle_pins.py.  Every mutant must fail at least one pin, and the
+unmutated source must pass them all.
+"""
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import exact_ieee as X
+import oracle
+from tensor_all_reduce_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = open(os.path.join(os.path.dirname(HERE), "oracle", "ar_oracle.c")).read()
+GOLDEN = json.load(open(os.path.join(HERE, "golden", "fixtures.json")))
+
+MUTANTS = {
+    "reverse_rank_order": ("""    float acc = orc_widen(xs[0][i]);
+    for (int p = 1; p < P; ++p) acc = acc + orc_widen(xs[p][i]);""",
+                           """    float acc = orc_widen(xs[P - 1][i]);
+    for (int p = P - 2; p >= 0; --p) acc = acc + orc_widen(xs[p][i]);"""),
+    "start_from_plus_zero": ("""    float acc = orc_widen(xs[0][i]);
+    for (int p = 1; p < P; ++p) acc = acc + orc_widen(xs[p][i]);""",
+                             """    float acc = 0.0f;
+    for (int p = 0; p < P; ++p) acc = acc + orc_widen(xs[p][i]);"""),
+    "drop_rank_one": ("for (int p = 1; p < P; ++p) acc = acc + orc_widen(xs[p][i]);",
+                      "for (int p = 2; p < P; ++p) acc = acc + orc_widen(xs[p][i]);"),
+    "ties_away_from_zero": ("if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
+                            "if (rest >= 0x8000u) keep += 1u;"),
+    "truncate": ("if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;",
+                 "(void)rest;"),
+    "nan_not_canonical": ("if (isnan(a)) return 0x7FC0u;", ""),
+    "pack_swapped_halves": ("return ((uint64_t)seq << 32) | ((uint64_t)hi << 16) | (uint64_t)lo;",
+                            "return ((uint64_t)seq << 32) | ((uint64_t)lo << 16) | (uint64_t)hi;"),
+    "unpack_first_index_off_by_one": ("if ((uint64_t)j < err[1]) err[1] = (uint64_t)j;",
+                                      "if ((uint64_t)j + 1 < err[1]) err[1] = (uint64_t)j + 1;"),
+    "rd_partner_descending": ("int q = r ^ (1 << k);", "int q = r ^ (1 << (L - 1 - k));"),
+    "rd_no_step_rounding": ("nxt[(size_t)r * n + 2 * j + h] = fp32_carry ? s : orc_widen(orc_rn(s));",
+                            "nxt[(size_t)r * n + 2 * j + h] = s;"),
+    "rd_seq_not_incremented": ("for (size_t t = 0; t < (size_t)P * W; ++t) seq[t] = seq0 + (uint32_t)k + 1u;",
+                               "for (size_t t = 0; t < (size_t)P * W; ++t) seq[t] = seq0 + (uint32_t)k;"),
+    "shard_not_group_aligned": ("return per * 8;", "return (n + (size_t)P - 1) / (size_t)P;"),
+    "gather_skips_last_shard": ("""    for (int r = 0; r < P; ++r) {                 /* stage 2 */
+        for (int s = 0; s < P; ++s) {""", """    for (int r = 0; r < P; ++r) {                 /* stage 2 */
+        for (int s = 0; s < P - 1; ++s) {"""),
+    "chunk_drops_partial_tail": ("for (size_t c0 = e0; c0 < e1; c0 += chunk_elems) {",
+                                 "for (size_t c0 = e0; c0 + chunk_elems <= e1; c0 += chunk_elems) {"),
+}
+
+
+def build_variant(tmp_path, name, src):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"lib{name}.so"
+    c.write_text(src)
+    subprocess.run(["gcc", *oracle.GCC_FLAGS, str(c), "-o", str(so), "-lm"], check=True,
+                   capture_output=True)
+    return str(so)
+
+
+def with_lib(path):
+    """Point the oracle wrappers at another build of the C source."""
+    saved = oracle._lib, oracle._LIB_PATH
+    oracle._lib = None
+    oracle._LIB_PATH = path
+    oracle.lib()
+    return saved
+
+
+def restore(saved):
+    oracle._lib, oracle._LIB_PATH = saved
+
+
+def h16(s):
+    return int(s, 16)
+
+
+def pins_failed():
+    """Run a compact set of pins against the current oracle build; return the
+    names of those that fail."""
+    failed = []
+
+    def check(name, cond):
+        if not cond:
+            failed.append(name)
+
+    try:
+        ok = all(int(oracle.reduce_seq([np.array([h16(x)], np.uint16) for x in c["ranks"]])[0]) == h16(c["seq"])
+                 for c in GOLDEN["reduce"])
+        check("golden_reduce", ok)
+        for c in GOLDEN["shard"]:
+            check("golden_shard", oracle.shard_len(c["P"], c["n"]) == c["S"])
+        # exact model brute force with special values
+        xs = synth.rank_buffers("logmag", 4, 40, 930)
+        xs[1][:6] = np.array([0x7F81, 0x8000, 0x0001, 0x7F7F, 0xFF80, 0x3B80], np.uint16)
+        got = oracle.reduce_seq(xs)
+        check("exact_model", all(int(got[i]) == X.seq_sum([int(x[i]) for x in xs]) for i in range(40)))
+        # two-stage and ubatch equal one-shot (ragged sizes, odd chunks)
+        ys = synth.rank_buffers("normal", 8, 30 * 72, 931)
+        seq = oracle.reduce_seq(ys)
+        check("2stage", all(np.array_equal(o, seq) for o in oracle.reduce_2stage(ys)))
+        check("ubatch", all(np.array_equal(o, seq) for o in oracle.reduce_ubatch(ys, 30, 72, 2, [7, 23], 2056)))
+        # pack layout, round trip, exact mismatch counts
+        for c in GOLDEN["pack"]:
+            w = oracle.pack(np.array([h16(v) for v in c["x"]], np.uint16), h16(c["seq"]))
+            check("golden_pack", [f"{int(v):016X}" for v in w] == c["words"])
+        x = synth.normal(4000, 932)
+        w = oracle.pack(x, 5)
+        w[[17, 901, 1500]] ^= np.uint64(1) << np.uint64(33)
+        y, err = oracle.unpack(w, 5)
+        check("unpack_counts", np.array_equal(y, x) and int(err[0]) == 3 and int(err[1]) == 17)
+        # RD: golden R1/R2 fixture, exact tree, output sequence numbers
+        for c in GOLDEN["rd"]:
+            words = [oracle.pack(np.array([h16(b), 0], np.uint16), 3) for b in c["ranks"]]
+            for carry, key in ((False, "r1"), (True, "r2")):
+                outs, _ = oracle.rd(words, 3, carry)
+                check("golden_rd", int(outs[0][0]) & 0xFFFF == h16(c[key]))
+        zs = synth.rank_buffers("logmag", 8, 24, 933)
+        outs, rd_err = oracle.rd([oracle.pack(z, 0xFFFFFFFE) for z in zs], 0xFFFFFFFE)
+        dat, e = oracle.unpack(outs[0], 1)
+        check("rd_seq", int(e[0]) == 0 and int(rd_err[0]) == 0)
+        check("rd_tree", all(int(dat[i]) == X.tree_sum([int(z[i]) for z in zs], True) for i in range(24)))
+    except Exception as ex:  # a mutant that crashes a wrapper counts as caught
+        failed.append(f"exception: {ex!r}")
+    return failed
+
+
+def test_unmutated_source_passes(tmp_path):
+    saved = with_lib(build_variant(tmp_path, "clean", SRC))
+    try:
+        assert pins_failed() == []
+    finally:
+        restore(saved)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) == 1, f"mutation site for {name} not found exactly once"
+    saved = with_lib(build_variant(tmp_path, name, SRC.replace(old, new)))
+    try:
+        failed = pins_failed()
+    finally:
+        restore(saved)
+    assert failed, f"mutant {name} passed every pin"
