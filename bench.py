@@ -335,6 +335,46 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     res["latency"] = lat
     log("latency measured")
 
+    # the same calls captured in one HIP graph (100 calls per graph), which
+    # removes the per-launch host cost from each call
+    glat = {}
+    side = torch.cuda.Stream()
+    side.wait_stream(main_s)
+    for T in (8, 32, 128):
+        m = T * HIDDEN
+        xi = [x[:m] for x in ins]
+        xo = [o[:m] for o in outs]
+        key = f"{2 * m // 1024}KiB"
+        glat[key] = {}
+        for name in ("oneshot", "2stage_fused"):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                if name == "oneshot":
+                    tar.ar_reduce_oneshot(xi, xo[0], stream=side)
+                else:
+                    tar.ar_reduce_2stage(xi, xo, stream=side)
+                side.synchronize()
+                with torch.cuda.graph(g, stream=side):
+                    for _ in range(100):
+                        if name == "oneshot":
+                            tar.ar_reduce_oneshot(xi, xo[0], stream=side)
+                        else:
+                            tar.ar_reduce_2stage(xi, xo, stream=side)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(main_s)
+            for _ in range(20):
+                g.replay()
+            e1.record(main_s)
+            torch.cuda.synchronize()
+            glat[key][name] = {"us_per_call": round(e0.elapsed_time(e1) * 1e3 / 2000, 2)}
+            del g
+    res["latency_hip_graph"] = glat
+    log("graph latency measured")
+
     # ubatch reduce at its own shape: [16384 x 16384] per rank, 2 streams, 1 MiB chunks
     from tensor_all_reduce_amd import synth
     m = UB_ROWS * UB_HIDDEN

@@ -13,7 +13,7 @@
 // {data_j, seq, data_j+1, seq}.
 //
 // Validation: every lane checks its words' sequence numbers; a wavefront
-// folds its 64 lanes' verdicts with one ballot.  When the whole wavefront is
+// folds its 64 lanes' flags with one ballot.  When the whole wavefront is
 // clean (the normal case) that is the only cost; otherwise one ballot per
 // word slot gives the wave-uniform count and first index, and one lane
 // issues two atomics.

@@ -509,3 +509,57 @@ def test_permuted_ranks_within_tolerance():
     tar.ar_reduce_oneshot([up16(ints[p]) for p in g.permutation(P)], out)
     torch.cuda.synchronize()
     check_full(out, iref, "permuted integers")
+
+
+# ------------------------------------------------------------ HIP graph capture
+
+def test_graph_capture_replays():
+    """The hot-path calls (error-record init, one-shot, fused two-stage, pack,
+    recursive doubling, unpack) captured in one HIP graph; the graph is
+    replayed several times with fresh inputs copied in and eager library
+    calls between replays, and every replay is checked against the oracle."""
+    P, n = 8, 32 * HIDDEN
+    ins = [empty16(n) for _ in range(P)]
+    out1 = empty16(n)
+    outs = [empty16(n) for _ in range(P)]
+    words = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+    rdo = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+    x = empty16(n)
+    err = torch.empty(2, dtype=torch.int64, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    note("graph capture")
+    with torch.cuda.stream(side):
+        # warm the library's one-time initialisation outside the capture
+        tar.ar_err_init(err, stream=side)
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            tar.ar_err_init(err, stream=side)
+            tar.ar_reduce_oneshot(ins, out1, stream=side)
+            tar.ar_reduce_2stage(ins, outs, stream=side)
+            for r in range(P):
+                tar.ar_pack_fused(ins[r], words[r], 9, stream=side)
+            tar.ar_rd_schedule(words, rdo, 9, err, stream=side)
+            tar.ar_unpack_fused(rdo[2], x, 12, err, stream=side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        xs = synth.rank_buffers("normal", P, n, 60, rep)
+        for t, h in zip(ins, xs):
+            t.copy_(up16(h))
+        # eager library work between replays, on the default stream
+        scratch_out = empty16(n)
+        tar.ar_reduce_oneshot(ins[::-1], scratch_out)
+        torch.cuda.synchronize()
+        note(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.reduce_seq(xs)
+        check_full(out1, ref, f"graph replay {rep} oneshot")
+        for o in outs:
+            check_full(o, ref, f"graph replay {rep} 2stage")
+        rw, _ = oracle.rd([oracle.pack(v, 9) for v in xs], 9)
+        want, _ = oracle.unpack(rw[2], 12)
+        check_full(x, want, f"graph replay {rep} rd")
+        assert err_host(err) == (0, 2 ** 64 - 1)
+        check_full(scratch_out, oracle.reduce_seq(xs[::-1]), "eager between replays")
