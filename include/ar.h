@@ -128,6 +128,31 @@ int ar_unpack_fused(const uint64_t* words, void* x, size_t n, uint32_t expected_
                     uint64_t* d_err, void* stream);
 
 /*
+ * Unpack with a bounded wait for the producer ([NVRAR] Optimizations,
+ * "Fused Payloads" and "Sequence-Number Synchronization": the receiver polls
+ * its buffer until each payload carries the expected sequence number; no
+ * separate signal).  Meant for a producer that writes `words` concurrently,
+ * from another stream of the same device (e.g. ar_pack_fused).  Each word is
+ * read with a 64-bit agent-scope atomic load, so a word that shows the
+ * expected sequence number also shows its data.  A wavefront re-polls its
+ * words (sleeping briefly between polls) until all carry expected_seq or
+ * until it has polled max_spins times in total; then it writes the data it
+ * holds.  The kernel runs on a persistent grid of a few workgroups per CU and
+ * requests no LDS, so the producer can always be scheduled beside it.
+ *   d_err    as ar_unpack_fused: words whose sequence number still differs
+ *            after the wait are counted, with the first index.
+ *   max_spins >= 1.  Every wait is bounded: the call always completes.
+ * The producer must be able to run while this kernel waits: HIP maps streams
+ * onto a few hardware queues, and a producer queued behind this call on the
+ * same queue only starts after the wait has run out (its words then count as
+ * mismatches).  Queue the producer first, or on a stream known to be on
+ * another queue.
+ * Errors: as ar_unpack_fused, plus AR_ERR_INVALID for max_spins == 0.
+ */
+int ar_unpack_fused_wait(const uint64_t* words, void* x, size_t n, uint32_t expected_seq,
+                         uint32_t max_spins, uint64_t* d_err, void* stream);
+
+/*
  * Recursive-doubling combine over P = 2, 4 or 8 payload buffers ([NVRAR]
  * Methodology 3, phase 2 "Inter-node Recursive-Doubling", and Optimizations
  * "Fused Payloads" / "Sequence-Number Synchronization").
@@ -198,6 +223,8 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 #define AR_KERNEL_UNPACK   6   /* ar_unpack_fused                            */
 #define AR_KERNEL_RD       7   /* ar_rd_schedule, fused                      */
 #define AR_KERNEL_RDSTEP   8   /* ar_rd_schedule, staged (per step)          */
+#define AR_KERNEL_UNPACK_WAIT 9 /* ar_unpack_fused_wait; wg_per_cu sets the
+                                   persistent grid, no LDS is requested      */
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu);
 int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
                         int* wg_per_cu);

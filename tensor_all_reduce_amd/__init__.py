@@ -25,7 +25,8 @@ __all__ = [
     "AR_ERR_HIP", "AR_MAX_RANKS", "AR_VARIANT_ONESHOT", "AR_VARIANT_2STAGE",
     "AR_RD_STAGED", "AR_RD_FP32_CARRY", "ar_set_launch_shape", "ar_get_launch_shape",
     "AR_KERNEL_ONESHOT", "AR_KERNEL_2STAGE", "AR_KERNEL_UBATCH", "AR_KERNEL_RS", "AR_KERNEL_AG",
-    "AR_KERNEL_PACK", "AR_KERNEL_UNPACK", "AR_KERNEL_RD", "AR_KERNEL_RDSTEP",
+    "AR_KERNEL_PACK", "AR_KERNEL_UNPACK", "AR_KERNEL_RD", "AR_KERNEL_RDSTEP", "AR_KERNEL_UNPACK_WAIT",
+    "ar_unpack_fused_wait",
 ]
 
 AR_OK = 0
@@ -48,6 +49,7 @@ AR_KERNEL_PACK = 5
 AR_KERNEL_UNPACK = 6
 AR_KERNEL_RD = 7
 AR_KERNEL_RDSTEP = 8
+AR_KERNEL_UNPACK_WAIT = 9
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libarcore.so")
@@ -87,6 +89,8 @@ def lib():
         L.ar_pack_fused.argtypes = [_vp, _vp, _sz, _u32, _vp]
         L.ar_unpack_fused.restype = ctypes.c_int
         L.ar_unpack_fused.argtypes = [_vp, _vp, _sz, _u32, _vp, _vp]
+        L.ar_unpack_fused_wait.restype = ctypes.c_int
+        L.ar_unpack_fused_wait.argtypes = [_vp, _vp, _sz, _u32, _u32, _vp, _vp]
         L.ar_rd_schedule.restype = ctypes.c_int
         L.ar_rd_schedule.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz,
                                      _u32, _vp, ctypes.c_int, _vp, _vp]
@@ -194,6 +198,18 @@ def ar_unpack_fused(words, x, expected_seq: int, d_err, n: int | None = None, st
     (ep,) = _bufs([d_err], 8, "d_err", 2)
     _check(lib().ar_unpack_fused(wp, xp, n, int(expected_seq) & 0xFFFFFFFF, ep, _stream(stream)),
            "ar_unpack_fused")
+
+
+def ar_unpack_fused_wait(words, x, expected_seq: int, d_err, max_spins: int = 1 << 20,
+                         n: int | None = None, stream=None) -> None:
+    """Unpack, waiting (at most max_spins polls per wavefront) for a
+    concurrent producer to write payloads carrying expected_seq."""
+    n = x.numel() if n is None else int(n)
+    (wp,) = _bufs([words], 8, "words", n // 2)
+    (xp,) = _bufs([x], 2, "x", n)
+    (ep,) = _bufs([d_err], 8, "d_err", 2)
+    _check(lib().ar_unpack_fused_wait(wp, xp, n, int(expected_seq) & 0xFFFFFFFF, int(max_spins), ep,
+                                      _stream(stream)), "ar_unpack_fused_wait")
 
 
 def rd_mailbox_words(P: int, n: int) -> int:

@@ -45,10 +45,11 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {128, 1, 0, 1, 12, 0},  // unpack, 2 -> 1
     {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
     {64, 1, 1, 1, 8, 0},    // staged recursive-doubling step, 8 -> 8
+    {256, 1, 0, 0, 1, 0},   // waiting unpack: 1 persistent workgroup per CU
 };
 constexpr const char* kShapeEnv[ar::kKinds] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
-    "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP"};
+    "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT"};
 
 std::mutex g_mu;
 DevInfo g_dev[kMaxDevices];
@@ -254,6 +255,20 @@ int ar_unpack_fused(const uint64_t* words, void* x, size_t n, uint32_t expected_
   ar::Launch L;
   if ((rc = resolve(&L, stream))) return rc;
   return hip_status(ar::launch_unpack(L, words, x, n, expected_seq, d_err));
+}
+
+int ar_unpack_fused_wait(const uint64_t* words, void* x, size_t n, uint32_t expected_seq,
+                         uint32_t max_spins, uint64_t* d_err, void* stream) {
+  if (!x || !words || (n & 1u) || mul_overflows(n, 4) || max_spins == 0) return AR_ERR_INVALID;
+  int rc = check_err(d_err);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(words)) return AR_ERR_ALIGN;
+  const Span sx = span_of(x, n * 2), sw = span_of(words, n * 4), se = span_of(d_err, 16);
+  if (overlap(sx, sw) || overlap(se, sx) || overlap(se, sw)) return AR_ERR_ALIAS;
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  return hip_status(ar::launch_unpack_wait(L, words, x, n, expected_seq, max_spins, d_err));
 }
 
 int ar_rd_schedule(const uint64_t* const* in_words, uint64_t* const* out_words, int P, size_t n,

@@ -36,6 +36,7 @@ enum Kind {
   kUnpack,       // 2 -> 1 (payload words -> bf16)
   kRD,           // fused recursive doubling, 8 payloads -> 8 payloads
   kRDStep,       // staged recursive-doubling step
+  kUnpackWait,   // unpack that waits for the producer (persistent grid, no LDS request)
   kKinds
 };
 
@@ -70,6 +71,8 @@ hipError_t launch_rd_fused(const Launch& L, const WordIn& in, const WordOut& out
                            size_t n, uint32_t seq0, int fp32_carry, uint64_t* d_err);
 hipError_t launch_rd_staged(const Launch& L, const WordIn& in, const WordOut& out, int P,
                             size_t n, uint32_t seq0, uint64_t* mailbox, uint64_t* d_err);
+hipError_t launch_unpack_wait(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,
+                              uint32_t max_spins, uint64_t* d_err);
 hipError_t launch_err_init(const Launch& L, uint64_t* d_err);
 
 }  // namespace ar

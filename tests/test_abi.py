@@ -118,6 +118,16 @@ def test_pack_unpack_validation():
     assert L.ar_unpack_fused(A, B, 0, 1, C, None) == tar.AR_OK
 
 
+def test_unpack_wait_validation():
+    L = tar.lib()
+    assert L.ar_unpack_fused_wait(A, B, 8, 1, 0, C, None) == tar.AR_ERR_INVALID   # max_spins 0
+    assert L.ar_unpack_fused_wait(A, B, 7, 1, 5, C, None) == tar.AR_ERR_INVALID   # odd n
+    assert L.ar_unpack_fused_wait(A, B, 8, 1, 5, None, None) == tar.AR_ERR_INVALID
+    assert L.ar_unpack_fused_wait(A, B + 2, 8, 1, 5, C, None) == tar.AR_ERR_ALIGN
+    assert L.ar_unpack_fused_wait(A, A + 16, 8, 1, 5, C, None) == tar.AR_ERR_ALIAS
+    assert L.ar_unpack_fused_wait(A, B, 0, 1, 5, C, None) == tar.AR_OK
+
+
 def test_rd_validation():
     L = tar.lib()
     ins3 = arr(A, A + 0x1000, A + 0x2000)
@@ -166,13 +176,13 @@ def test_binding_raises_on_error():
 
 def test_launch_shape_roundtrip_and_validation():
     L = tar.lib()
-    for kind in range(9):
+    for kind in range(10):
         before = tar.ar_get_launch_shape(kind)
         tar.ar_set_launch_shape(kind, 128, 2, 0, 1, 7)
         assert tar.ar_get_launch_shape(kind) == (128, 2, 0, 1, 7)
         tar.ar_set_launch_shape(kind, *before)
         assert tar.ar_get_launch_shape(kind) == before
-    assert L.ar_set_launch_shape(9, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(10, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 96, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 3, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 1, 2, 1, 0) == tar.AR_ERR_INVALID
