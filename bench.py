@@ -125,6 +125,12 @@ def main():
                                  ctypes.POINTER(ctypes.c_double)]
     blib.arb_copy.restype = ctypes.c_int
     blib.arb_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    blib.arb_alu.restype = ctypes.c_int
+    blib.arb_alu.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    blib.arb_consume_chunks.restype = ctypes.c_int
+    blib.arb_consume_chunks.argtypes = [vp, ctypes.c_uint32, vp, vp, ctypes.c_size_t, ctypes.c_size_t,
+                                        ctypes.c_uint32, ctypes.c_uint32, vp, ctypes.c_int, vp,
+                                        ctypes.c_int, vp]
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -375,6 +381,8 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     res["latency_hip_graph"] = glat
     log("graph latency measured")
 
+    res.update(overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1))
+
     # ubatch reduce at its own shape: [16384 x 16384] per rank, 2 streams, 1 MiB chunks
     from tensor_all_reduce_amd import synth
     m = UB_ROWS * UB_HIDDEN
@@ -407,6 +415,106 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     del uin, uout
     torch.cuda.empty_cache()
     return res
+
+
+def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
+    """Two-stream overlap on one GPU.
+
+    tbo: the two-stage reduce of one 8192-row ubatch on the comm stream s0,
+    beside an ALU-bound stand-in for the partner ubatch's compute on s1 sized
+    to take about as long; overlap = (t_reduce + t_compute - t_both) /
+    min(t_reduce, t_compute).
+    chunk_pipeline: the same reduce with per-chunk completion flags, and a
+    consumer on s1 that takes each 1 MiB chunk of one output as soon as its
+    flag is set, compared with running the two one after the other.  Two
+    consumers: a plain copy (HBM-bound like the reduce, so the two share the
+    bandwidth and overlap cannot shorten the makespan), and the copy plus
+    FMA work per word sized to take about as long as the reduce (the case
+    per-chunk flags are for: the consumer's compute hides the reduce)."""
+    rows = ROWS // 2
+    m = rows * HIDDEN
+    xi = [x[:m] for x in ins]
+    xo = [o[:m] for o in outs]
+    alu_grid = 512
+    alu_out = torch.empty(alu_grid * 256, dtype=torch.float32, device=dev)
+    dst = torch.empty(m, dtype=torch.int16, device=dev)
+    nchunks = tar.ubatch_chunk_count(rows, HIDDEN, 1, None, CHUNK_BYTES)
+    done = torch.zeros(nchunks, dtype=torch.int32, device=dev)
+    tiles = torch.zeros(nchunks, dtype=torch.int32, device=dev)
+    timeouts = torch.zeros(1, dtype=torch.int32, device=dev)
+    epoch = [0]
+
+    def reduce(flags=False):
+        if flags:
+            epoch[0] += 1
+            tar.ar_reduce_ubatch_flags(xi, xo, rows, HIDDEN, done, tiles, epoch[0], 1, None, CHUNK_BYTES,
+                                       tar.AR_VARIANT_2STAGE, [s0])
+        else:
+            tar.ar_reduce_ubatch(xi, xo, rows, HIDDEN, 1, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, [s0])
+
+    def compute(iters):
+        if blib.arb_alu(alu_out.data_ptr(), iters, alu_grid, s1.cuda_stream) != 0:
+            raise RuntimeError("arb_alu failed")
+
+    cons_grid = 2 * torch.cuda.get_device_properties(dev).multi_processor_count   # most a waiting consumer may take
+    sink = torch.zeros(cons_grid * 256, dtype=torch.float32, device=dev)
+
+    def consume(work=0):
+        if blib.arb_consume_chunks(done.data_ptr(), epoch[0], xo[0].data_ptr(), dst.data_ptr(), m,
+                                   CHUNK_BYTES // 2, 0, 1 << 24, timeouts.data_ptr(), work,
+                                   sink.data_ptr() if work else None, cons_grid, s1.cuda_stream) != 0:
+            raise RuntimeError("arb_consume_chunks failed")
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(reps):
+            s0.wait_stream(main_s)
+            s1.wait_stream(main_s)
+            fn()
+            main_s.wait_stream(s0)
+            main_s.wait_stream(s1)
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_r = timed(lambda: reduce())
+    iters = 4096
+    t_c = timed(lambda: compute(iters))
+    iters = max(64, int(iters * t_r / t_c))
+    t_c = timed(lambda: compute(iters))
+    t_both = timed(lambda: (reduce(), compute(iters)))
+    ov = (t_r + t_c - t_both) / min(t_r, t_c)
+    t_rf = timed(lambda: reduce(True))
+    t_cons = timed(lambda: consume())           # flags already set: the consumer alone
+    t_pipe = timed(lambda: (reduce(True), consume()))
+    work = 64
+    t_w = timed(lambda: consume(work))
+    for _ in range(2):                          # the copy part does not scale with work
+        work = max(1, int(work * t_rf / t_w))
+        t_w = timed(lambda: consume(work))
+    t_wpipe = timed(lambda: (reduce(True), consume(work)))
+    torch.cuda.synchronize()
+    if int(timeouts.item()) != 0:
+        raise RuntimeError("chunk consumer timed out")
+    ov_w = (t_rf + t_w - t_wpipe) / min(t_rf, t_w)
+    log(f"overlap: reduce {t_r:.3f} ms, compute {t_c:.3f} ms, both {t_both:.3f} ms -> {ov:.2f}; "
+        f"chunk pipeline: copy consumer {t_pipe:.3f} ms vs serial {t_rf + t_cons:.3f} ms; "
+        f"compute consumer {t_wpipe:.3f} ms vs serial {t_rf + t_w:.3f} ms -> {ov_w:.2f}")
+    return {"tbo_overlap": {"reduce_ms": round(t_r, 4), "compute_ms": round(t_c, 4),
+                            "both_ms": round(t_both, 4), "overlap_fraction": round(ov, 3),
+                            "reduce": "two-stage, one ubatch of [8192 x 8192] x 8 ranks, 1 MiB chunks",
+                            "compute": f"ALU stand-in, {alu_grid} x 256 lanes, {iters} FMA rounds"},
+            "chunk_pipeline": {"flagged_reduce_ms": round(t_rf, 4), "chunks": nchunks,
+                               "copy_consumer": {"alone_ms": round(t_cons, 4),
+                                                 "serial_ms": round(t_rf + t_cons, 4),
+                                                 "pipelined_ms": round(t_pipe, 4)},
+                               "compute_consumer": {"fma_rounds_per_16B": work, "alone_ms": round(t_w, 4),
+                                                    "serial_ms": round(t_rf + t_w, 4),
+                                                    "pipelined_ms": round(t_wpipe, 4),
+                                                    "overlap_fraction": round(ov_w, 3)}}}
 
 
 def cpu_baseline(args, np):

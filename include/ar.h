@@ -225,9 +225,50 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 #define AR_KERNEL_RDSTEP   8   /* ar_rd_schedule, staged (per step)          */
 #define AR_KERNEL_UNPACK_WAIT 9 /* ar_unpack_fused_wait; wg_per_cu sets the
                                    persistent grid, no LDS is requested      */
+#define AR_KERNEL_UBATCH_FLAGS 10 /* ar_reduce_ubatch_flags (both variants)  */
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu);
 int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
                         int* wg_per_cu);
+
+/*
+ * Chunked ubatch reduce with per-chunk completion flags ([NVRAR]
+ * Optimizations, "Chunked Non-blocking Communication": the next stage starts
+ * on a chunk as soon as it is reduced; [TBO-AR] pull request overview: the
+ * all-reduce of a ubatch runs beside the partner's compute).  Same work and
+ * arguments as ar_reduce_ubatch, plus:
+ *   chunk_done   device uint32[n_flags]: entry g is set to `epoch` once
+ *                chunk g has been written to every output.  The outputs of a
+ *                flagged call are written through to device-coherent memory
+ *                (not left dirty in one XCD's L2), and the flag is stored with
+ *                a device-scope store only after every workgroup of the chunk
+ *                has had its stores acknowledged, so publishing costs no L2
+ *                writeback.  Chunks are numbered across ubatches in order,
+ *                ubatch 0's first.  A consumer on any stream of the device
+ *                polls chunk_done[g] with device-scope loads until it equals
+ *                epoch, then performs a device-scope acquire (fence or
+ *                acquire load) before reading chunk g of the outputs.  Poll
+ *                with relaxed loads and acquire once: an acquire on every
+ *                poll invalidates the XCD's L2 each time.  A waiting consumer
+ *                must leave the GPU room for the producer's workgroups (a
+ *                grid that fills every wave slot keeps them from starting),
+ *                and should be queued after the producer: streams can share
+ *                a hardware queue.
+ *   chunk_tiles  device uint32[n_flags], zero before the first call; every
+ *                call leaves it zero again, so it is reused without
+ *                re-initialisation.  Calls that overlap in time must not
+ *                share it.
+ *   n_flags      entries in each array: at least the total chunk count,
+ *                the sum over ubatches of ceil(rows_u * hidden * 2 / chunk_bytes).
+ *   epoch        nonzero value published by this call (e.g. a call counter).
+ * Errors: as ar_reduce_ubatch, plus AR_ERR_INVALID for epoch == 0, a NULL or
+ *         too short array, AR_ERR_ALIGN for arrays not 4-byte aligned, and
+ *         AR_ERR_ALIAS if the arrays overlap each other or a data buffer.
+ */
+int ar_reduce_ubatch_flags(const void* const* ins, void* const* outs, int P, size_t rows,
+                           size_t hidden, int n_ubatch, const size_t* ubatch_rows,
+                           size_t chunk_bytes, int variant, void* const* streams,
+                           uint32_t* chunk_done, uint32_t* chunk_tiles, size_t n_flags,
+                           uint32_t epoch);
 
 /*
  * Initialise an error record for ar_unpack_fused / ar_rd_schedule on

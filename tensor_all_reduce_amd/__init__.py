@@ -26,7 +26,7 @@ __all__ = [
     "AR_RD_STAGED", "AR_RD_FP32_CARRY", "ar_set_launch_shape", "ar_get_launch_shape",
     "AR_KERNEL_ONESHOT", "AR_KERNEL_2STAGE", "AR_KERNEL_UBATCH", "AR_KERNEL_RS", "AR_KERNEL_AG",
     "AR_KERNEL_PACK", "AR_KERNEL_UNPACK", "AR_KERNEL_RD", "AR_KERNEL_RDSTEP", "AR_KERNEL_UNPACK_WAIT",
-    "ar_unpack_fused_wait",
+    "AR_KERNEL_UBATCH_FLAGS", "ar_unpack_fused_wait", "ar_reduce_ubatch_flags", "ubatch_chunk_count",
 ]
 
 AR_OK = 0
@@ -50,6 +50,7 @@ AR_KERNEL_UNPACK = 6
 AR_KERNEL_RD = 7
 AR_KERNEL_RDSTEP = 8
 AR_KERNEL_UNPACK_WAIT = 9
+AR_KERNEL_UBATCH_FLAGS = 10
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libarcore.so")
@@ -98,6 +99,10 @@ def lib():
         L.ar_reduce_ubatch.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz,
                                        _sz, ctypes.c_int, ctypes.POINTER(_sz), _sz, ctypes.c_int,
                                        ctypes.POINTER(_vp)]
+        L.ar_reduce_ubatch_flags.restype = ctypes.c_int
+        L.ar_reduce_ubatch_flags.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz,
+                                             _sz, ctypes.c_int, ctypes.POINTER(_sz), _sz, ctypes.c_int,
+                                             ctypes.POINTER(_vp), _vp, _vp, _sz, _u32]
         L.ar_err_init.restype = ctypes.c_int
         L.ar_err_init.argtypes = [_vp, _vp]
         L.ar_set_launch_shape.restype = ctypes.c_int
@@ -253,6 +258,42 @@ def ar_reduce_ubatch(ins: Sequence, outs: Sequence, rows: int, hidden: int, n_ub
     _check(lib().ar_reduce_ubatch(_ptr_array(ip), _ptr_array(op), len(ip), int(rows), int(hidden),
                                   int(n_ubatch), ub, int(chunk_bytes), int(variant), sp),
            "ar_reduce_ubatch")
+
+
+def ubatch_chunk_count(rows: int, hidden: int, n_ubatch: int = 2, ubatch_rows=None,
+                       chunk_bytes: int = 1 << 20) -> int:
+    """Total chunks of a ubatch reduce (size of the flag arrays)."""
+    if ubatch_rows is None:
+        ubatch_rows = [rows // n_ubatch] * (n_ubatch - 1)
+        ubatch_rows.append(rows - sum(ubatch_rows))
+    ce = chunk_bytes // 2
+    return sum((int(r) * hidden + ce - 1) // ce for r in ubatch_rows)
+
+
+def ar_reduce_ubatch_flags(ins: Sequence, outs: Sequence, rows: int, hidden: int, chunk_done,
+                           chunk_tiles, epoch: int, n_ubatch: int = 2,
+                           ubatch_rows: Sequence[int] | None = None, chunk_bytes: int = 1 << 20,
+                           variant: int = AR_VARIANT_2STAGE, streams: Sequence | None = None) -> None:
+    """ar_reduce_ubatch that also publishes done[chunk] = epoch per chunk."""
+    n = int(rows) * int(hidden)
+    ip = _bufs(ins, 2, "ins", n)
+    op = _bufs(outs, 2, "outs", n)
+    if streams is None:
+        streams = [None] * n_ubatch
+    if len(streams) != n_ubatch:
+        raise ValueError("need one stream per ubatch")
+    sp = _ptr_array([_stream(s) for s in streams])
+    ub = None
+    if ubatch_rows is not None:
+        if len(ubatch_rows) != n_ubatch:
+            raise ValueError("need one row count per ubatch")
+        ub = (_sz * n_ubatch)(*[int(r) for r in ubatch_rows])
+    (dp,) = _bufs([chunk_done], 4, "chunk_done")
+    (tp,) = _bufs([chunk_tiles], 4, "chunk_tiles")
+    nf = min(chunk_done.numel(), chunk_tiles.numel())
+    _check(lib().ar_reduce_ubatch_flags(_ptr_array(ip), _ptr_array(op), len(ip), int(rows), int(hidden),
+                                        int(n_ubatch), ub, int(chunk_bytes), int(variant), sp, dp, tp,
+                                        nf, int(epoch) & 0xFFFFFFFF), "ar_reduce_ubatch_flags")
 
 
 def ar_err_init(d_err, stream=None) -> None:

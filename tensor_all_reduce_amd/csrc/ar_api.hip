@@ -46,10 +46,12 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
     {64, 1, 1, 1, 8, 0},    // staged recursive-doubling step, 8 -> 8
     {256, 1, 0, 0, 1, 0},   // waiting unpack: 1 persistent workgroup per CU
+    {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few fences and counter atomics per chunk
 };
 constexpr const char* kShapeEnv[ar::kKinds] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
-    "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT"};
+    "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT",
+    "AR_SHAPE_UBATCH_FLAGS"};
 
 std::mutex g_mu;
 DevInfo g_dev[kMaxDevices];
@@ -312,9 +314,15 @@ int ar_rd_schedule(const uint64_t* const* in_words, uint64_t* const* out_words, 
       ar::launch_rd_fused(L, in, out, P, n, seq0, (flags & AR_RD_FP32_CARRY) ? 1 : 0, d_err));
 }
 
-int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t rows, size_t hidden,
-                     int n_ubatch, const size_t* ubatch_rows, size_t chunk_bytes, int variant,
-                     void* const* streams) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of ar_reduce_ubatch and ar_reduce_ubatch_flags (done == NULL:
+// no completion flags).
+int ubatch_impl(const void* const* ins, void* const* outs, int P, size_t rows, size_t hidden,
+                int n_ubatch, const size_t* ubatch_rows, size_t chunk_bytes, int variant,
+                void* const* streams, uint32_t* done, uint32_t* tiles, size_t n_flags, uint32_t epoch) {
   if (variant != AR_VARIANT_ONESHOT && variant != AR_VARIANT_2STAGE) return AR_ERR_INVALID;
   if (n_ubatch < 1 || n_ubatch > kMaxUbatch || !streams) return AR_ERR_INVALID;
   if (chunk_bytes == 0 || (chunk_bytes & 15u)) return AR_ERR_INVALID;
@@ -343,20 +351,54 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
     total += split[u];
   }
   if (total != rows) return AR_ERR_INVALID;
+  const size_t chunk = chunk_bytes / 2;
+  if (done) {
+    if (!tiles || epoch == 0) return AR_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(done) & 3u) || (reinterpret_cast<uintptr_t>(tiles) & 3u))
+      return AR_ERR_ALIGN;
+    size_t need = 0;
+    for (int u = 0; u < n_ubatch; ++u) need += (split[u] * hidden + chunk - 1) / chunk;
+    if (need > n_flags || need > 0xFFFFFFFFull || mul_overflows(n_flags, 4)) return AR_ERR_INVALID;
+    const Span sd = span_of(done, n_flags * 4), st = span_of(tiles, n_flags * 4);
+    if (overlap(sd, st) || check_disjoint(sd, si, P) || check_disjoint(sd, so, nout) ||
+        check_disjoint(st, si, P) || check_disjoint(st, so, nout))
+      return AR_ERR_ALIAS;
+  }
   if (n == 0) return AR_OK;
   ar::Launch L;
   if ((rc = resolve(&L, nullptr))) return rc;
-  const size_t chunk = chunk_bytes / 2;
-  size_t row0 = 0;
+  size_t row0 = 0, chunk0 = 0;
   for (int u = 0; u < n_ubatch; ++u) {
     const size_t e0 = row0 * hidden, e1 = (row0 + split[u]) * hidden;
     row0 += split[u];
     if (e1 == e0) continue;
     L.stream = static_cast<hipStream_t>(streams[u]);
-    rc = hip_status(ar::launch_chunked(L, in, out, P, e0, e1, chunk, nout > 1 ? 1 : 0));
+    const ar::ChunkSignal sig{done, done ? tiles : nullptr, epoch, (uint32_t)chunk0};
+    rc = hip_status(ar::launch_chunked(L, in, out, P, e0, e1, chunk, nout > 1 ? 1 : 0, sig));
     if (rc) return rc;
+    chunk0 += (e1 - e0 + chunk - 1) / chunk;
   }
   return AR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t rows, size_t hidden,
+                     int n_ubatch, const size_t* ubatch_rows, size_t chunk_bytes, int variant,
+                     void* const* streams) {
+  return ubatch_impl(ins, outs, P, rows, hidden, n_ubatch, ubatch_rows, chunk_bytes, variant, streams,
+                     nullptr, nullptr, 0, 0);
+}
+
+int ar_reduce_ubatch_flags(const void* const* ins, void* const* outs, int P, size_t rows,
+                           size_t hidden, int n_ubatch, const size_t* ubatch_rows, size_t chunk_bytes,
+                           int variant, void* const* streams, uint32_t* chunk_done,
+                           uint32_t* chunk_tiles, size_t n_flags, uint32_t epoch) {
+  if (!chunk_done) return AR_ERR_INVALID;
+  return ubatch_impl(ins, outs, P, rows, hidden, n_ubatch, ubatch_rows, chunk_bytes, variant, streams,
+                     chunk_done, chunk_tiles, n_flags, epoch);
 }
 
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu) {

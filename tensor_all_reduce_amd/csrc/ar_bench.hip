@@ -22,6 +22,92 @@ __global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ src, u32
   if (v < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
 }
 
+// Consumer of a flagged chunked reduce.  Persistent grid (no LDS request,
+// at most two workgroups per CU, so the producer's workgroups always fit
+// beside it: a waiting grid that filled every wave slot would keep them
+// out): workgroup b walks tiles b, b+G, ... (G = grid) in chunk order; a
+// tile is 4 groups of 16 bytes per lane (16 KiB), so each chunk is spread
+// over many workgroups and its consumer work over the whole GPU.  Before a
+// tile, wavefront 0 polls done[first + c] with relaxed device-scope loads,
+// sleeping between polls, at most max_spins times, then performs one
+// device-scope acquire fence (an L1 and L2 invalidate; polling with acquire
+// loads would invalidate the XCD's L2 on every spin, evicting the
+// producer's lines while it runs); a workgroup barrier passes the
+// acquired view on to the other wavefronts, which share the CU's L1.  The
+// tile is copied from src to dst; with WORK, each lane also runs `work`
+// dependent FMA rounds on the words it loaded (a compute-bound consumer)
+// and stores its total to sink[b * 256 + lane].  A tile whose flag never
+// arrived counts one timeout and is still copied (so a premature read shows
+// up as wrong data).
+template <bool WORK>
+__global__ __launch_bounds__(256) void k_consume(const uint32_t* done, uint32_t epoch, const u32x4* src,
+                                                 u32x4* dst, size_t nvec, size_t chunk_vec,
+                                                 uint32_t first, uint32_t max_spins, uint32_t* timeouts,
+                                                 int work, float* sink) {
+  constexpr int V = 4;
+  const size_t tile = (size_t)V * blockDim.x;
+  const size_t tiles_per_chunk = (chunk_vec + tile - 1) / tile;
+  const size_t nchunks = (nvec + chunk_vec - 1) / chunk_vec;
+  const size_t ntiles = nchunks * tiles_per_chunk;
+  float total = 0.0f;
+  for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const size_t c = t / tiles_per_chunk, k = t % tiles_per_chunk;
+    if (threadIdx.x < 64) {
+      uint32_t f = __hip_atomic_load(done + first + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t s = 0; f != epoch && s < max_spins; ++s) {
+        __builtin_amdgcn_s_sleep(2);
+        f = __hip_atomic_load(done + first + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (f != epoch && threadIdx.x == 0) atomicAdd(timeouts, 1u);
+    }
+    __syncthreads();
+    const size_t c1 = (c + 1) * chunk_vec < nvec ? (c + 1) * chunk_vec : nvec;
+    const size_t b0 = c * chunk_vec + k * tile + threadIdx.x;
+    u32x4 x[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const size_t v = b0 + (size_t)u * blockDim.x;
+      if (v < c1) x[u] = src[v];
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const size_t v = b0 + (size_t)u * blockDim.x;
+      if (v < c1) {
+        __builtin_nontemporal_store(x[u], dst + v);
+        if constexpr (WORK) {
+          // four independent chains, seeded in [1, 2) from the data
+          float a = __uint_as_float((x[u].x & 0x007FFFFFu) | 0x3F800000u);
+          float b = __uint_as_float((x[u].y & 0x007FFFFFu) | 0x3F800000u);
+          float e = __uint_as_float((x[u].z & 0x007FFFFFu) | 0x3F800000u);
+          float d = __uint_as_float((x[u].w & 0x007FFFFFu) | 0x3F800000u);
+          for (int i = 0; i < work; ++i) {
+            a = __builtin_fmaf(a, 0.999f, 0.001f);
+            b = __builtin_fmaf(b, 0.998f, 0.002f);
+            e = __builtin_fmaf(e, 0.997f, 0.003f);
+            d = __builtin_fmaf(d, 0.996f, 0.004f);
+          }
+          total += (a + b) + (e + d);
+        }
+      }
+    }
+  }
+  if constexpr (WORK) sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = total;
+}
+
+// ALU-bound stand-in for the partner ubatch's compute: `iters` rounds of
+// dependent fused multiply-adds on four accumulators per lane; one float out.
+__global__ __launch_bounds__(256) void k_alu(float* out, int iters) {
+  float a = threadIdx.x * 1e-3f, b = 1.0f, c = 0.5f, d = 0.25f;
+  for (int i = 0; i < iters; ++i) {
+    a = __builtin_fmaf(a, 0.999f, 0.001f);
+    b = __builtin_fmaf(b, 0.998f, 0.002f);
+    c = __builtin_fmaf(c, 0.997f, 0.003f);
+    d = __builtin_fmaf(d, 0.996f, 0.004f);
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = a + b + c + d;
+}
+
 int call(int which, const void* const* ins, void* const* outs, int P, size_t n, void* scratch,
          void* stream) {
   switch (which) {
@@ -99,6 +185,40 @@ int arb_copy(const void* src, void* dst, size_t bytes, int block, void* stream) 
   if (grid == 0 || grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
   hipLaunchKernelGGL(k_copy, dim3((unsigned)grid), dim3(block), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), nvec);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+// Launch the chunk consumer (n_elems and chunk_elems multiples of 8, buffers
+// 16-byte aligned) with `grid` workgroups of 256 lanes, at most two per CU
+// of the current device.  work > 0 adds that many FMA rounds per 16-byte
+// group and needs sink (grid * 256 floats).
+int arb_consume_chunks(const uint32_t* done, uint32_t epoch, const void* src, void* dst, size_t n_elems,
+                       size_t chunk_elems, uint32_t first_chunk, uint32_t max_spins, uint32_t* timeouts,
+                       int work, float* sink, int grid, void* stream) {
+  if (!done || !src || !dst || !timeouts || (n_elems & 7u) || (chunk_elems & 7u) || chunk_elems == 0 ||
+      grid <= 0 || work < 0 || (work > 0 && !sink))
+    return AR_ERR_INVALID;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return AR_ERR_HIP;
+  if (grid > 2 * cus) return AR_ERR_INVALID;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* d = static_cast<u32x4*>(dst);
+  if (work > 0)
+    hipLaunchKernelGGL(k_consume<true>, dim3(grid), dim3(256), 0, st, done, epoch, s, d, n_elems / 8,
+                       chunk_elems / 8, first_chunk, max_spins, timeouts, work, sink);
+  else
+    hipLaunchKernelGGL(k_consume<false>, dim3(grid), dim3(256), 0, st, done, epoch, s, d, n_elems / 8,
+                       chunk_elems / 8, first_chunk, max_spins, timeouts, 0, (float*)nullptr);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+// Launch the ALU stand-in: `grid` workgroups of 256 lanes, out holds grid*256 floats.
+int arb_alu(float* out, int iters, int grid, void* stream) {
+  if (!out || iters < 0 || grid <= 0) return AR_ERR_INVALID;
+  hipLaunchKernelGGL(k_alu, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), out, iters);
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 

@@ -32,6 +32,28 @@ __device__ __forceinline__ void st4(u32x4* p, u32x4 v) {
   else *p = v;
 }
 
+// Device-coherent 16-byte store for data that a completion flag will cover.
+// The buffer store carries the SC1 cache policy (aux bit 4; bit 1 adds the
+// streaming NT hint): it is written through to the level every XCD's L2
+// sees, so once the wave's store counter drains no dirty copy sits in one
+// XCD's L2 and the flag can be published without an L2 writeback (the
+// writeback an agent-scope release fence performs costs more than the
+// reduce itself).  `base` is the wave-uniform start of the written span,
+// `bytes` its length (the buffer descriptor's range), `off` this lane's
+// byte offset in it.  Descriptor word 3 = 0x00020000 selects the 32-bit
+// data format (any nonzero format works for untyped access).
+template <bool NT>
+__device__ __forceinline__ void st4_coherent(u32x4* base, uint32_t bytes, uint32_t off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, NT ? (16 | 2) : 16);
+}
+
+// s_waitcnt with vmcnt = 0 and expcnt / lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): the wave
+// waits until all of its vector memory operations, stores included, are
+// acknowledged.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // bf16 -> binary32 is exact: the bf16 bits are the high half of the float.
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

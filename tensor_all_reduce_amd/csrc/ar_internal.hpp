@@ -37,6 +37,7 @@ enum Kind {
   kRD,           // fused recursive doubling, 8 payloads -> 8 payloads
   kRDStep,       // staged recursive-doubling step
   kUnpackWait,   // unpack that waits for the producer (persistent grid, no LDS request)
+  kUbatchFlags,  // chunked reduce that publishes per-chunk completion flags
   kKinds
 };
 
@@ -53,6 +54,13 @@ struct Launch {
 struct InPtrs { const void* p[AR_MAX_RANKS]; };
 struct OutPtrs { void* p[AR_MAX_RANKS]; };
 struct WordIn { const uint64_t* p[AR_MAX_RANKS]; };
+// Per-chunk completion signal of the chunked reduce (done == nullptr: none).
+struct ChunkSignal {
+  uint32_t* done;    // done[base + c] = epoch once chunk c is fully written
+  uint32_t* tiles;   // per-chunk tile counters, zero between calls
+  uint32_t epoch;
+  uint32_t base;     // index of this launch's first chunk in done / tiles
+};
 struct WordOut { uint64_t* p[AR_MAX_RANKS]; };
 
 hipError_t launch_oneshot(const Launch& L, const InPtrs& in, int P, void* out, size_t n);
@@ -62,7 +70,8 @@ hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs
                                 size_t n, void* scratch);
 // Chunked reduce of elements [e0, e1) of every buffer, chunk-major workgroups.
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
-                          size_t e0, size_t e1, size_t chunk_elems, int two_stage);
+                          size_t e0, size_t e1, size_t chunk_elems, int two_stage,
+                          const ChunkSignal& sig);
 
 hipError_t launch_pack(const Launch& L, const void* x, uint64_t* w, size_t n, uint32_t seq);
 hipError_t launch_unpack(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,

@@ -38,9 +38,21 @@ namespace ar {
 // done element by element.  NOUT == 1: one-shot; NOUT == P: fused two-stage
 // (write mode).  Every group is reduced by exactly one lane, which reads it
 // from every input before writing it, so an output equal to an input is safe.
-template <int P, int NOUT, int V, bool NTL, bool NTS>
+//
+// SIG: the workgroups of a chunk also publish its completion.  Every output
+// store is device-coherent (written through past the XCD's L2), each wave
+// waits until its stores are acknowledged, the workgroup meets at a barrier,
+// and one lane adds 1 to the chunk's tile counter; the workgroup that
+// completes the count resets the counter to zero (ready for the next call)
+// and stores sig.epoch into done[chunk].  This is an agent-scope release
+// without the L2 writeback: nothing the flag covers was left dirty in an L2.
+// The flag store depends on the counter's returned value, and every counter
+// increment follows its workgroup's acknowledged stores, so a consumer that
+// acquire-loads done[chunk] == epoch (which invalidates its own L2 and L1
+// copies) sees the whole chunk of every output.
+template <int P, int NOUT, int V, bool NTL, bool NTS, bool SIG>
 __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, size_t e0, size_t e1,
-                                                     size_t chunk, unsigned bpc) {
+                                                     size_t chunk, unsigned bpc, ChunkSignal sig) {
   const size_t span = (size_t)V * blockDim.x * 8;
   const size_t c = blockIdx.x / bpc;
   const unsigned t = blockIdx.x % bpc;
@@ -66,7 +78,13 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
     if (v < vb1) {
       const u32x4 r = reduce8<P>(x[u]);
 #pragma unroll
-      for (int o = 0; o < NOUT; ++o) st4<NTS>(static_cast<u32x4*>(out.p[o]) + v, r);
+      for (int o = 0; o < NOUT; ++o) {
+        if constexpr (SIG)
+          st4_coherent<NTS>(static_cast<u32x4*>(out.p[o]) + vb0, (uint32_t)((vb1 - vb0) * 16),
+                            (uint32_t)((v - vb0) * 16), r);
+        else
+          st4<NTS>(static_cast<u32x4*>(out.p[o]) + v, r);
+      }
     }
   }
   // element-wise head [b0, min(8*vb0, b1)) and tail [max(8*vb1, 8*vb0), b1)
@@ -80,7 +98,25 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
     for (int p = 0; p < P; ++p) in16[p] = static_cast<const uint16_t*>(in.p[p]);
     const uint16_t r = reduce1<P>(in16, i);
 #pragma unroll
-    for (int o = 0; o < NOUT; ++o) static_cast<uint16_t*>(out.p[o])[i] = r;
+    for (int o = 0; o < NOUT; ++o) {
+      uint16_t* dst = static_cast<uint16_t*>(out.p[o]) + i;
+      if constexpr (SIG) __hip_atomic_store(dst, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *dst = r;
+    }
+  }
+  if constexpr (SIG) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned g = sig.base + (unsigned)c;
+      const unsigned tiles_here = (unsigned)((c1 - c0 + span - 1) / span);
+      const unsigned old = __hip_atomic_fetch_add(sig.tiles + g, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      if (old + 1u == tiles_here) {
+        __hip_atomic_store(sig.tiles + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sig.done + g, sig.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -137,7 +173,7 @@ namespace {
 
 template <int P, int NOUT, int V>
 hipError_t range_v(const Shape& sh, hipStream_t st, const InPtrs& in, const OutPtrs& out, size_t e0,
-                   size_t e1, size_t chunk) {
+                   size_t e1, size_t chunk, const ChunkSignal& sig) {
   const size_t span = (size_t)V * sh.block * 8;
   const size_t bpc = cdiv(chunk, span);
   const size_t nchunks = cdiv(e1 - e0, chunk);
@@ -145,20 +181,29 @@ hipError_t range_v(const Shape& sh, hipStream_t st, const InPtrs& in, const OutP
   if (blocks > 0x7FFFFFFFull || bpc > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
   const unsigned g = (unsigned)blocks, b = (unsigned)bpc;
   const dim3 blk(sh.block);
+  if (sig.done != nullptr) {
+    if (sh.nt_loads && sh.nt_stores)
+      return launch_k(k_reduce<P, NOUT, V, true, true, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
+    if (sh.nt_loads)
+      return launch_k(k_reduce<P, NOUT, V, true, false, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
+    if (sh.nt_stores)
+      return launch_k(k_reduce<P, NOUT, V, false, true, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
+    return launch_k(k_reduce<P, NOUT, V, false, false, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
+  }
   if (sh.nt_loads && sh.nt_stores)
-    return launch_k(k_reduce<P, NOUT, V, true, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
+    return launch_k(k_reduce<P, NOUT, V, true, true, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
   if (sh.nt_loads)
-    return launch_k(k_reduce<P, NOUT, V, true, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
+    return launch_k(k_reduce<P, NOUT, V, true, false, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
   if (sh.nt_stores)
-    return launch_k(k_reduce<P, NOUT, V, false, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
-  return launch_k(k_reduce<P, NOUT, V, false, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b);
+    return launch_k(k_reduce<P, NOUT, V, false, true, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
+  return launch_k(k_reduce<P, NOUT, V, false, false, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
 }
 
 template <int P, int NOUT>
 hipError_t range_p(const Shape& sh, hipStream_t st, const InPtrs& in, const OutPtrs& out, size_t e0,
-                   size_t e1, size_t chunk) {
-  if (sh.vec == 2) return range_v<P, NOUT, 2>(sh, st, in, out, e0, e1, chunk);
-  return range_v<P, NOUT, 1>(sh, st, in, out, e0, e1, chunk);
+                   size_t e1, size_t chunk, const ChunkSignal& sig = ChunkSignal{nullptr, nullptr, 0, 0}) {
+  if (sh.vec == 2) return range_v<P, NOUT, 2>(sh, st, in, out, e0, e1, chunk, sig);
+  return range_v<P, NOUT, 1>(sh, st, in, out, e0, e1, chunk, sig);
 }
 
 template <int P>
@@ -211,11 +256,17 @@ hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs
 }
 
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
-                          size_t e0, size_t e1, size_t chunk_elems, int two_stage) {
+                          size_t e0, size_t e1, size_t chunk_elems, int two_stage,
+                          const ChunkSignal& sig) {
+  // the flagged variant has its own shape: every workgroup of a chunk waits
+  // for its stores and adds to a counter, so fewer, larger workgroups are
+  // cheaper (256 lanes: the wait is hidden by the other waves)
+  const Shape& sh2 = sig.done ? L.shape[kUbatchFlags] : L.shape[kUbatch];
+  const Shape& sh1 = sig.done ? L.shape[kUbatchFlags] : L.shape[kOneshot];
   if (two_stage) {
-    AR_DISPATCH_P(P, (range_p<PP, PP>(L.shape[kUbatch], L.stream, in, out, e0, e1, chunk_elems)))
+    AR_DISPATCH_P(P, (range_p<PP, PP>(sh2, L.stream, in, out, e0, e1, chunk_elems, sig)))
   }
-  AR_DISPATCH_P(P, (range_p<PP, 1>(L.shape[kOneshot], L.stream, in, out, e0, e1, chunk_elems)))
+  AR_DISPATCH_P(P, (range_p<PP, 1>(sh1, L.stream, in, out, e0, e1, chunk_elems, sig)))
 }
 
 }  // namespace ar

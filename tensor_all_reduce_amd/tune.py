@@ -38,11 +38,12 @@ KINDS = {
     "oneshot": tar.AR_KERNEL_ONESHOT, "2stage": tar.AR_KERNEL_2STAGE, "ubatch": tar.AR_KERNEL_UBATCH,
     "rs": tar.AR_KERNEL_RS, "ag": tar.AR_KERNEL_AG, "pack": tar.AR_KERNEL_PACK,
     "unpack": tar.AR_KERNEL_UNPACK, "rd": tar.AR_KERNEL_RD, "rdstep": tar.AR_KERNEL_RDSTEP,
+    "ubatch_flags": tar.AR_KERNEL_UBATCH_FLAGS,
 }
 
 
 def candidates(kind: str):
-    vecs = (1, 2) if kind in ("oneshot", "2stage", "ubatch") else (1,)
+    vecs = (1, 2) if kind in ("oneshot", "2stage", "ubatch", "ubatch_flags") else (1,)
     return list(itertools.product((64, 128, 256), vecs, (0, 1), (0, 1), WGS))
 
 
@@ -71,6 +72,10 @@ def main(argv=None):
     main_s = torch.cuda.current_stream()
     s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
     B = 2 * n
+    nflags = tar.ubatch_chunk_count(ROWS, HIDDEN, 2, None, 1 << 20)
+    done = torch.zeros(nflags, dtype=torch.int32, device=dev)
+    tiles = torch.zeros(nflags, dtype=torch.int32, device=dev)
+    epoch = [0]
     for r in range(P):
         tar.ar_pack_fused(ins[r], words[r], 1)
     tar.ar_err_init(err)
@@ -88,6 +93,14 @@ def main(argv=None):
             tar.ar_reduce_ubatch(ins, outs, ROWS, HIDDEN, 2, None, 1 << 20, tar.AR_VARIANT_2STAGE, [s0, s1])
             main_s.wait_stream(s0)
             main_s.wait_stream(s1)
+        elif kind == "ubatch_flags":
+            epoch[0] += 1
+            s0.wait_stream(main_s)
+            s1.wait_stream(main_s)
+            tar.ar_reduce_ubatch_flags(ins, outs, ROWS, HIDDEN, done, tiles, epoch[0], 2, None, 1 << 20,
+                                       tar.AR_VARIANT_2STAGE, [s0, s1])
+            main_s.wait_stream(s0)
+            main_s.wait_stream(s1)
         elif kind == "pack":
             for r in range(P):
                 tar.ar_pack_fused(ins[r], words[r], 1)
@@ -99,7 +112,8 @@ def main(argv=None):
         elif kind == "rdstep":
             tar.ar_rd_schedule(words, rdo, 1, err, mailbox=mailbox, flags=tar.AR_RD_STAGED)
 
-    credited = {"oneshot": (P + 1) * B, "2stage": 2 * P * B, "ubatch": 2 * P * B, "rs": 2 * P * B,
+    credited = {"oneshot": (P + 1) * B, "2stage": 2 * P * B, "ubatch": 2 * P * B, "ubatch_flags": 2 * P * B,
+                "rs": 2 * P * B,
                 "ag": 2 * P * B, "pack": 3 * P * B, "unpack": 3 * P * B, "rd": 4 * P * B, "rdstep": 4 * P * B}
 
     def time_one(kind):

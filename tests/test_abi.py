@@ -162,6 +162,26 @@ def test_ubatch_validation():
     assert L.ar_reduce_ubatch(ins, arr(C, None), 2, 0, 8, 2, None, 4096, 0, streams) == tar.AR_OK
 
 
+def test_ubatch_flags_validation():
+    L = tar.lib()
+    ins = arr(A, B)
+    outs = arr(C, C + 0x100000)
+    streams = arr(None, None)
+    D = 0x40000000
+    T = 0x40010000
+    args = lambda done, tiles, nf, epoch: (ins, outs, 2, 4, 8, 2, None, 16, 1, streams, done, tiles, nf, epoch)
+    # 4 rows x 8 = 32 elements, 16-byte chunks = 8 elements: 2 ubatches x 2 chunks
+    assert L.ar_reduce_ubatch_flags(*args(None, T, 4, 1)) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch_flags(*args(D, None, 4, 1)) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_ubatch_flags(*args(D, T, 4, 0)) == tar.AR_ERR_INVALID      # epoch 0
+    assert L.ar_reduce_ubatch_flags(*args(D, T, 3, 1)) == tar.AR_ERR_INVALID      # too short
+    assert L.ar_reduce_ubatch_flags(*args(D + 2, T, 4, 1)) == tar.AR_ERR_ALIGN
+    assert L.ar_reduce_ubatch_flags(*args(D, D + 8, 4, 1)) == tar.AR_ERR_ALIAS    # arrays overlap
+    assert L.ar_reduce_ubatch_flags(*args(C, T, 4, 1)) == tar.AR_ERR_ALIAS        # flags over an output
+    assert tar.ubatch_chunk_count(4, 8, 2, None, 16) == 4
+    assert tar.ubatch_chunk_count(16384, 16384, 2, None, 1 << 20) == 512
+
+
 def test_err_init_validation():
     L = tar.lib()
     assert L.ar_err_init(None, None) == tar.AR_ERR_INVALID
@@ -176,13 +196,13 @@ def test_binding_raises_on_error():
 
 def test_launch_shape_roundtrip_and_validation():
     L = tar.lib()
-    for kind in range(10):
+    for kind in range(11):
         before = tar.ar_get_launch_shape(kind)
         tar.ar_set_launch_shape(kind, 128, 2, 0, 1, 7)
         assert tar.ar_get_launch_shape(kind) == (128, 2, 0, 1, 7)
         tar.ar_set_launch_shape(kind, *before)
         assert tar.ar_get_launch_shape(kind) == before
-    assert L.ar_set_launch_shape(10, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(11, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 96, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 3, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 1, 2, 1, 0) == tar.AR_ERR_INVALID
