@@ -127,6 +127,15 @@ def main():
     blib.arb_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
     blib.arb_alu.restype = ctypes.c_int
     blib.arb_alu.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    blib.arb_stream_rot_us.restype = ctypes.c_double
+    blib.arb_stream_rot_us.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                       ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp]
+    blib.arb_decode_us.restype = ctypes.c_double
+    blib.arb_decode_us.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                   ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t, vp, ctypes.c_int, vp,
+                                   ctypes.c_int, ctypes.c_int, vp]
+    blib.arb_readsum.restype = ctypes.c_int
+    blib.arb_readsum.argtypes = [vp, ctypes.c_size_t, vp, vp]
     blib.arb_consume_chunks.restype = ctypes.c_int
     blib.arb_consume_chunks.argtypes = [vp, ctypes.c_uint32, vp, vp, ctypes.c_size_t, ctypes.c_size_t,
                                         ctypes.c_uint32, ctypes.c_uint32, vp, ctypes.c_int, vp,
@@ -315,11 +324,34 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
         gbps = 2 * cb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         best = max(best, gbps)
     res["copy_GBps"] = round(best, 1)
-    del src, dst
-    log(f"copy bandwidth {best:.0f} GB/s")
+    # attainable read bandwidth: read-only sweep of the same 2 GiB
+    sink = torch.empty(cb // 16384 + 1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        if blib.arb_readsum(src.data_ptr(), cb, sink.data_ptr(), sh) != 0:
+            raise RuntimeError("arb_readsum failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main_s)
+    for _ in range(10):
+        blib.arb_readsum(src.data_ptr(), cb, sink.data_ptr(), sh)
+    e1.record(main_s)
+    torch.cuda.synchronize()
+    res["read_GBps"] = round(cb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst, sink
+    log(f"copy bandwidth {best:.0f} GB/s, read-only {res['read_GBps']:.0f} GB/s")
 
-    # latency at decode sizes, 128 KiB .. 2 MiB per buffer
+    # latency at decode sizes: P = 2 at one token ([1 x 8192], 16 KiB), then
+    # P = 8 at 128 KiB .. 2 MiB per buffer
     lat = {}
+    m = HIDDEN
+    xi = [x[:m] for x in ins[:2]]
+    xo = [o[:m] for o in outs[:2]]
+    us = blib.arb_stream_us(0, parr(xi), parr(xo), 2, m, None, 5000, sh)
+    p50, p10, p90 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    if blib.arb_wall_us(0, parr(xi), parr(xo), 2, m, None, 2000, sh, ctypes.byref(p50), ctypes.byref(p10),
+                        ctypes.byref(p90)) != 0:
+        raise RuntimeError("arb_wall_us failed")
+    lat["P2_16KiB"] = {"oneshot": {"stream_us": round(us, 2), "wall_us_p50": round(p50.value, 2),
+                                   "wall_us_p90": round(p90.value, 2)}}
     for T in (8, 32, 128):
         m = T * HIDDEN
         xi = [x[:m] for x in ins]
@@ -340,6 +372,57 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
                               "GBps_hot": round(cred / (us * 1e-6) / 1e9, 1)}
     res["latency"] = lat
     log("latency measured")
+
+    # the same sizes cold: call k uses the (k mod sets)-th disjoint slice of
+    # the prefill buffers, at least 1 GiB in all (four times the 256 MiB
+    # last-level cache), so every call reads and writes HBM
+    cold = {}
+    for T in (8, 32, 128):
+        m = T * HIDDEN
+        sets = min(n // m, -(-(1 << 30) // (2 * P * 2 * m)))
+        key = f"{2 * m // 1024}KiB"
+        cold[key] = {"sets": sets}
+        for which, name in ((0, "oneshot"), (1, "2stage_fused")):
+            us = blib.arb_stream_rot_us(which, parr(ins), parr(outs), P, m, m, sets, 4 * sets, sh)
+            if us < 0:
+                raise RuntimeError(f"arb_stream_rot_us failed: {us}")
+            cred = (P + 1) * 2 * m if which == 0 else 2 * P * 2 * m
+            cold[key][name] = {"stream_us": round(us, 2), "GBps": round(cred / (us * 1e-6) / 1e9, 1)}
+    res["latency_cold"] = cold
+    log("cold latency measured")
+
+    # decode all-reduce on fused payloads at [128 x 8192] per rank, P = 8:
+    # recursive doubling alone, and the whole chain (P packs, error reset,
+    # recursive doubling, P unpacks), seq0 = 1
+    def e64(k):
+        return torch.empty(k, dtype=torch.int64, device=dev)
+
+    m = 128 * HIDDEN
+    xi = [x[:m] for x in ins]
+    yo = [o[:m] for o in outs]
+    win = [e64(m // 2) for _ in range(P)]
+    wout = [e64(m // 2) for _ in range(P)]
+    mbox = e64(tar.rd_mailbox_words(P, m))
+    derr = e64(2)
+    tar.ar_err_init(derr, stream=main_s)
+    for p in range(P):
+        tar.ar_pack_fused(xi[p], win[p], 1, stream=main_s)
+    dec = {}
+    for name, mb, flags, chain in (("rd_fused_R1", None, 0, 0), ("rd_fused_R2", None, tar.AR_RD_FP32_CARRY, 0),
+                                   ("rd_staged_R1", mbox, tar.AR_RD_STAGED, 0),
+                                   ("chain_fused_R1", None, 0, 1), ("chain_staged_R1", mbox, tar.AR_RD_STAGED, 1)):
+        us = blib.arb_decode_us(parr(xi), parr(yo), parr(win), parr(wout), P, m,
+                                mb.data_ptr() if mb is not None else None, flags, derr.data_ptr(), chain, 2000, sh)
+        if us < 0:
+            raise RuntimeError(f"arb_decode_us failed: {us}")
+        dec[name] = {"stream_us": round(us, 2)}
+    torch.cuda.synchronize()
+    e = derr.cpu().tolist()
+    if e[0] != 0:
+        raise RuntimeError(f"decode chain saw {e[0]} bad sequence numbers")
+    res["decode_fused_payload_128x8192"] = dec
+    del win, wout, mbox
+    log("decode chain measured")
 
     # the same calls captured in one HIP graph (100 calls per graph), which
     # removes the per-launch host cost from each call
@@ -412,6 +495,28 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
                                  "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
                                  "streams": 2, "chunk_bytes": CHUNK_BYTES}
     log(f"ubatch [16384x16384]: {ms:.3f} ms, {gbps:.0f} GB/s")
+
+    # the one-shot variant at the same shape (one output, (P + 1) B credited)
+    def ub1():
+        s0.wait_stream(main_s)
+        s1.wait_stream(main_s)
+        tar.ar_reduce_ubatch(uin, uout[:1], UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_ONESHOT,
+                             [s0, s1])
+        main_s.wait_stream(s0)
+        main_s.wait_stream(s1)
+
+    for _ in range(3):
+        ub1()
+    e0.record(main_s)
+    for _ in range(reps):
+        ub1()
+    e1.record(main_s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = (P + 1) * 2 * m / (ms * 1e-3) / 1e9
+    res["ubatch_16384x16384_oneshot"] = {"ms": round(ms, 4), "GBps_credited": round(gbps, 1),
+                                         "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+    log(f"ubatch one-shot [16384x16384]: {ms:.3f} ms, {gbps:.0f} GB/s")
     del uin, uout
     torch.cuda.empty_cache()
     return res

@@ -95,6 +95,27 @@ __global__ __launch_bounds__(256) void k_consume(const uint32_t* done, uint32_t 
   if constexpr (WORK) sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = total;
 }
 
+// Read-only sweep: every lane loads 16-byte groups (non-temporal) and folds
+// them with xor; one word per workgroup is written so the loads stay live.
+// Measures the attainable read bandwidth beside the copy's read+write rate.
+__global__ __launch_bounds__(256) void k_readsum(const u32x4* __restrict__ src, size_t nvec,
+                                                 uint32_t* __restrict__ out) {
+  constexpr int V = 4;
+  const size_t b0 = (size_t)blockIdx.x * blockDim.x * V + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const size_t v = b0 + (size_t)u * blockDim.x;
+    if (v < nvec) acc ^= __builtin_nontemporal_load(src + v);
+  }
+  uint32_t w = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (int o = 32; o > 0; o >>= 1) w ^= __shfl_xor(w, o, 64);
+  __shared__ uint32_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 // ALU-bound stand-in for the partner ubatch's compute: `iters` rounds of
 // dependent fused multiply-adds on four accumulators per lane; one float out.
 __global__ __launch_bounds__(256) void k_alu(float* out, int iters) {
@@ -116,6 +137,49 @@ int call(int which, const void* const* ins, void* const* outs, int P, size_t n, 
     case 2: return ar_reduce_2stage(ins, outs, P, n, scratch, stream);
     default: return AR_ERR_INVALID;
   }
+}
+
+// Events released on every return path.
+struct EventPair {
+  hipEvent_t a = nullptr, b = nullptr;
+  bool ok = false;
+  EventPair() { ok = hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess; }
+  ~EventPair() {
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+  }
+  double us_between(hipStream_t s, int iters) {
+    (void)hipEventSynchronize(b);
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, a, b);
+    (void)s;
+    return 1000.0 * (double)ms / iters;
+  }
+};
+
+// One decode all-reduce on fused payloads: P packs, error-record reset,
+// recursive doubling, P unpacks (chain != 0); or the recursive doubling
+// alone (chain == 0).
+int decode_once(const void* const* x, void* const* y, uint64_t* const* w_in, uint64_t* const* w_out, int P,
+                size_t n, uint32_t seq0, uint64_t* mailbox, int flags, uint64_t* d_err, int chain,
+                void* stream) {
+  int L = 0;
+  while ((1 << L) < P) ++L;
+  if (chain) {
+    for (int p = 0; p < P; ++p) {
+      int rc = ar_pack_fused(x[p], w_in[p], n, seq0, stream);
+      if (rc) return rc;
+    }
+    int rc = ar_err_init(d_err, stream);
+    if (rc) return rc;
+  }
+  int rc = ar_rd_schedule(w_in, w_out, P, n, seq0, mailbox, flags, d_err, stream);
+  if (rc || !chain) return rc;
+  for (int p = 0; p < P; ++p) {
+    rc = ar_unpack_fused(w_out[p], y[p], n, seq0 + (uint32_t)L, d_err, stream);
+    if (rc) return rc;
+  }
+  return AR_OK;
 }
 
 }  // namespace
@@ -173,6 +237,77 @@ int arb_wall_us(int which, const void* const* ins, void* const* outs, int P, siz
   *p10 = t[t.size() / 10];
   *p90 = t[(t.size() * 9) / 10];
   return AR_OK;
+}
+
+// Like arb_stream_us, but call k works on the k % nsets-th of nsets
+// disjoint element ranges: every buffer pointer is advanced by
+// (k % nsets) * stride_elems bf16 elements.  With a footprint above the
+// 256 MiB last-level cache this measures the cold (HBM) cost of small
+// calls.  which: 0 one-shot (outs[0]), 1 two-stage fused.
+double arb_stream_rot_us(int which, const void* const* ins, void* const* outs, int P, size_t n,
+                         size_t stride_elems, int nsets, int iters, void* stream) {
+  if (which < 0 || which > 1 || P < 1 || P > AR_MAX_RANKS || nsets < 1 || iters < 1 || stride_elems < n)
+    return AR_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  if (!ev.ok) return AR_ERR_HIP;
+  const void* in_k[AR_MAX_RANKS];
+  void* out_k[AR_MAX_RANKS];
+  auto one = [&](int k) {
+    const size_t off = (size_t)(k % nsets) * stride_elems * 2;
+    for (int p = 0; p < P; ++p) {
+      in_k[p] = static_cast<const char*>(ins[p]) + off;
+      out_k[p] = static_cast<char*>(outs[p]) + off;
+    }
+    return call(which, in_k, out_k, P, n, nullptr, stream);
+  };
+  for (int i = 0; i < 2 * nsets; ++i) {
+    int rc = one(i);
+    if (rc) return rc;
+  }
+  (void)hipEventRecord(ev.a, s);
+  for (int i = 0; i < iters; ++i) {
+    int rc = one(i);
+    if (rc) return rc;
+  }
+  (void)hipEventRecord(ev.b, s);
+  return ev.us_between(s, iters);
+}
+
+// Average stream time, in microseconds, of `iters` back-to-back decode
+// all-reduces on fused payloads (see decode_once; seq0 = 1 throughout, so
+// d_err stays zero when every payload is valid).  mailbox NULL: fused
+// recursive doubling; non-NULL: staged.
+double arb_decode_us(const void* const* x, void* const* y, uint64_t* const* w_in, uint64_t* const* w_out,
+                     int P, size_t n, uint64_t* mailbox, int flags, uint64_t* d_err, int chain, int iters,
+                     void* stream) {
+  if (iters < 1) return AR_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EventPair ev;
+  if (!ev.ok) return AR_ERR_HIP;
+  for (int i = 0; i < 20; ++i) {
+    int rc = decode_once(x, y, w_in, w_out, P, n, 1u, mailbox, flags, d_err, chain, stream);
+    if (rc) return rc;
+  }
+  (void)hipEventRecord(ev.a, s);
+  for (int i = 0; i < iters; ++i) {
+    int rc = decode_once(x, y, w_in, w_out, P, n, 1u, mailbox, flags, d_err, chain, stream);
+    if (rc) return rc;
+  }
+  (void)hipEventRecord(ev.b, s);
+  return ev.us_between(s, iters);
+}
+
+// Read-only sweep of `bytes` (a multiple of 16, 16-byte aligned); out holds
+// one word per workgroup: ceil(bytes / 16384) words.
+int arb_readsum(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  if ((bytes & 15u) || !src || !out) return AR_ERR_INVALID;
+  const size_t nvec = bytes / 16;
+  const size_t grid = (nvec + 1023) / 1024;
+  if (grid == 0 || grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
+  hipLaunchKernelGGL(k_readsum, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), nvec, out);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
 // Plain device copy of `bytes` (a multiple of 16, 16-byte aligned buffers),

@@ -4,6 +4,8 @@
            row, the rocprofv3 average over all dispatches and the average
            over the timed steps only (warmup steps dropped), next to the
            rocprofv3 kernel_stats line.
+  decode   kernel-only durations of the decode-size calls that
+           decode_trace.py issues, labelled by the plan it writes.
   traffic  HBM bytes per launch from two --pmc runs (FETCH_SIZE, then
            WRITE_SIZE; KiB per dispatch), each scaled by what the same
            counter reads for the plain 1 GiB copies that bench.py
@@ -15,6 +17,7 @@ step is that row's kernel whatever its template arguments.
 
 Usage:
   python -m tensor_all_reduce_amd.profsum stats DIR --warmup W --command "..."
+  python -m tensor_all_reduce_amd.profsum decode DIR PLAN.json --command "..."
   python -m tensor_all_reduce_amd.profsum traffic FETCH_DIR WRITE_DIR --calib-bytes B \
       --command-fetch "..." --command-write "..."
 """
@@ -114,6 +117,41 @@ def cmd_stats(a):
                   f"min {float(r['MinNs']) * 1e-6:.4f}  max {float(r['MaxNs']) * 1e-6:.4f}")
 
 
+def cmd_decode(a):
+    import json
+    trace = one(os.path.join(a.dir, "*kernel_trace.csv"))
+    rows = [r for r in csv.DictReader(open(trace)) if "ar::k_" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    plan = json.load(open(a.plan))
+    need = sum(p["dispatches_per_call"] * p["calls"] for p in plan)
+    if need != len(rows):
+        raise SystemExit(f"plan covers {need} library dispatches, trace has {len(rows)}")
+    print("# rocprofv3 kernel trace of decode-size calls (kernel-only time per call, launch excluded)")
+    print(f"# command: {a.command}")
+    print("# per call: sum of its dispatches' durations; first 10% of calls of each phase dropped")
+    print(f"# {'phase':28s} {'calls':>5s} {'mean_us':>8s} {'p50_us':>8s} {'p10_us':>8s} {'p90_us':>8s} "
+          f"{'GB/s(p50)':>9s}  kernels")
+    i = 0
+    for p in plan:
+        k, c = p["dispatches_per_call"], p["calls"]
+        calls = []
+        names = []
+        for j in range(c):
+            ds = rows[i + j * k: i + (j + 1) * k]
+            calls.append(sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in ds) * 1e-3)
+            if j == 0:
+                names = [r["Kernel_Name"].split("(")[0].replace("void ", "") for r in ds]
+        i += k * c
+        if p["phase"] == "setup":
+            continue
+        t = sorted(calls[c // 10:])
+        p50 = statistics.median(t)
+        gb = p["credited_bytes_per_call"] / (p50 * 1e-6) / 1e9 if p["credited_bytes_per_call"] else 0.0
+        uniq = sorted(set(names), key=names.index)
+        print(f"{p['phase']:30s} {len(t):5d} {statistics.mean(t):8.2f} {p50:8.2f} {t[len(t) // 10]:8.2f} "
+              f"{t[(len(t) * 9) // 10]:8.2f} {gb:9.1f}  {' + '.join(uniq)}")
+
+
 def counters(d):
     f = one(os.path.join(d, "*counter_collection.csv"))
     rows = list(csv.DictReader(open(f)))
@@ -156,6 +194,10 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--warmup", type=int, default=2)
     s.add_argument("--command", default="")
+    d = sub.add_parser("decode")
+    d.add_argument("dir")
+    d.add_argument("plan")
+    d.add_argument("--command", default="")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
@@ -163,7 +205,7 @@ def main(argv=None):
     t.add_argument("--command-fetch", default="")
     t.add_argument("--command-write", default="")
     a = ap.parse_args(argv)
-    return cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+    return {"stats": cmd_stats, "decode": cmd_decode, "traffic": cmd_traffic}[a.cmd](a)
 
 
 if __name__ == "__main__":
