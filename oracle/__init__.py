@@ -83,6 +83,20 @@ def lib():
         L.orc_rd.restype = ctypes.c_int
         L.orc_rd.argtypes = [ctypes.c_int, ctypes.POINTER(u64p), ctypes.c_size_t, ctypes.c_uint32,
                              ctypes.c_int, ctypes.POINTER(u64p), u64p]
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        L.orc_e4m3_value.restype = ctypes.c_float
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_rn.restype = ctypes.c_uint8
+        L.orc_e4m3_rn.argtypes = [ctypes.c_double]
+        L.orc_e4m3_rn_array.restype = None
+        L.orc_e4m3_rn_array.argtypes = [ctypes.c_void_p, ctypes.c_size_t, u8p]
+        L.orc_fp8_block_exp.restype = ctypes.c_int
+        L.orc_fp8_block_exp.argtypes = [u16p, ctypes.c_size_t]
+        L.orc_quant_fp8.restype = None
+        L.orc_quant_fp8.argtypes = [u16p, ctypes.c_size_t, u8p, u8p]
+        L.orc_reduce_fp8.restype = ctypes.c_int
+        L.orc_reduce_fp8.argtypes = [ctypes.c_int, ctypes.POINTER(u8p), ctypes.POINTER(u8p),
+                                     ctypes.c_size_t, u16p]
         _lib = L
     return _lib
 
@@ -221,3 +235,58 @@ def rd(in_words, seq0: int, fp32_carry: bool = False, err: np.ndarray | None = N
     if rc != 0:
         raise ValueError("oracle recursive doubling: P must be a power of two in [2, 64]")
     return outs, err
+
+
+# --- fp8-quantised contributions -------------------------------------------
+FP8_BLOCK = 32
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 (OCP "FN") code."""
+    return float(lib().orc_e4m3_value(int(code) & 0xFF))
+
+
+def e4m3_rn(v: float) -> int:
+    """Nearest E4M3 code to v (|v| <= 448), ties to even; else 0x7F."""
+    return int(lib().orc_e4m3_rn(float(v)))
+
+
+def e4m3_rn_array(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64).reshape(-1)
+    out = np.empty(v.size, dtype=np.uint8)
+    lib().orc_e4m3_rn_array(v.ctypes.data, v.size, _ptr8(out))
+    return out
+
+
+def fp8_block_exp(x: np.ndarray) -> int:
+    x = _u16(np.asarray(x)).reshape(-1)
+    return int(lib().orc_fp8_block_exp(_ptr16(x), x.size))
+
+
+def _ptr8(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def quant_fp8(x: np.ndarray):
+    """Returns (codes uint8[n], scales uint8[ceil(n/32)]) for one rank buffer."""
+    x = _u16(np.asarray(x)).reshape(-1)
+    codes = np.empty(x.size, dtype=np.uint8)
+    scales = np.empty(-(-x.size // FP8_BLOCK), dtype=np.uint8)
+    lib().orc_quant_fp8(_ptr16(x), x.size, _ptr8(codes), _ptr8(scales))
+    return codes, scales
+
+
+def reduce_fp8(codes, scales) -> np.ndarray:
+    """Sum of the dequantised contributions of P ranks, rounded to bf16."""
+    cs = [np.ascontiguousarray(c, dtype=np.uint8).reshape(-1) for c in codes]
+    ss = [np.ascontiguousarray(s, dtype=np.uint8).reshape(-1) for s in scales]
+    n = cs[0].size
+    if any(c.size != n for c in cs) or any(s.size != -(-n // FP8_BLOCK) for s in ss) or len(cs) != len(ss):
+        raise ValueError("need P code buffers of n bytes and P scale buffers of ceil(n/32) bytes")
+    out = np.empty(n, dtype=np.uint16)
+    T = ctypes.POINTER(ctypes.c_uint8) * len(cs)
+    rc = lib().orc_reduce_fp8(len(cs), T(*[_ptr8(c) for c in cs]), T(*[_ptr8(s) for s in ss]), n,
+                              _ptr16(out))
+    if rc != 0:
+        raise ValueError("oracle fp8 reduce: P must be in [1, 64]")
+    return out

@@ -233,4 +233,101 @@ int orc_rd(int P, const uint64_t* const* in, size_t n, uint32_t seq0,
     return 0;
 }
 
+/* ---------------------------------------------------------------------------
+ * fp8-quantised contributions ([TBO-AR] diff, the caller passes the
+ * ca_fp8_quant flag of the custom all-reduce; the pages give no scheme).
+ * Reading taken here: each rank's bf16 contribution travels as fp8 E4M3
+ * codes (the OCP "FN" variant: bias 7, no infinities, 0x7F/0xFF are NaN,
+ * largest finite 448) with one power-of-two scale per block of 32
+ * consecutive elements, the block/scale layout of the OCP Microscaling
+ * formats; the scale is the smallest power of two at which no element of
+ * the block exceeds 448 (so nothing clips).  The receiver dequantises
+ * exactly (code value times the scale) and sums in binary32 in rank order
+ * 0..P-1, then rounds once to bf16 as orc_reduce_seq does.
+ * ------------------------------------------------------------------------- */
+
+#define ORC_FP8_BLOCK 32
+
+/* Value of an E4M3 code: sign bit 7, exponent bits 6..3 (bias 7), mantissa
+ * bits 2..0.  Exponent 0: subnormal m * 2^-9; otherwise (1 + m/8) * 2^(e-7);
+ * exponent 15 with mantissa 7 is NaN. */
+float orc_e4m3_value(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (float)(s ? -v : v);
+}
+
+/* Nearest E4M3 code to v, ties to the code with an even mantissa.  Defined
+ * for |v| <= 448; a larger or non-finite v gives the NaN code 0x7F.  The
+ * non-negative codes 0x00..0x7E are in increasing order of value, so the
+ * candidates are the largest code not above |v| and the next one.  The sign
+ * is kept, so a negative value that rounds to zero gives 0x80. */
+uint8_t orc_e4m3_rn(double v) {
+    if (!(fabs(v) <= 448.0)) return 0x7Fu;
+    double a = fabs(v);
+    uint8_t lo = 0;
+    while (lo < 0x7E && (double)orc_e4m3_value((uint8_t)(lo + 1)) <= a) ++lo;
+    uint8_t c = lo;
+    if (lo < 0x7E) {
+        double dl = a - (double)orc_e4m3_value(lo);
+        double dh = (double)orc_e4m3_value((uint8_t)(lo + 1)) - a;
+        if (dh < dl || (dh == dl && (lo & 1u))) c = (uint8_t)(lo + 1);
+    }
+    return (uint8_t)((signbit(v) ? 0x80u : 0u) | c);
+}
+
+void orc_e4m3_rn_array(const double* v, size_t n, uint8_t* out) {
+    for (size_t i = 0; i < n; ++i) out[i] = orc_e4m3_rn(v[i]);
+}
+
+/* Scale exponent of one block: the smallest k in [-127, 127] with
+ * amax <= 448 * 2^k, amax = the largest |x| over the block's finite
+ * elements (0 if none). */
+int orc_fp8_block_exp(const uint16_t* x, size_t len) {
+    double amax = 0.0;
+    for (size_t i = 0; i < len; ++i) {
+        double f = (double)orc_widen(x[i]);
+        if (isfinite(f) && fabs(f) > amax) amax = fabs(f);
+    }
+    int k = -127;
+    while (k < 127 && amax > ldexp(448.0, k)) ++k;
+    return k;
+}
+
+/* Quantise one rank buffer of n bf16 elements: scales[b] = k_b + 127 for
+ * block b (ceil(n/32) blocks, the last one possibly short), and
+ * codes[i] = rn_e4m3(x_i / 2^k_b); a NaN or infinite x_i gives 0x7F. */
+void orc_quant_fp8(const uint16_t* x, size_t n, uint8_t* codes, uint8_t* scales) {
+    for (size_t b0 = 0; b0 < n; b0 += ORC_FP8_BLOCK) {
+        size_t len = n - b0 < ORC_FP8_BLOCK ? n - b0 : ORC_FP8_BLOCK;
+        int k = orc_fp8_block_exp(x + b0, len);
+        scales[b0 / ORC_FP8_BLOCK] = (uint8_t)(k + 127);
+        for (size_t i = b0; i < b0 + len; ++i) {
+            double f = (double)orc_widen(x[i]);
+            codes[i] = isfinite(f) ? orc_e4m3_rn(ldexp(f, -k)) : (uint8_t)0x7Fu;
+        }
+    }
+}
+
+/* Dequantised value of element i of one rank: code value times 2^k
+ * (exact in binary32 for every code and k in [-127, 127]). */
+float orc_dequant_fp8(const uint8_t* codes, const uint8_t* scales, size_t i) {
+    int k = (int)scales[i / ORC_FP8_BLOCK] - 127;
+    return (float)ldexp((double)orc_e4m3_value(codes[i]), k);
+}
+
+/* out[i] = rn(((d_0 + d_1) + d_2) + ... + d_{P-1}) over the dequantised
+ * contributions, binary32 sums in rank order, one bf16 rounding. */
+int orc_reduce_fp8(int P, const uint8_t* const* codes, const uint8_t* const* scales, size_t n,
+                   uint16_t* out) {
+    if (P < 1 || P > ORC_MAX_P) return -1;
+    for (size_t i = 0; i < n; ++i) {
+        float acc = orc_dequant_fp8(codes[0], scales[0], i);
+        for (int p = 1; p < P; ++p) acc = acc + orc_dequant_fp8(codes[p], scales[p], i);
+        out[i] = orc_rn(acc);
+    }
+    return 0;
+}
+
 int orc_version(void) { return 1; }

@@ -10,6 +10,7 @@ import subprocess
 
 import numpy as np
 import pytest
+import torch
 
 import exact_ieee as X
 import oracle
@@ -50,6 +51,17 @@ MUTANTS = {
         for (int s = 0; s < P - 1; ++s) {"""),
     "chunk_drops_partial_tail": ("for (size_t c0 = e0; c0 < e1; c0 += chunk_elems) {",
                                  "for (size_t c0 = e0; c0 + chunk_elems <= e1; c0 += chunk_elems) {"),
+    "fp8_scale_off_by_one": ("while (k < 127 && amax > ldexp(448.0, k)) ++k;",
+                             "while (k < 127 && amax >= ldexp(448.0, k)) ++k;"),
+    "fp8_ties_away": ("if (dh < dl || (dh == dl && (lo & 1u))) c = (uint8_t)(lo + 1);",
+                      "if (dh <= dl) c = (uint8_t)(lo + 1);"),
+    "fp8_subnormal_exponent": ("double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);",
+                               "double v = e == 0 ? ldexp((double)m, -10) : ldexp((double)(8 + m), e - 10);"),
+    "fp8_value_drops_sign": ("return (float)(s ? -v : v);", "(void)s; return (float)v;"),
+    "fp8_scale_bias": ("scales[b0 / ORC_FP8_BLOCK] = (uint8_t)(k + 127);",
+                       "scales[b0 / ORC_FP8_BLOCK] = (uint8_t)(k + 128);"),
+    "fp8_amax_counts_non_finite": ("if (isfinite(f) && fabs(f) > amax) amax = fabs(f);",
+                                   "if (fabs(f) > amax) amax = fabs(f);"),
 }
 
 
@@ -124,6 +136,29 @@ def pins_failed():
         dat, e = oracle.unpack(outs[0], 1)
         check("rd_seq", int(e[0]) == 0 and int(rd_err[0]) == 0)
         check("rd_tree", all(int(dat[i]) == X.tree_sum([int(z[i]) for z in zs], True) for i in range(24)))
+        # fp8: code values and rounding against torch, the scale at and just
+        # above 448, non-finite inputs, exact round trip and sum on the grid
+        codes = np.arange(256, dtype=np.uint8)
+        tv = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+        ov = np.array([oracle.e4m3_value(c) for c in codes], dtype=np.float32)
+        check("fp8_values", np.all((tv == ov) | (np.isnan(tv) & np.isnan(ov))))
+        f = ((np.arange(65536, dtype=np.uint32) << 16).view(np.float32))
+        f = f[np.isfinite(f) & (np.abs(f) <= 448)]
+        tc = torch.from_numpy(f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        check("fp8_rn", np.array_equal(oracle.e4m3_rn_array(f.astype(np.float64)), tc))
+        blk = np.zeros(32, dtype=np.uint16)
+        blk[3] = 0x43E0                                    # 448
+        k_at = oracle.fp8_block_exp(blk)
+        blk[3] = 0x43E1
+        check("fp8_scale", k_at == 0 and oracle.fp8_block_exp(blk) == 1)
+        blk[:4] = [0x7FC0, 0x7F80, 0xFF80, 0x3F80]
+        check("fp8_non_finite", oracle.fp8_block_exp(blk) == -8)
+        ints = [synth.integers(700, -15, 15, 934, p) for p in range(5)]
+        q = [oracle.quant_fp8(x) for x in ints]
+        got = oracle.reduce_fp8([c for c, _ in q], [s for _, s in q])
+        exact = np.sum([((x.astype(np.uint32) << 16).view(np.float32)).astype(np.int64) for x in ints], axis=0)
+        check("fp8_grid_sum", np.array_equal((got.astype(np.uint32) << 16).view(np.float32),
+                                             exact.astype(np.float32)))
     except Exception as ex:  # a mutant that crashes a wrapper counts as caught
         failed.append(f"exception: {ex!r}")
     return failed
