@@ -465,6 +465,7 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     log("graph latency measured")
 
     res.update(overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1))
+    res.update(fp8(tar, torch, dev, main_s, ins, outs))
 
     # ubatch reduce at its own shape: [16384 x 16384] per rank, 2 streams, 1 MiB chunks
     from tensor_all_reduce_amd import synth
@@ -620,6 +621,82 @@ def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
                                                     "serial_ms": round(t_rf + t_w, 4),
                                                     "pipelined_ms": round(t_wpipe, 4),
                                                     "overlap_fraction": round(ov_w, 3)}}}
+
+
+def fp8(tar, torch, dev, main_s, ins, outs):
+    """fp8-quantised contributions at the prefill shape (P = 8, [16384 x
+    8192] per rank) and at the decode sizes: quantise all P buffers (one
+    launch), then reduce into one output or into all P.  Algorithmic bytes:
+    quantise P (2n + n + n/32), reduce P (n + n/32) + 2n per output."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(reps):
+            fn()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    n = ROWS * HIDDEN
+    nb = tar.fp8_scale_count(n)
+    codes = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(P)]
+    scales = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(P)]
+    b_q = P * (3 * n + nb)
+    b_r1 = P * (n + nb) + 2 * n
+    b_rp = P * (n + nb) + P * 2 * n
+    t_q = timed(lambda: tar.ar_quantize_fp8(ins, codes, scales), 10)
+    t_r1 = timed(lambda: tar.ar_reduce_fp8(codes, scales, outs[:1]), 10)
+    t_rp = timed(lambda: tar.ar_reduce_fp8(codes, scales, outs), 10)
+    g = lambda b, t: round(b / (t * 1e-3) / 1e9, 1)
+    res = {"quantize_x8": {"ms": round(t_q, 4), "GBps": g(b_q, t_q), "frac_of_peak": round(g(b_q, t_q) / PEAK_HBM_GBPS, 4)},
+           "reduce_one_output": {"ms": round(t_r1, 4), "GBps": g(b_r1, t_r1),
+                                 "frac_of_peak": round(g(b_r1, t_r1) / PEAK_HBM_GBPS, 4)},
+           "reduce_all_outputs": {"ms": round(t_rp, 4), "GBps": g(b_rp, t_rp),
+                                  "frac_of_peak": round(g(b_rp, t_rp) / PEAK_HBM_GBPS, 4)}}
+    log(f"fp8 prefill: quantise {t_q:.3f} ms ({g(b_q, t_q):.0f} GB/s), reduce->1 {t_r1:.3f} ms "
+        f"({g(b_r1, t_r1):.0f} GB/s), reduce->{P} {t_rp:.3f} ms ({g(b_rp, t_rp):.0f} GB/s)")
+    del codes, scales
+    # decode sizes: 100 calls captured in one HIP graph, replayed (per-call
+    # time without the host's launch cost, as in latency_hip_graph)
+    side = torch.cuda.Stream()
+    side.wait_stream(main_s)
+
+    def graph_us(fn):
+        with torch.cuda.stream(side):
+            fn(side)
+            side.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=side):
+                for _ in range(100):
+                    fn(side)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(20):
+            gr.replay()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / 2000, 2)
+
+    lat = {}
+    for T in (8, 32, 128):
+        m = T * HIDDEN
+        xi = [x[:m] for x in ins]
+        xo = [o[:m] for o in outs]
+        cs = [torch.empty(m, dtype=torch.uint8, device=dev) for _ in range(P)]
+        ss = [torch.empty(tar.fp8_scale_count(m), dtype=torch.uint8, device=dev) for _ in range(P)]
+        lat[f"{2 * m // 1024}KiB"] = {
+            "quantize_x8": graph_us(lambda st: tar.ar_quantize_fp8(xi, cs, ss, stream=st)),
+            "reduce_one": graph_us(lambda st: tar.ar_reduce_fp8(cs, ss, xo[:1], stream=st)),
+            "reduce_all": graph_us(lambda st: tar.ar_reduce_fp8(cs, ss, xo, stream=st))}
+    res["decode_us_per_call_hip_graph"] = lat
+    log("fp8 decode sizes timed")
+    return {"fp8": res}
 
 
 def cpu_baseline(args, np):

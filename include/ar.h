@@ -226,6 +226,9 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 #define AR_KERNEL_UNPACK_WAIT 9 /* ar_unpack_fused_wait; wg_per_cu sets the
                                    persistent grid, no LDS is requested      */
 #define AR_KERNEL_UBATCH_FLAGS 10 /* ar_reduce_ubatch_flags (both variants)  */
+#define AR_KERNEL_QUANT_FP8 11  /* ar_quantize_fp8                          */
+#define AR_KERNEL_REDUCE_FP8 12 /* ar_reduce_fp8, one output               */
+#define AR_KERNEL_REDUCE_FP8_ALL 13 /* ar_reduce_fp8, P outputs            */
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu);
 int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
                         int* wg_per_cu);
@@ -269,6 +272,48 @@ int ar_reduce_ubatch_flags(const void* const* ins, void* const* outs, int P, siz
                            size_t chunk_bytes, int variant, void* const* streams,
                            uint32_t* chunk_done, uint32_t* chunk_tiles, size_t n_flags,
                            uint32_t epoch);
+
+/*
+ * fp8-quantised contributions ([TBO-AR] reviewed diff: the custom
+ * all-reduce call site passes a ca_fp8_quant flag; the page gives no
+ * scheme, so the following is this library's reading).  A rank's bf16
+ * buffer travels as E4M3 codes -- the OCP "FN" encoding: bias 7, no
+ * infinities, 0x7F / 0xFF are NaN, largest finite 448 -- with one
+ * power-of-two scale per block of 32 consecutive elements (the block and
+ * scale layout of the OCP Microscaling formats).
+ *
+ * ar_quantize_fp8: for each of the P buffers xs[p] (n bf16 elements):
+ *   scales[p][b] = k_b + 127, where k_b is the smallest integer in
+ *                  [-127, 127] with max |x_i| <= 448 * 2^k_b over the finite
+ *                  elements of block b (elements 32b .. min(32b+32, n)-1;
+ *                  0 if none); so no element is clipped.
+ *   codes[p][i]  = the E4M3 code nearest to x_i / 2^k_b (ties to even
+ *                  mantissa; the sign is kept, so -0 and negative values that
+ *                  round to zero give 0x80); a NaN or infinite x_i gives 0x7F.
+ *   xs, codes   host arrays of P device pointers; xs[p] and codes[p] 16-byte
+ *               aligned, codes[p] n bytes.
+ *   scales      host array of P device pointers, ceil(n/32) bytes each, any
+ *               alignment.
+ * All P buffers are quantised by one launch.  No code or scale buffer may
+ * overlap an input or another code / scale buffer.
+ *
+ * ar_reduce_fp8: out[i] = rn(((d_0 + d_1) + d_2) + ... + d_{P-1}), where
+ *   d_p = value(codes[p][i]) * 2^(scales[p][i/32] - 127) is exact in
+ *   binary32 (only an element of magnitude >= 1.9375 * 2^127, the top 8
+ *   finite bf16 values, dequantises to infinity: its code is 256 at scale
+ *   2^120), the sums are binary32 in rank order and rn is the same bf16
+ *   rounding as ar_reduce_oneshot (NaN -> 0x7FC0; a NaN code poisons its
+ *   element).  n_out == 1: outs[0] only (one rank's share); n_out == P:
+ *   every outs[r] gets the sum (all-reduce write mode).  outs[] 16-byte
+ *   aligned, n bf16 each, disjoint from each other and from every code and
+ *   scale buffer.
+ * Errors (both): AR_ERR_INVALID for NULL pointers, P outside [1, 8] or
+ *   n_out not in {1, P}; AR_ERR_ALIGN; AR_ERR_ALIAS.  n == 0 queues nothing.
+ */
+int ar_quantize_fp8(const void* const* xs, uint8_t* const* codes, uint8_t* const* scales, int P,
+                    size_t n, void* stream);
+int ar_reduce_fp8(const uint8_t* const* codes, const uint8_t* const* scales, int P, void* const* outs,
+                  int n_out, size_t n, void* stream);
 
 /*
  * Initialise an error record for ar_unpack_fused / ar_rd_schedule on

@@ -310,8 +310,11 @@ void orc_quant_fp8(const uint16_t* x, size_t n, uint8_t* codes, uint8_t* scales)
     }
 }
 
-/* Dequantised value of element i of one rank: code value times 2^k
- * (exact in binary32 for every code and k in [-127, 127]). */
+/* Dequantised value of element i of one rank: code value times 2^k, exact
+ * in binary32 except at the top of the range: a block whose maximum is
+ * 1.9375 * 2^127 or more (the 8 largest finite bf16 magnitudes) gets k = 120
+ * and that element the code of 256, and 256 * 2^120 = 2^128 is infinite in
+ * binary32, as rounding such a value to bf16 directly would also be. */
 float orc_dequant_fp8(const uint8_t* codes, const uint8_t* scales, size_t i) {
     int k = (int)scales[i / ORC_FP8_BLOCK] - 127;
     return (float)ldexp((double)orc_e4m3_value(codes[i]), k);

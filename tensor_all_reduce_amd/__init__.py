@@ -27,6 +27,8 @@ __all__ = [
     "AR_KERNEL_ONESHOT", "AR_KERNEL_2STAGE", "AR_KERNEL_UBATCH", "AR_KERNEL_RS", "AR_KERNEL_AG",
     "AR_KERNEL_PACK", "AR_KERNEL_UNPACK", "AR_KERNEL_RD", "AR_KERNEL_RDSTEP", "AR_KERNEL_UNPACK_WAIT",
     "AR_KERNEL_UBATCH_FLAGS", "ar_unpack_fused_wait", "ar_reduce_ubatch_flags", "ubatch_chunk_count",
+    "AR_KERNEL_QUANT_FP8", "AR_KERNEL_REDUCE_FP8", "AR_KERNEL_REDUCE_FP8_ALL", "ar_quantize_fp8", "ar_reduce_fp8", "fp8_scale_count",
+    "FP8_BLOCK",
 ]
 
 AR_OK = 0
@@ -51,6 +53,10 @@ AR_KERNEL_RD = 7
 AR_KERNEL_RDSTEP = 8
 AR_KERNEL_UNPACK_WAIT = 9
 AR_KERNEL_UBATCH_FLAGS = 10
+AR_KERNEL_QUANT_FP8 = 11
+AR_KERNEL_REDUCE_FP8 = 12
+AR_KERNEL_REDUCE_FP8_ALL = 13
+FP8_BLOCK = 32                  # elements per power-of-two scale
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libarcore.so")
@@ -105,6 +111,12 @@ def lib():
                                              ctypes.POINTER(_vp), _vp, _vp, _sz, _u32]
         L.ar_err_init.restype = ctypes.c_int
         L.ar_err_init.argtypes = [_vp, _vp]
+        L.ar_quantize_fp8.restype = ctypes.c_int
+        L.ar_quantize_fp8.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                      ctypes.c_int, _sz, _vp]
+        L.ar_reduce_fp8.restype = ctypes.c_int
+        L.ar_reduce_fp8.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int,
+                                    ctypes.POINTER(_vp), ctypes.c_int, _sz, _vp]
         L.ar_set_launch_shape.restype = ctypes.c_int
         L.ar_set_launch_shape.argtypes = [ctypes.c_int] * 6
         ip = ctypes.POINTER(ctypes.c_int)
@@ -294,6 +306,39 @@ def ar_reduce_ubatch_flags(ins: Sequence, outs: Sequence, rows: int, hidden: int
     _check(lib().ar_reduce_ubatch_flags(_ptr_array(ip), _ptr_array(op), len(ip), int(rows), int(hidden),
                                         int(n_ubatch), ub, int(chunk_bytes), int(variant), sp, dp, tp,
                                         nf, int(epoch) & 0xFFFFFFFF), "ar_reduce_ubatch_flags")
+
+
+def fp8_scale_count(n: int) -> int:
+    """Scale bytes per rank for n elements: one per block of 32."""
+    return -(-int(n) // FP8_BLOCK)
+
+
+def ar_quantize_fp8(xs: Sequence, codes: Sequence, scales: Sequence, n: int | None = None,
+                    stream=None) -> None:
+    """Quantise P bf16 buffers to E4M3 codes (uint8[n]) and per-32-element
+    power-of-two scales (uint8[ceil(n/32)], exponent + 127), one launch."""
+    n = xs[0].numel() if n is None else int(n)
+    xp = _bufs(xs, 2, "xs", n)
+    cp = _bufs(codes, 1, "codes", n)
+    sp = _bufs(scales, 1, "scales", fp8_scale_count(n))
+    if not (len(xp) == len(cp) == len(sp)):
+        raise ValueError("need one code and one scale buffer per input")
+    _check(lib().ar_quantize_fp8(_ptr_array(xp), _ptr_array(cp), _ptr_array(sp), len(xp), n,
+                                 _stream(stream)), "ar_quantize_fp8")
+
+
+def ar_reduce_fp8(codes: Sequence, scales: Sequence, outs: Sequence, n: int | None = None,
+                  stream=None) -> None:
+    """outs[r][:n] = rank-order binary32 sum of the dequantised contributions,
+    rounded to bf16; len(outs) is 1 (one share) or P (all-reduce)."""
+    n = codes[0].numel() if n is None else int(n)
+    cp = _bufs(codes, 1, "codes", n)
+    sp = _bufs(scales, 1, "scales", fp8_scale_count(n))
+    op = _bufs(outs, 2, "outs", n)
+    if len(cp) != len(sp):
+        raise ValueError("need one scale buffer per code buffer")
+    _check(lib().ar_reduce_fp8(_ptr_array(cp), _ptr_array(sp), len(cp), _ptr_array(op), len(op), n,
+                               _stream(stream)), "ar_reduce_fp8")
 
 
 def ar_err_init(d_err, stream=None) -> None:

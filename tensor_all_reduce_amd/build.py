@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libarcore.so")
 BENCH_LIB = os.path.join(HERE, "libarbench.so")
-SOURCES = ["ar_api.hip", "ar_reduce.hip", "ar_fused.hip"]
+SOURCES = ["ar_api.hip", "ar_reduce.hip", "ar_fused.hip", "ar_fp8.hip"]
 BENCH_SOURCES = ["ar_bench.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

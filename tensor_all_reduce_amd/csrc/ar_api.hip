@@ -46,12 +46,15 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
     {64, 1, 1, 1, 8, 0},    // staged recursive-doubling step, 8 -> 8
     {256, 1, 0, 0, 1, 0},   // waiting unpack: 1 persistent workgroup per CU
-    {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few fences and counter atomics per chunk
+    {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few store waits and counter atomics per chunk
+    {64, 2, 1, 1, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
+    {64, 1, 1, 1, 10, 0},   // fp8 reduce, P code streams -> 1 output
+    {128, 1, 0, 0, 3, 0},   // fp8 reduce, P code streams -> P outputs
 };
 constexpr const char* kShapeEnv[ar::kKinds] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
     "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT",
-    "AR_SHAPE_UBATCH_FLAGS"};
+    "AR_SHAPE_UBATCH_FLAGS", "AR_SHAPE_QUANT_FP8", "AR_SHAPE_REDUCE_FP8", "AR_SHAPE_REDUCE_FP8_ALL"};
 
 std::mutex g_mu;
 DevInfo g_dev[kMaxDevices];
@@ -271,6 +274,67 @@ int ar_unpack_fused_wait(const uint64_t* words, void* x, size_t n, uint32_t expe
   ar::Launch L;
   if ((rc = resolve(&L, stream))) return rc;
   return hip_status(ar::launch_unpack_wait(L, words, x, n, expected_seq, max_spins, d_err));
+}
+
+int ar_quantize_fp8(const void* const* xs, uint8_t* const* codes, uint8_t* const* scales, int P,
+                    size_t n, void* stream) {
+  ar::InPtrs in{};
+  ar::ByteOut co{}, sc{};
+  Span si[AR_MAX_RANKS], sb[2 * AR_MAX_RANKS];
+  int rc = check_ranks(xs, P, n, &in, si);
+  if (rc) return rc;
+  if (!codes || !scales) return AR_ERR_INVALID;
+  const size_t nblk = (n + 31) / 32;
+  for (int p = 0; p < P; ++p) {
+    if (!codes[p] || !scales[p]) return AR_ERR_INVALID;
+    if (!aligned16(codes[p])) return AR_ERR_ALIGN;
+    co.p[p] = codes[p];
+    sc.p[p] = scales[p];
+    sb[2 * p] = span_of(codes[p], n);
+    sb[2 * p + 1] = span_of(scales[p], nblk);
+  }
+  for (int a = 0; a < 2 * P; ++a) {
+    if ((rc = check_disjoint(sb[a], si, P))) return rc;
+    for (int b = a + 1; b < 2 * P; ++b)
+      if (overlap(sb[a], sb[b])) return AR_ERR_ALIAS;
+  }
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  return hip_status(ar::launch_quant_fp8(L, in, co, sc, P, n));
+}
+
+int ar_reduce_fp8(const uint8_t* const* codes, const uint8_t* const* scales, int P, void* const* outs,
+                  int n_out, size_t n, void* stream) {
+  if (!codes || !scales || !outs || P < 1 || P > AR_MAX_RANKS || mul_overflows(n, 2))
+    return AR_ERR_INVALID;
+  if (n_out != 1 && n_out != P) return AR_ERR_INVALID;
+  ar::ByteIn co{}, sc{};
+  ar::OutPtrs out{};
+  Span sb[2 * AR_MAX_RANKS], so[AR_MAX_RANKS];
+  const size_t nblk = (n + 31) / 32;
+  for (int p = 0; p < P; ++p) {
+    if (!codes[p] || !scales[p]) return AR_ERR_INVALID;
+    if (!aligned16(codes[p])) return AR_ERR_ALIGN;
+    co.p[p] = codes[p];
+    sc.p[p] = scales[p];
+    sb[2 * p] = span_of(codes[p], n);
+    sb[2 * p + 1] = span_of(scales[p], nblk);
+  }
+  for (int o = 0; o < n_out; ++o) {
+    if (!outs[o]) return AR_ERR_INVALID;
+    if (!aligned16(outs[o])) return AR_ERR_ALIGN;
+    out.p[o] = outs[o];
+    so[o] = span_of(outs[o], n * 2);
+  }
+  int rc;
+  if ((rc = check_outputs(so, 0, so, n_out))) return rc;
+  for (int o = 0; o < n_out; ++o)
+    if ((rc = check_disjoint(so[o], sb, 2 * P))) return rc;
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  return hip_status(ar::launch_reduce_fp8(L, co, sc, out, P, n_out, n));
 }
 
 int ar_rd_schedule(const uint64_t* const* in_words, uint64_t* const* out_words, int P, size_t n,

@@ -1,0 +1,262 @@
+// fp8-quantised contributions ("[DSV4] perf(tbo): overlap pure-TP all_reduce
+// on TBO + Delay TP", reviewed diff: the custom all-reduce call site passes a
+// ca_fp8_quant flag; the page gives no scheme).  The reading implemented:
+// each rank's bf16 buffer travels as E4M3 codes (OCP "FN": bias 7, no
+// infinities, 0x7F / 0xFF are NaN, largest finite 448) with one
+// power-of-two scale byte per block of 32 consecutive elements; the scale is
+// the smallest power of two at which no element of the block exceeds 448,
+// so nothing clips.  The receiver dequantises exactly (code value times the
+// scale) and sums in binary32 in rank order 0..P-1, then rounds once to bf16.
+//
+// Quantise: one lane per 8 elements (16 bytes of bf16 in, 8 code bytes out);
+// the 4 lanes of a quad hold one 32-element block and find its largest
+// magnitude with two DPP lane swaps.  x / 2^k is exact (a power-of-two
+// scaling), so the hardware E4M3 conversion (round to nearest even) gives
+// the code of the exact quotient.
+// Reduce: one lane per 16 elements (one 16-byte load of codes per rank plus
+// its block's scale byte), hardware E4M3 -> binary32 conversion (exact),
+// ldexp by the scale (exact), rank-order binary32 sums, the integer
+// nearest-even rounding to bf16 shared with the other reduce kernels.
+#include "ar_device.hpp"
+#include "ar_internal.hpp"
+
+namespace ar {
+namespace {
+
+constexpr int kFp8Block = 32;
+
+// Largest of the 4 values held by one quad of lanes (lanes 4q..4q+3).
+// DPP quad permutations [1,0,3,2] and [2,3,0,1]; every lane must be active.
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
+// Scale exponent k from the binary32 bits A of the block's largest finite
+// magnitude: the smallest k in [-127, 127] with A <= 448 * 2^k.  For a
+// normal A = (1 + F/2^23) * 2^(E-127) and 448 = 1.75 * 2^8, that is E - 135,
+// plus one when the significand exceeds 1.75 (F > 0x600000).  Zero and
+// binary32 subnormals (below 2^-126, far below 448 * 2^-127) give -127;
+// the largest finite bf16 gives 120, so no upper clamp is reached.
+__device__ __forceinline__ int fp8_scale_exp(uint32_t A) {
+  const int E = (int)(A >> 23);
+  if (E == 0) return -127;
+  const int k = E - 135 + ((A & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return k < -127 ? -127 : k;
+}
+
+// Binary32 bits of bf16 element j (0..7) of a 16-byte group.
+__device__ __forceinline__ uint32_t elem_bits(const uint32_t (&w)[4], int j) {
+  return (j & 1) ? (w[j >> 1] & 0xFFFF0000u) : (w[j >> 1] << 16);
+}
+
+// Codes of 4 elements (bits b[0..3]) scaled by 2^-k, as one little-endian
+// word; a NaN or infinite element gives 0x7F.
+__device__ __forceinline__ uint32_t codes4(const uint32_t* b, int k) {
+  const float s0 = __builtin_ldexpf(__uint_as_float(b[0]), -k);
+  const float s1 = __builtin_ldexpf(__uint_as_float(b[1]), -k);
+  const float s2 = __builtin_ldexpf(__uint_as_float(b[2]), -k);
+  const float s3 = __builtin_ldexpf(__uint_as_float(b[3]), -k);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(s0, s1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(s2, s3, w, true);
+  uint32_t bad = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if ((b[j] & 0x7FFFFFFFu) >= 0x7F800000u) bad |= 0xFFu << (8 * j);
+  return ((uint32_t)w & ~bad) | (0x7F7F7F7Fu & bad);
+}
+
+// Workgroup b quantises tile b % tiles of buffer b / tiles; a tile is
+// V * blockDim groups of 8 elements.  Lanes past the end take part in the
+// quad maximum with zeros and store nothing.
+template <int V, bool NTL, bool NTS>
+__global__ __launch_bounds__(kMaxBlock) void k_quant_fp8(InPtrs xs, ByteOut codes, ByteOut scales,
+                                                         size_t n, unsigned tiles) {
+  const unsigned p = blockIdx.x / tiles;
+  const size_t tile0 = (size_t)(blockIdx.x % tiles) * V * blockDim.x;
+  const u32x4* x4 = static_cast<const u32x4*>(xs.p[p]);
+  const uint16_t* x16 = static_cast<const uint16_t*>(xs.p[p]);
+  uint8_t* cp = codes.p[p];
+  uint8_t* sp = scales.p[p];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const size_t g = tile0 + (size_t)u * blockDim.x + threadIdx.x;
+    const size_t i0 = g * 8;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (i0 + 8 <= n) {
+      const u32x4 v = ld4<NTL>(x4 + g);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e = i0 + j < n ? (uint32_t)x16[i0 + j] : 0u;
+        w[j >> 1] |= (j & 1) ? (e << 16) : e;
+      }
+    }
+    uint32_t b[8];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      b[j] = elem_bits(w, j);
+      const uint32_t a = b[j] & 0x7FFFFFFFu;
+      if (a < 0x7F800000u) amax = max(amax, a);
+    }
+    amax = quad_max(amax);
+    const int k = fp8_scale_exp(amax);
+    const uint32_t lo = codes4(b, k), hi = codes4(b + 4, k);
+    if (i0 + 8 <= n) {
+      const uint64_t c = (uint64_t)lo | ((uint64_t)hi << 32);
+      uint64_t* dst = reinterpret_cast<uint64_t*>(cp + i0);
+      if constexpr (NTS) __builtin_nontemporal_store(c, dst);
+      else *dst = c;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (i0 + j < n) cp[i0 + j] = (uint8_t)(((j < 4 ? lo : hi) >> (8 * (j & 3))) & 0xFFu);
+    }
+    if ((threadIdx.x & 3u) == 0 && i0 < n) sp[g >> 2] = (uint8_t)(k + 127);
+  }
+}
+
+// Binary32 value of codes byte-pairs: element 2h and 2h+1 of word w.
+__device__ __forceinline__ void dequant4(uint32_t w, int k, float* d) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  d[0] = __builtin_ldexpf(lo[0], k);
+  d[1] = __builtin_ldexpf(lo[1], k);
+  d[2] = __builtin_ldexpf(hi[0], k);
+  d[3] = __builtin_ldexpf(hi[1], k);
+}
+
+// Flat tiles of V * blockDim groups of 16 elements.  A group that runs past
+// n is done element by element by its lane.
+template <int P, int NOUT, int V, bool NTL, bool NTS>
+__global__ __launch_bounds__(kMaxBlock) void k_reduce_fp8(ByteIn codes, ByteIn scales, OutPtrs out,
+                                                          size_t n) {
+  const size_t tile0 = (size_t)blockIdx.x * V * blockDim.x;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const size_t g = tile0 + (size_t)u * blockDim.x + threadIdx.x;
+    const size_t i0 = g * 16;
+    if (i0 >= n) return;
+    if (i0 + 16 <= n) {
+      u32x4 c[P];
+      int k[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        c[p] = ld4<NTL>(reinterpret_cast<const u32x4*>(codes.p[p]) + g);
+        k[p] = (int)scales.p[p][g >> 1] - 127;
+      }
+      float acc[16];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint32_t cw[4] = {c[p].x, c[p].y, c[p].z, c[p].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float d[4];
+          dequant4(cw[q], k[p], d);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[4 * q + j] = p == 0 ? d[j] : acc[4 * q + j] + d[j];
+        }
+      }
+      u32x4 r0, r1;
+      r0.x = pack_bf16x2(acc[0], acc[1]);
+      r0.y = pack_bf16x2(acc[2], acc[3]);
+      r0.z = pack_bf16x2(acc[4], acc[5]);
+      r0.w = pack_bf16x2(acc[6], acc[7]);
+      r1.x = pack_bf16x2(acc[8], acc[9]);
+      r1.y = pack_bf16x2(acc[10], acc[11]);
+      r1.z = pack_bf16x2(acc[12], acc[13]);
+      r1.w = pack_bf16x2(acc[14], acc[15]);
+#pragma unroll
+      for (int o = 0; o < NOUT; ++o) {
+        u32x4* dst = static_cast<u32x4*>(out.p[o]) + 2 * g;
+        st4<NTS>(dst, r0);
+        st4<NTS>(dst + 1, r1);
+      }
+    } else {
+      for (size_t i = i0; i < n; ++i) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float v = __builtin_amdgcn_cvt_f32_fp8((int)codes.p[p][i], 0);
+          const float d = __builtin_ldexpf(v, (int)scales.p[p][i / kFp8Block] - 127);
+          acc = p == 0 ? d : acc + d;
+        }
+        const uint16_t r = (uint16_t)(rne_hi(acc) >> 16);
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) static_cast<uint16_t*>(out.p[o])[i] = r;
+      }
+    }
+  }
+}
+
+template <int V>
+hipError_t quant_v(const Shape& sh, hipStream_t st, const InPtrs& xs, const ByteOut& codes,
+                   const ByteOut& scales, int P, size_t n) {
+  const size_t groups = cdiv(n, 8);
+  const size_t tiles = cdiv(groups, (size_t)V * sh.block);
+  if (tiles * (size_t)P > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+  const unsigned g = (unsigned)(tiles * P), t = (unsigned)tiles;
+  const dim3 blk(sh.block);
+  if (sh.nt_loads && sh.nt_stores)
+    return launch_k(k_quant_fp8<V, true, true>, g, blk, sh.lds, st, xs, codes, scales, n, t);
+  if (sh.nt_loads) return launch_k(k_quant_fp8<V, true, false>, g, blk, sh.lds, st, xs, codes, scales, n, t);
+  if (sh.nt_stores) return launch_k(k_quant_fp8<V, false, true>, g, blk, sh.lds, st, xs, codes, scales, n, t);
+  return launch_k(k_quant_fp8<V, false, false>, g, blk, sh.lds, st, xs, codes, scales, n, t);
+}
+
+template <int P, int NOUT, int V>
+hipError_t reduce_v(const Shape& sh, hipStream_t st, const ByteIn& codes, const ByteIn& scales,
+                    const OutPtrs& out, size_t n) {
+  const size_t blocks = cdiv(cdiv(n, 16), (size_t)V * sh.block);
+  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+  const unsigned g = (unsigned)blocks;
+  const dim3 blk(sh.block);
+  if (sh.nt_loads && sh.nt_stores)
+    return launch_k(k_reduce_fp8<P, NOUT, V, true, true>, g, blk, sh.lds, st, codes, scales, out, n);
+  if (sh.nt_loads)
+    return launch_k(k_reduce_fp8<P, NOUT, V, true, false>, g, blk, sh.lds, st, codes, scales, out, n);
+  if (sh.nt_stores)
+    return launch_k(k_reduce_fp8<P, NOUT, V, false, true>, g, blk, sh.lds, st, codes, scales, out, n);
+  return launch_k(k_reduce_fp8<P, NOUT, V, false, false>, g, blk, sh.lds, st, codes, scales, out, n);
+}
+
+template <int P>
+hipError_t reduce_p(const Shape& sh, hipStream_t st, const ByteIn& codes, const ByteIn& scales,
+                    const OutPtrs& out, int nout, size_t n) {
+  if (nout == 1) {
+    if (sh.vec == 2) return reduce_v<P, 1, 2>(sh, st, codes, scales, out, n);
+    return reduce_v<P, 1, 1>(sh, st, codes, scales, out, n);
+  }
+  if (sh.vec == 2) return reduce_v<P, P, 2>(sh, st, codes, scales, out, n);
+  return reduce_v<P, P, 1>(sh, st, codes, scales, out, n);
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const Launch& L, const InPtrs& xs, const ByteOut& codes,
+                            const ByteOut& scales, int P, size_t n) {
+  const Shape& sh = L.shape[kQuantFp8];
+  if (sh.vec == 2) return quant_v<2>(sh, L.stream, xs, codes, scales, P, n);
+  return quant_v<1>(sh, L.stream, xs, codes, scales, P, n);
+}
+
+hipError_t launch_reduce_fp8(const Launch& L, const ByteIn& codes, const ByteIn& scales,
+                             const OutPtrs& out, int P, int nout, size_t n) {
+  const Shape& sh = L.shape[nout == 1 ? kReduceFp8 : kReduceFp8All];
+  switch (P) {
+    case 1: return reduce_p<1>(sh, L.stream, codes, scales, out, nout, n);
+    case 2: return reduce_p<2>(sh, L.stream, codes, scales, out, nout, n);
+    case 3: return reduce_p<3>(sh, L.stream, codes, scales, out, nout, n);
+    case 4: return reduce_p<4>(sh, L.stream, codes, scales, out, nout, n);
+    case 5: return reduce_p<5>(sh, L.stream, codes, scales, out, nout, n);
+    case 6: return reduce_p<6>(sh, L.stream, codes, scales, out, nout, n);
+    case 7: return reduce_p<7>(sh, L.stream, codes, scales, out, nout, n);
+    case 8: return reduce_p<8>(sh, L.stream, codes, scales, out, nout, n);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ar

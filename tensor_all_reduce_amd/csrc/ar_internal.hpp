@@ -38,6 +38,9 @@ enum Kind {
   kRDStep,       // staged recursive-doubling step
   kUnpackWait,   // unpack that waits for the producer (persistent grid, no LDS request)
   kUbatchFlags,  // chunked reduce that publishes per-chunk completion flags
+  kQuantFp8,     // bf16 -> fp8 codes + block scales, P buffers in one launch
+  kReduceFp8,    // P fp8 contributions -> 1 bf16 output
+  kReduceFp8All, // P fp8 contributions -> P bf16 outputs
   kKinds
 };
 
@@ -62,6 +65,8 @@ struct ChunkSignal {
   uint32_t base;     // index of this launch's first chunk in done / tiles
 };
 struct WordOut { uint64_t* p[AR_MAX_RANKS]; };
+struct ByteIn { const uint8_t* p[AR_MAX_RANKS]; };
+struct ByteOut { uint8_t* p[AR_MAX_RANKS]; };
 
 hipError_t launch_oneshot(const Launch& L, const InPtrs& in, int P, void* out, size_t n);
 hipError_t launch_2stage_fused(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
@@ -72,6 +77,11 @@ hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                           size_t e0, size_t e1, size_t chunk_elems, int two_stage,
                           const ChunkSignal& sig);
+
+hipError_t launch_quant_fp8(const Launch& L, const InPtrs& xs, const ByteOut& codes,
+                            const ByteOut& scales, int P, size_t n);
+hipError_t launch_reduce_fp8(const Launch& L, const ByteIn& codes, const ByteIn& scales,
+                             const OutPtrs& out, int P, int nout, size_t n);
 
 hipError_t launch_pack(const Launch& L, const void* x, uint64_t* w, size_t n, uint32_t seq);
 hipError_t launch_unpack(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,

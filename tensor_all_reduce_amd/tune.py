@@ -38,12 +38,14 @@ KINDS = {
     "oneshot": tar.AR_KERNEL_ONESHOT, "2stage": tar.AR_KERNEL_2STAGE, "ubatch": tar.AR_KERNEL_UBATCH,
     "rs": tar.AR_KERNEL_RS, "ag": tar.AR_KERNEL_AG, "pack": tar.AR_KERNEL_PACK,
     "unpack": tar.AR_KERNEL_UNPACK, "rd": tar.AR_KERNEL_RD, "rdstep": tar.AR_KERNEL_RDSTEP,
-    "ubatch_flags": tar.AR_KERNEL_UBATCH_FLAGS,
+    "ubatch_flags": tar.AR_KERNEL_UBATCH_FLAGS, "quant_fp8": tar.AR_KERNEL_QUANT_FP8,
+    "reduce_fp8": tar.AR_KERNEL_REDUCE_FP8_ALL, "reduce_fp8_one": tar.AR_KERNEL_REDUCE_FP8,
 }
 
 
 def candidates(kind: str):
-    vecs = (1, 2) if kind in ("oneshot", "2stage", "ubatch", "ubatch_flags") else (1,)
+    vecs = (1, 2) if kind in ("oneshot", "2stage", "ubatch", "ubatch_flags", "quant_fp8", "reduce_fp8",
+                              "reduce_fp8_one") else (1,)
     return list(itertools.product((64, 128, 256), vecs, (0, 1), (0, 1), WGS))
 
 
@@ -79,6 +81,9 @@ def main(argv=None):
     for r in range(P):
         tar.ar_pack_fused(ins[r], words[r], 1)
     tar.ar_err_init(err)
+    codes = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(P)]
+    scales = [torch.empty(tar.fp8_scale_count(n), dtype=torch.uint8, device=dev) for _ in range(P)]
+    tar.ar_quantize_fp8(ins, codes, scales)
 
     def op(kind):
         if kind == "oneshot":
@@ -111,10 +116,19 @@ def main(argv=None):
             tar.ar_rd_schedule(words, rdo, 1, err)
         elif kind == "rdstep":
             tar.ar_rd_schedule(words, rdo, 1, err, mailbox=mailbox, flags=tar.AR_RD_STAGED)
+        elif kind == "quant_fp8":
+            tar.ar_quantize_fp8(ins, codes, scales)
+        elif kind == "reduce_fp8":
+            tar.ar_reduce_fp8(codes, scales, outs)
+        elif kind == "reduce_fp8_one":
+            tar.ar_reduce_fp8(codes, scales, outs[:1])
 
     credited = {"oneshot": (P + 1) * B, "2stage": 2 * P * B, "ubatch": 2 * P * B, "ubatch_flags": 2 * P * B,
                 "rs": 2 * P * B,
-                "ag": 2 * P * B, "pack": 3 * P * B, "unpack": 3 * P * B, "rd": 4 * P * B, "rdstep": 4 * P * B}
+                "ag": 2 * P * B, "pack": 3 * P * B, "unpack": 3 * P * B, "rd": 4 * P * B, "rdstep": 4 * P * B,
+                "quant_fp8": P * (3 * n + tar.fp8_scale_count(n)),
+                "reduce_fp8": P * (n + tar.fp8_scale_count(n)) + P * B,
+                "reduce_fp8_one": P * (n + tar.fp8_scale_count(n)) + B}
 
     def time_one(kind):
         op(kind)

@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["ar_reduce_oneshot", "ar_reduce_2stage", "ar_pack_fused", "ar_unpack_fused",
-                 "ar_rd_schedule", "ar_reduce_ubatch", "ar_status_str", "ar_version", "ar_err_init"]:
+                 "ar_rd_schedule", "ar_reduce_ubatch", "ar_status_str", "ar_version", "ar_err_init",
+                 "ar_unpack_fused_wait", "ar_reduce_ubatch_flags", "ar_quantize_fp8", "ar_reduce_fp8"]:
         assert want in names
 
 
@@ -182,6 +183,38 @@ def test_ubatch_flags_validation():
     assert tar.ubatch_chunk_count(16384, 16384, 2, None, 1 << 20) == 512
 
 
+def test_fp8_validation():
+    L = tar.lib()
+    xs = arr(A, B)
+    codes = arr(C, C + 0x1000)
+    scales = arr(C + 0x2000, C + 0x2001)          # one byte each for n = 32: any alignment
+    # n = 32: codes 32 bytes, scales 1 byte; n = 0 passes every check and launches nothing
+    assert L.ar_quantize_fp8(xs, codes, scales, 2, 0, None) == tar.AR_OK
+    assert L.ar_quantize_fp8(None, codes, scales, 2, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_quantize_fp8(xs, codes, scales, 0, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_quantize_fp8(xs, codes, scales, 9, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_quantize_fp8(xs, arr(C, None), scales, 2, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_quantize_fp8(xs, arr(C + 8, C + 0x1000), scales, 2, 32, None) == tar.AR_ERR_ALIGN
+    assert L.ar_quantize_fp8(arr(A + 2, B), codes, scales, 2, 32, None) == tar.AR_ERR_ALIGN
+    assert L.ar_quantize_fp8(xs, arr(C, C + 16), scales, 2, 32, None) == tar.AR_ERR_ALIAS   # codes overlap
+    assert L.ar_quantize_fp8(xs, codes, arr(C + 0x2000, C + 0x2000), 2, 32, None) == tar.AR_ERR_ALIAS
+    assert L.ar_quantize_fp8(xs, codes, arr(C + 31, C + 0x2001), 2, 32, None) == tar.AR_ERR_ALIAS  # scale in codes
+    assert L.ar_quantize_fp8(xs, arr(A + 32, C), scales, 2, 32, None) == tar.AR_ERR_ALIAS    # codes over input
+    outs = arr(A, B)
+    assert L.ar_reduce_fp8(codes, scales, 2, outs, 2, 0, None) == tar.AR_OK
+    assert L.ar_reduce_fp8(codes, scales, 2, outs, 3, 32, None) == tar.AR_ERR_INVALID       # n_out not 1 or P
+    assert L.ar_reduce_fp8(codes, scales, 2, outs, 0, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_fp8(codes, scales, 0, outs, 1, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_fp8(None, scales, 2, outs, 1, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_fp8(codes, arr(C + 0x2000, None), 2, outs, 1, 32, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_fp8(arr(C + 4, C + 0x1000), scales, 2, outs, 1, 32, None) == tar.AR_ERR_ALIGN
+    assert L.ar_reduce_fp8(codes, scales, 2, arr(A + 2, B), 1, 32, None) == tar.AR_ERR_ALIGN
+    assert L.ar_reduce_fp8(codes, scales, 2, arr(A, A + 32), 2, 32, None) == tar.AR_ERR_ALIAS  # outputs overlap
+    assert L.ar_reduce_fp8(codes, scales, 2, arr(C, B), 2, 32, None) == tar.AR_ERR_ALIAS      # output over codes
+    assert L.ar_reduce_fp8(codes, scales, 2, arr(C + 0x1FF0, B), 2, 32, None) == tar.AR_ERR_ALIAS  # over a scale
+    assert tar.fp8_scale_count(0) == 0 and tar.fp8_scale_count(32) == 1 and tar.fp8_scale_count(33) == 2
+
+
 def test_err_init_validation():
     L = tar.lib()
     assert L.ar_err_init(None, None) == tar.AR_ERR_INVALID
@@ -196,13 +229,13 @@ def test_binding_raises_on_error():
 
 def test_launch_shape_roundtrip_and_validation():
     L = tar.lib()
-    for kind in range(11):
+    for kind in range(14):
         before = tar.ar_get_launch_shape(kind)
         tar.ar_set_launch_shape(kind, 128, 2, 0, 1, 7)
         assert tar.ar_get_launch_shape(kind) == (128, 2, 0, 1, 7)
         tar.ar_set_launch_shape(kind, *before)
         assert tar.ar_get_launch_shape(kind) == before
-    assert L.ar_set_launch_shape(11, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(14, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 96, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 3, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 1, 2, 1, 0) == tar.AR_ERR_INVALID

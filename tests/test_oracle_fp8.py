@@ -198,6 +198,18 @@ def test_reduce_propagates_non_finite_as_canonical_nan():
     assert list(got) == [0x7FC0, 0x7FC0, 0x0000, 0x0000]       # 2 + (-2) = +0; +0 + -0 = +0
 
 
+def test_top_of_the_bf16_range_dequantises_to_infinity():
+    # bf16 0x7F78 = 1.9375 * 2^127 and above: k = 120, x / 2^120 >= 248 rounds
+    # (ties to even) to 256, and 256 * 2^120 = 2^128 overflows binary32;
+    # 0x7F77 stays below the tie and keeps a finite value
+    x = np.array([0x7F78, 0x7F7F, 0xFF7A, 0x7F77] + [0] * 28, dtype=np.uint16)
+    codes, scales = oracle.quant_fp8(x)
+    assert int(scales[0]) - 127 == 120
+    assert list(codes[:4]) == [0x78, 0x78, 0xF8, 0x77]       # 256, 256, -256, 240
+    got = oracle.reduce_fp8([codes], [scales])
+    assert list(got[:4]) == [0x7F80, 0x7F80, 0xFF80, int(bf16_of([240.0 * 2.0 ** 120])[0])]
+
+
 def test_reduce_empty():
     c = np.zeros(0, dtype=np.uint8)
     s = np.zeros(0, dtype=np.uint8)
