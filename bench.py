@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu-all-cores", action="store_true",
+                    help="time the oracle on one core only (skip the all-cores run)")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -705,9 +707,14 @@ def cpu_baseline(args, np):
     import oracle
     from tensor_all_reduce_amd import synth
 
-    def step(rows_s):
+    def gen(rows_s):
+        return [synth.normal(rows_s * HIDDEN, 4, 0, p) for p in range(P)]
+
+    def step(rows_s, xs=None, barrier=None):
         m = rows_s * HIDDEN
-        xs = [synth.normal(m, 4, 0, p) for p in range(P)]
+        xs = gen(rows_s) if xs is None else xs
+        if barrier is not None:
+            barrier.wait()
         t0 = time.perf_counter()
         oracle.reduce_seq(xs)
         oracle.reduce_2stage(xs)
@@ -716,10 +723,12 @@ def cpu_baseline(args, np):
         for w in rw:
             oracle.unpack(w, 4)
         oracle.reduce_ubatch(xs, rows_s, HIDDEN, 2, None, CHUNK_BYTES // 2, oracle.TWOSTAGE)
-        dt = time.perf_counter() - t0
+        t1 = time.perf_counter()
         b = 2 * m
         cred = (P + 1) * b + 2 * P * b + 3 * P * b + 4 * P * b + 3 * P * b + 2 * P * b
-        return dt, cred
+        if barrier is not None:
+            return t0, t1, cred
+        return t1 - t0, cred
 
     dt, _ = step(16)
     rows_s = int(min(ROWS, max(16, 16 * args.cpu_seconds / max(dt, 1e-3))))
@@ -727,10 +736,31 @@ def cpu_baseline(args, np):
     log(f"cpu oracle: calibration 16 rows took {dt:.2f} s; timing {rows_s} rows")
     dt, cred = step(rows_s)
     gbps = cred / dt / 1e9
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full step (all six rows) of the oracle on the first {rows_s} of 16384 rows "
-                      f"(P=8, hidden 8192, N(0,1)); {dt:.1f} s on one host core; credited bytes as the GPU step",
-            "seconds": round(dt, 2)}
+    res = {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"one full step (all six rows) of the oracle on the first {rows_s} of 16384 rows "
+                     f"(P=8, hidden 8192, N(0,1)); {dt:.1f} s on one host core; credited bytes as the GPU step",
+           "seconds": round(dt, 2)}
+    if args.no_cpu_all_cores:
+        return res
+    # the same oracle on all host cores (at most 16): the step's rows split
+    # over threads, each running the unchanged oracle on its own rows (the C
+    # calls release the interpreter lock)
+    import concurrent.futures as cf
+    import threading
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    rows_t = max(2, min(rows_s, ROWS // cores))
+    rows_t -= rows_t % 2
+    data = gen(rows_t)                     # every thread reduces the same values
+    barrier = threading.Barrier(cores)
+    with cf.ThreadPoolExecutor(cores) as ex:
+        parts = list(ex.map(lambda _: step(rows_t, data, barrier), range(cores)))
+    wall = max(t1 for _, t1, _ in parts) - min(t0 for t0, _, _ in parts)
+    cred_all = sum(c for _, _, c in parts)
+    res["all_cores"] = {"value": round(cred_all / wall / 1e9, 3), "unit": "GB/s", "cores": cores,
+                        "seconds": round(wall, 2),
+                        "sample": f"{cores} threads, each one full oracle step on {rows_t} rows of its own"}
+    log(f"cpu oracle on {cores} cores: {res['all_cores']['value']} GB/s")
+    return res
 
 
 if __name__ == "__main__":

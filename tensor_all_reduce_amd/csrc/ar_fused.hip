@@ -118,68 +118,79 @@ __global__ __launch_bounds__(kMaxBlock) void k_unpack(const uint64_t* w, void* x
 }
 
 // ----------------------------------------------------------------------------
-// Fused recursive doubling: one lane owns a 16-byte group (2 payload words,
-// 4 bf16 elements) of every rank, checks every rank's sequence numbers, then
+// Fused recursive doubling: one lane owns V 16-byte groups (2 payload words,
+// 4 bf16 elements each) of every rank, checks every rank's sequence numbers, then
 // runs all log2 P exchange steps in registers.  Step k combines rank r with
 // r XOR 2^k; after step k ranks r and r XOR 2^k hold the same value, so the
 // steps reduce to a balanced tree ((x0 x1)(x2 x3))((x4 x5)(x6 x7)) computed
 // once per element and stored to all P outputs.  ROUND_EACH: every internal
 // node is rounded to bf16, as the exchanged payload is bf16; otherwise the
 // partials stay binary32 and are rounded once.
-template <int P, bool ROUND_EACH, bool NTL, bool NTS>
+template <int P, int V, bool ROUND_EACH, bool NTL, bool NTS>
 __global__ __launch_bounds__(kMaxBlock) void k_rd_fused(WordIn in, WordOut out, size_t W, uint32_t seq0,
                                                        uint64_t* err) {
   constexpr uint32_t L = P == 2 ? 1 : (P == 4 ? 2 : 3);
   const uint32_t seq_out = seq0 + L;
   const size_t nvec = W >> 1;
-  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool act = v < nvec;
-  u32x4 a[P];
+  // a workgroup owns V * blockDim consecutive groups; all V * P loads are
+  // issued before any arithmetic
+  const size_t base = (size_t)blockIdx.x * V * blockDim.x + threadIdx.x;
+  u32x4 a[V][P];
   bool any = false;
-  bool bad[P][2];
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    a[p] = act ? ld4<NTL>(reinterpret_cast<const u32x4*>(in.p[p]) + v) : u32x4{0u, seq0, 0u, seq0};
-    bad[p][0] = a[p][1] != seq0;
-    bad[p][1] = a[p][3] != seq0;
-    any |= bad[p][0] | bad[p][1];
+  for (int u = 0; u < V; ++u) {
+    const size_t v = base + (size_t)u * blockDim.x;
+    const bool act = v < nvec;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      a[u][p] = act ? ld4<NTL>(reinterpret_cast<const u32x4*>(in.p[p]) + v) : u32x4{0u, seq0, 0u, seq0};
+      any |= (a[u][p][1] != seq0) | (a[u][p][3] != seq0);
+    }
   }
   WaveErr e;
   if (__ballot(any)) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      wave_note(e, bad[p][0], (uint64_t)p * W + 2 * (uint64_t)v);
-      wave_note(e, bad[p][1], (uint64_t)p * W + 2 * (uint64_t)v + 1);
+    for (int u = 0; u < V; ++u) {
+      const uint64_t v = base + (uint64_t)u * blockDim.x;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        wave_note(e, a[u][p][1] != seq0, (uint64_t)p * W + 2 * v);
+        wave_note(e, a[u][p][3] != seq0, (uint64_t)p * W + 2 * v + 1);
+      }
     }
   }
   wave_flush(e, err);
-  if (act) {
-    float f[P][4];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      f[p][0] = lo_f32(a[p][0]);
-      f[p][1] = hi_f32(a[p][0]);
-      f[p][2] = lo_f32(a[p][2]);
-      f[p][3] = hi_f32(a[p][2]);
-    }
+  for (int u = 0; u < V; ++u) {
+    const size_t v = base + (size_t)u * blockDim.x;
+    if (v < nvec) {
+      float f[P][4];
 #pragma unroll
-    for (int h = 1; h < P; h <<= 1) {
+      for (int p = 0; p < P; ++p) {
+        f[p][0] = lo_f32(a[u][p][0]);
+        f[p][1] = hi_f32(a[u][p][0]);
+        f[p][2] = lo_f32(a[u][p][2]);
+        f[p][3] = hi_f32(a[u][p][2]);
+      }
 #pragma unroll
-      for (int i = 0; i < P; i += 2 * h) {
+      for (int h = 1; h < P; h <<= 1) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float s = f[i][k] + f[i + h][k];
-          f[i][k] = ROUND_EACH ? round_bf16(s) : s;
+        for (int i = 0; i < P; i += 2 * h) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float s = f[i][k] + f[i + h][k];
+            f[i][k] = ROUND_EACH ? round_bf16(s) : s;
+          }
         }
       }
-    }
-    u32x4 o;
-    o[0] = pack_bf16x2(f[0][0], f[0][1]);
-    o[1] = seq_out;
-    o[2] = pack_bf16x2(f[0][2], f[0][3]);
-    o[3] = seq_out;
+      u32x4 o;
+      o[0] = pack_bf16x2(f[0][0], f[0][1]);
+      o[1] = seq_out;
+      o[2] = pack_bf16x2(f[0][2], f[0][3]);
+      o[3] = seq_out;
 #pragma unroll
-    for (int p = 0; p < P; ++p) st4<NTS>(reinterpret_cast<u32x4*>(out.p[p]) + v, o);
+      for (int p = 0; p < P; ++p) st4<NTS>(reinterpret_cast<u32x4*>(out.p[p]) + v, o);
+    }
   }
   // odd word count: the last word, one lane
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0 && (W & 1)) {
@@ -368,17 +379,25 @@ inline bool grid_fits(const Shape& sh, size_t items) {
   return cdiv(items, (size_t)sh.block) <= 0x7FFFFFFFull;
 }
 
+template <int P, int V, bool RE>
+hipError_t rd_fused_v(const Shape& sh, hipStream_t st, const WordIn& in, const WordOut& out, size_t W,
+                      uint32_t seq0, uint64_t* err) {
+  const size_t gs = cdiv(W >> 1, (size_t)V * sh.block);
+  const unsigned g = (unsigned)(gs ? gs : 1);
+  const dim3 b(sh.block);
+  if (sh.nt_loads && sh.nt_stores)
+    return launch_k(k_rd_fused<P, V, RE, true, true>, g, b, sh.lds, st, in, out, W, seq0, err);
+  if (sh.nt_loads) return launch_k(k_rd_fused<P, V, RE, true, false>, g, b, sh.lds, st, in, out, W, seq0, err);
+  if (sh.nt_stores) return launch_k(k_rd_fused<P, V, RE, false, true>, g, b, sh.lds, st, in, out, W, seq0, err);
+  return launch_k(k_rd_fused<P, V, RE, false, false>, g, b, sh.lds, st, in, out, W, seq0, err);
+}
+
 template <int P, bool RE>
 hipError_t rd_fused_p(const Launch& L, const WordIn& in, const WordOut& out, size_t W, uint32_t seq0,
                       uint64_t* err) {
   const Shape& sh = L.shape[kRD];
-  const unsigned g = flat_grid(sh, W >> 1);
-  const dim3 b(sh.block);
-  if (sh.nt_loads && sh.nt_stores)
-    return launch_k(k_rd_fused<P, RE, true, true>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
-  if (sh.nt_loads) return launch_k(k_rd_fused<P, RE, true, false>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
-  if (sh.nt_stores) return launch_k(k_rd_fused<P, RE, false, true>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
-  return launch_k(k_rd_fused<P, RE, false, false>, g, b, sh.lds, L.stream, in, out, W, seq0, err);
+  if (sh.vec == 2) return rd_fused_v<P, 2, RE>(sh, L.stream, in, out, W, seq0, err);
+  return rd_fused_v<P, 1, RE>(sh, L.stream, in, out, W, seq0, err);
 }
 
 }  // namespace
