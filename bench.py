@@ -231,6 +231,8 @@ def main():
         assert torch.equal(o, out1), "two-stage/ubatch output differs from one-shot"
     ms_per_step = gpu_ms / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    step_ms = sorted(ev[k][0].elapsed_time(ev[k][len(rows)]) for k in range(K))
+    pct = lambda a, q: a[min(len(a) - 1, int(q * len(a)))]
     log(f"{ms_per_step:.3f} ms/step (wall {1e3 * wall / K:.3f}), {value:.1f} GB/s")
 
     per_row = {}
@@ -260,6 +262,8 @@ def main():
                    "step_credited_bytes": step_bytes, "parallelism": "none (one GPU)"},
         "roofline": roofline,
         "rows": per_row,
+        "step_ms_spread": {"p10": round(pct(step_ms, 0.1), 4), "p50": round(pct(step_ms, 0.5), 4),
+                           "p90": round(pct(step_ms, 0.9), 4)},
     }
 
     if args.copy_calib:
@@ -278,6 +282,10 @@ def main():
         result.update(extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1))
         del ins, outs, words, rdo, ux, ubo, out1
         torch.cuda.empty_cache()
+        # the same rates against the attainable bandwidth measured in this run
+        for r in rows:
+            per_row[r]["frac_of_copy"] = round(per_row[r]["GBps"] / result["copy_GBps"], 4)
+        roofline["frac_of_copy"] = round(achieved / result["copy_GBps"], 4)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, np)
     print(json.dumps(result), flush=True)

@@ -4,6 +4,9 @@
            row, the rocprofv3 average over all dispatches and the average
            over the timed steps only (warmup steps dropped), next to the
            rocprofv3 kernel_stats line.
+  pmc      any counters from one or more --pmc runs of the bench step:
+           per row, the mean per dispatch of every counter collected, and
+           derived figures (bytes per VMEM instruction, L2 hit rate).
   decode   kernel-only durations of the decode-size calls that
            decode_trace.py issues, labelled by the plan it writes.
   traffic  HBM bytes per launch from two --pmc runs (FETCH_SIZE, then
@@ -18,6 +21,7 @@ step is that row's kernel whatever its template arguments.
 Usage:
   python -m tensor_all_reduce_amd.profsum stats DIR --warmup W --command "..."
   python -m tensor_all_reduce_amd.profsum decode DIR PLAN.json --command "..."
+  python -m tensor_all_reduce_amd.profsum pmc DIR [DIR ...] --command "..." [--command "..."]
   python -m tensor_all_reduce_amd.profsum traffic FETCH_DIR WRITE_DIR --calib-bytes B \
       --command-fetch "..." --command-write "..."
 """
@@ -152,6 +156,44 @@ def cmd_decode(a):
               f"{t[(len(t) * 9) // 10]:8.2f} {gb:9.1f}  {' + '.join(uniq)}")
 
 
+def cmd_pmc(a):
+    per = {}                                   # counter -> row -> [values]
+    for d in a.dirs:
+        f = one(os.path.join(d, "*counter_collection.csv"))
+        rows = list(csv.DictReader(open(f)))
+        for name in sorted({r["Counter_Name"] for r in rows}):
+            sub = [r for r in rows if r["Counter_Name"] == name]
+            lab, _ = label(sub, "Kernel_Name", "Dispatch_Id")
+            per[name] = {row: [] for row in ROWS}
+            for _, row, r in lab:
+                if row in per[name]:
+                    per[name][row].append(float(r["Counter_Value"]))
+    names = sorted(per)
+    print("# rocprofv3 --pmc counters of the bench step kernels (P=8, bf16 [16384 x 8192] per rank),")
+    print("# mean per dispatch over every dispatch of each run")
+    for c in a.command:
+        print(f"# command: {c}")
+    print("# row       " + "  ".join(f"{n:>18s}" for n in names))
+    for row in ROWS:
+        vals = [statistics.mean(per[n][row]) if per[n][row] else float("nan") for n in names]
+        print(f"{row:10s} " + "  ".join(f"{v:18.1f}" for v in vals))
+    print("#")
+    print("# derived, per dispatch: algorithmic bytes per vector-memory instruction (a 64-lane")
+    print("# wavefront moving 16 bytes per lane = 1024), waves launched, L2 (TCC) hit rate")
+    for row in ROWS:
+        m = {n: (statistics.mean(per[n][row]) if per[n][row] else None) for n in names}
+        out = [f"{row:10s}"]
+        rd, wr = m.get("SQ_INSTS_VMEM_RD"), m.get("SQ_INSTS_VMEM_WR")
+        if rd is not None and wr is not None and rd + wr > 0:
+            out.append(f"bytes/VMEM-instr {ALGO[row] / (rd + wr):8.1f}")
+        if m.get("SQ_WAVES") is not None:
+            out.append(f"waves {m['SQ_WAVES']:10.0f}")
+        hit, miss = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+        if hit is not None and miss is not None and hit + miss > 0:
+            out.append(f"L2 hit rate {hit / (hit + miss):.3f}")
+        print("  ".join(out))
+
+
 def counters(d):
     f = one(os.path.join(d, "*counter_collection.csv"))
     rows = list(csv.DictReader(open(f)))
@@ -194,6 +236,9 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--warmup", type=int, default=2)
     s.add_argument("--command", default="")
+    pm = sub.add_parser("pmc")
+    pm.add_argument("dirs", nargs="+")
+    pm.add_argument("--command", action="append", default=[])
     d = sub.add_parser("decode")
     d.add_argument("dir")
     d.add_argument("plan")
@@ -205,7 +250,7 @@ def main(argv=None):
     t.add_argument("--command-fetch", default="")
     t.add_argument("--command-write", default="")
     a = ap.parse_args(argv)
-    return {"stats": cmd_stats, "decode": cmd_decode, "traffic": cmd_traffic}[a.cmd](a)
+    return {"stats": cmd_stats, "decode": cmd_decode, "traffic": cmd_traffic, "pmc": cmd_pmc}[a.cmd](a)
 
 
 if __name__ == "__main__":
