@@ -148,11 +148,11 @@ struct EventPair {
     if (a) (void)hipEventDestroy(a);
     if (b) (void)hipEventDestroy(b);
   }
-  double us_between(hipStream_t s, int iters) {
+  // average microseconds per iteration between a and b, once b has completed
+  double us_between(int iters) {
     (void)hipEventSynchronize(b);
     float ms = 0.f;
     (void)hipEventElapsedTime(&ms, a, b);
-    (void)s;
     return 1000.0 * (double)ms / iters;
   }
 };
@@ -192,33 +192,30 @@ extern "C" {
 // Returns a negative status on error.
 double arb_stream_us(int which, const void* const* ins, void* const* outs, int P, size_t n,
                      void* scratch, int iters, void* stream) {
+  if (iters < 1) return AR_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t e0, e1;
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return AR_ERR_HIP;
+  EventPair ev;
+  if (!ev.ok) return AR_ERR_HIP;
   for (int i = 0; i < 20; ++i) {
     int rc = call(which, ins, outs, P, n, scratch, stream);
     if (rc) return rc;
   }
-  (void)hipEventRecord(e0, s);
+  (void)hipEventRecord(ev.a, s);
   for (int i = 0; i < iters; ++i) {
     int rc = call(which, ins, outs, P, n, scratch, stream);
     if (rc) return rc;
   }
-  (void)hipEventRecord(e1, s);
-  (void)hipEventSynchronize(e1);
-  float ms = 0.f;
-  (void)hipEventElapsedTime(&ms, e0, e1);
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  return 1000.0 * (double)ms / iters;
+  (void)hipEventRecord(ev.b, s);
+  return ev.us_between(iters);
 }
 
 // Single-call wall latency: C-ABI call -> hipStreamSynchronize return,
 // host steady clock; writes the median, 10th and 90th percentiles (us).
 int arb_wall_us(int which, const void* const* ins, void* const* outs, int P, size_t n, void* scratch,
                 int iters, void* stream, double* p50, double* p10, double* p90) {
+  if (iters < 1 || !p50 || !p10 || !p90) return AR_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  std::vector<double> t(iters > 0 ? iters : 1);
+  std::vector<double> t(iters);
   for (int i = 0; i < 20; ++i) {
     int rc = call(which, ins, outs, P, n, scratch, stream);
     if (rc) return rc;
@@ -271,7 +268,7 @@ double arb_stream_rot_us(int which, const void* const* ins, void* const* outs, i
     if (rc) return rc;
   }
   (void)hipEventRecord(ev.b, s);
-  return ev.us_between(s, iters);
+  return ev.us_between(iters);
 }
 
 // Average stream time, in microseconds, of `iters` back-to-back decode
@@ -295,7 +292,7 @@ double arb_decode_us(const void* const* x, void* const* y, uint64_t* const* w_in
     if (rc) return rc;
   }
   (void)hipEventRecord(ev.b, s);
-  return ev.us_between(s, iters);
+  return ev.us_between(iters);
 }
 
 // Read-only sweep of `bytes` (a multiple of 16, 16-byte aligned); out holds

@@ -66,6 +66,27 @@ def test_flags_set_and_counters_return_to_zero():
             check(o, ref, f"epoch {epoch}")
 
 
+def test_flags_with_the_one_shot_variant():
+    """The one-shot variant publishes the same flags; only outs[0] is written
+    (the other outputs keep their sentinel)."""
+    P, rows, hidden, chunk = 5, 40, 2048 + 8, 4096 + 32
+    n = rows * hidden
+    xs = synth.rank_buffers("logmag", P, n, 93)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    outs = [torch.full((n,), 0x2222, dtype=torch.int16, device=DEV) for _ in range(P)]
+    nchunks = tar.ubatch_chunk_count(rows, hidden, 3, [13, 14, 13], chunk)
+    done, tiles = u32(nchunks), u32(nchunks)
+    note("flags, one-shot variant")
+    tar.ar_reduce_ubatch_flags(ins, outs, rows, hidden, done, tiles, 11, 3, [13, 14, 13], chunk,
+                               tar.AR_VARIANT_ONESHOT)
+    torch.cuda.synchronize()
+    assert np.all(done.cpu().numpy() == 11) and not tiles.cpu().numpy().any()
+    check(outs[0], ref, "one-shot flagged")
+    for o in outs[1:]:
+        assert np.all(down16(o) == 0x2222)
+
+
 def test_consumer_follows_flags():
     """The producer (flagged reduce) is queued first on one stream, the
     consumer right after on another; the consumer copies each chunk of one
