@@ -77,11 +77,12 @@ def sha256_files(paths):
     return h.hexdigest()
 
 
-def load_traffic(row: str, sources):
+def load_traffic(row: str, sources, path: str | None = None):
     """HBM bytes per launch of a row's kernel from the committed rocprofv3
     counter summary (profiles/traffic_prefill_step.txt, "key: value" lines),
     if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_prefill_step.txt")
+    if path is None:
+        path = os.path.join(ROOT, "profiles", "traffic_prefill_step.txt")
     if not os.path.exists(path):
         return None
     rec = {}
