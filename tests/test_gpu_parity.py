@@ -423,6 +423,58 @@ def test_ubatch_full_size():
     torch.cuda.empty_cache()
 
 
+def test_payload_path_full_size():
+    """The bench's fused-payload rows at their size: P=8 [16384 x 8192] per
+    rank (512 MiB of payload per rank), seq0 = 1.  Pack every rank, fused and
+    staged recursive doubling, unpack every rank.  Sampled payload words and
+    unpacked elements vs the oracle; all P outputs identical; no sequence
+    mismatch; staged == fused."""
+    P, n = 8, 16384 * 8192
+    W = n // 2
+    note("payload full size: generate")
+    ins = [bits16(t) for t in synth.device_rank_buffers("normal", P, n, 9)]
+    words = [torch.empty(W, dtype=torch.int64, device=DEV) for _ in range(P)]
+    note("payload full size: pack")
+    for r in range(P):
+        tar.ar_pack_fused(ins[r], words[r], 1)
+    rdo = [torch.empty(W, dtype=torch.int64, device=DEV) for _ in range(P)]
+    err = new_err()
+    note("payload full size: rd fused")
+    tar.ar_rd_schedule(words, rdo, 1, err)
+    xo = [empty16(n) for _ in range(P)]
+    note("payload full size: unpack")
+    for r in range(P):
+        tar.ar_unpack_fused(rdo[r], xo[r], 4, err)
+    torch.cuda.synchronize()
+    assert err_host(err) == (0, 2 ** 64 - 1)
+    widx = np.unique(sample_indices(W, 1 << 15, 71))
+    pairs = (widx[:, None] * 2 + np.arange(2)[None, :]).reshape(-1)
+    xs = gather_ranks(ins, pairs)
+    tw = torch.from_numpy(widx.astype(np.int64)).to(DEV)
+    for r in (0, 5):
+        assert np.array_equal(down64(words[r][tw]), oracle.pack(xs[r], 1)), f"pack rank {r}"
+    want_w, want_err = oracle.rd([oracle.pack(x, 1) for x in xs], 1)
+    assert int(want_err[0]) == 0
+    assert np.array_equal(down64(rdo[3][tw]), want_w[3])
+    for o in rdo[1:]:
+        assert torch.equal(o, rdo[0])
+    want_x, _ = oracle.unpack(want_w[0], 4)
+    for r in (0, 7):
+        assert np.array_equal(gather(xo[r], pairs), want_x), f"unpack rank {r}"
+    del xo
+    mbox = torch.empty(tar.rd_mailbox_words(P, n), dtype=torch.int64, device=DEV)
+    rds = [torch.empty(W, dtype=torch.int64, device=DEV) for _ in range(P)]
+    err2 = new_err()
+    note("payload full size: rd staged")
+    tar.ar_rd_schedule(words, rds, 1, err2, mailbox=mbox, flags=tar.AR_RD_STAGED)
+    torch.cuda.synchronize()
+    assert err_host(err2) == (0, 2 ** 64 - 1)
+    for o in rds:
+        assert torch.equal(o, rdo[0])
+    del ins, words, rdo, rds, mbox
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ reordered variants (tolerance)
 
 def _f64(bits: np.ndarray) -> np.ndarray:
