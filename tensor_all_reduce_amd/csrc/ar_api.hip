@@ -48,8 +48,8 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {256, 1, 0, 0, 1, 0},   // waiting unpack: 1 persistent workgroup per CU
     {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few store waits and counter atomics per chunk
     {64, 2, 1, 1, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
-    {64, 1, 1, 1, 10, 0},   // fp8 reduce, P code streams -> 1 output
-    {128, 1, 0, 0, 3, 0},   // fp8 reduce, P code streams -> P outputs
+    {128, 1, 1, 1, 8, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)
+    {128, 1, 1, 1, 6, 0},   // fp8 reduce, P code streams -> P outputs
 };
 constexpr const char* kShapeEnv[ar::kKinds] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
