@@ -41,8 +41,8 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {64, 1, 1, 1, 6, 0},    // ubatch, 8 -> 8 on two streams
     {256, 1, 1, 1, 5, 0},   // staged reduce-scatter, 8 -> 1
     {64, 1, 1, 1, 3, 0},    // staged all-gather, 1 -> 8
-    {256, 1, 1, 0, 6, 0},   // pack, 1 -> 2
-    {128, 1, 0, 1, 12, 0},  // unpack, 2 -> 1
+    {64, 1, 1, 1, 0, 0},    // pack, 1 -> 2 (vec: 16-byte bf16 groups per lane; 1 = 8 bytes)
+    {64, 1, 1, 1, 0, 0},    // unpack, 2 -> 1
     {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
     {64, 1, 1, 1, 8, 0},    // staged recursive-doubling step, 8 -> 8
     {256, 1, 0, 0, 1, 0},   // waiting unpack: 1 persistent workgroup per CU

@@ -32,6 +32,18 @@ __device__ __forceinline__ void st4(u32x4* p, u32x4 v) {
   else *p = v;
 }
 
+template <bool NT>
+__device__ __forceinline__ uint64_t ld8(const uint64_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void st8(uint64_t* p, uint64_t v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // Device-coherent 16-byte store for data that a completion flag will cover.
 // The buffer store carries the SC1 cache policy (aux bit 4; bit 1 adds the
 // streaming NT hint): it is written through to the level every XCD's L2

@@ -45,7 +45,7 @@ KINDS = {
 
 def candidates(kind: str):
     vecs = (1, 2) if kind in ("oneshot", "2stage", "ubatch", "ubatch_flags", "quant_fp8", "reduce_fp8",
-                              "reduce_fp8_one", "rd") else (1,)
+                              "reduce_fp8_one", "rd", "pack", "unpack") else (1,)
     return list(itertools.product((64, 128, 256), vecs, (0, 1), (0, 1), WGS))
 
 
