@@ -45,7 +45,7 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {64, 1, 1, 1, 0, 0},    // unpack, 2 -> 1
     {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
     {64, 1, 1, 1, 8, 0},    // staged recursive-doubling step, 8 -> 8
-    {256, 1, 0, 0, 1, 0},   // waiting unpack: 1 persistent workgroup per CU
+    {256, 1, 0, 1, 2, 0},   // waiting unpack: 2 persistent workgroups (8 waves) per CU
     {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few store waits and counter atomics per chunk
     {64, 2, 1, 1, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
     {128, 1, 1, 1, 8, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)

@@ -308,11 +308,12 @@ __global__ __launch_bounds__(kMaxBlock) void k_rd_step(WordIn src, WordOut dst, 
 // read with a 64-bit agent-scope atomic load: the data and its sequence
 // number are one naturally aligned 8-byte word, so a load that returns the
 // expected sequence number returns that word's data with it (the producer's
-// stores write whole aligned words).  Persistent grid: a wavefront walks its
-// groups in steps of gridDim * blockDim (a multiple of 64, so every lane of
-// the wavefront runs the same trip count); `spins` is the wavefront's total
-// poll budget across all its groups, which bounds the kernel's run time even
-// when the producer never comes.
+// stores write whole aligned words).  Persistent grid: wavefront q of Q owns
+// the 256-word tiles q, q + Q, ...; its k-th load instruction reads words
+// tile + 64k + lane, so every load (512 bytes) and every data store (256
+// bytes) of a wavefront is one contiguous span.  `spins` is the wavefront's
+// total poll budget across all its tiles, which bounds the kernel's run time
+// even when the producer never comes.
 __device__ __forceinline__ uint64_t ld_word_agent(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -320,19 +321,21 @@ __device__ __forceinline__ uint64_t ld_word_agent(const uint64_t* p) {
 template <bool NTS>
 __global__ __launch_bounds__(kMaxBlock) void k_unpack_wait(const uint64_t* w, void* x, size_t n, uint32_t seq,
                                                           uint32_t max_spins, uint64_t* err) {
-  const size_t nvec = n >> 3;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  constexpr int K = 4;                          // words per lane per tile
+  const size_t W = n >> 1;
+  const size_t wave = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const size_t nwaves = (size_t)gridDim.x * blockDim.x / kWave;
+  const uint32_t lane = lane_id();
+  uint32_t* x32 = static_cast<uint32_t*>(x);
   uint32_t spins = 0;
   WaveErr e;
-  for (size_t base = (size_t)blockIdx.x * blockDim.x + (threadIdx.x & ~(kWave - 1)); base < nvec;
-       base += stride) {
-    const size_t v = base + lane_id();
-    const bool act = v < nvec;
-    uint64_t q[4];
+  for (size_t tile = wave * (K * kWave); tile < W; tile += nwaves * (K * kWave)) {
+    uint64_t q[K];
     bool ok = true;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      q[k] = act ? ld_word_agent(w + 4 * v + k) : ((uint64_t)seq << 32);
+    for (int k = 0; k < K; ++k) {
+      const size_t j = tile + (size_t)k * kWave + lane;
+      q[k] = j < W ? ld_word_agent(w + j) : ((uint64_t)seq << 32);
       ok = ok && (uint32_t)(q[k] >> 32) == seq;
     }
     while (__ballot(!ok) && spins < max_spins) {
@@ -341,42 +344,30 @@ __global__ __launch_bounds__(kMaxBlock) void k_unpack_wait(const uint64_t* w, vo
       if (!ok) {
         ok = true;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if ((uint32_t)(q[k] >> 32) != seq) q[k] = ld_word_agent(w + 4 * v + k);
+        for (int k = 0; k < K; ++k) {
+          const size_t j = tile + (size_t)k * kWave + lane;
+          if ((uint32_t)(q[k] >> 32) != seq) q[k] = ld_word_agent(w + j);
           ok = ok && (uint32_t)(q[k] >> 32) == seq;
         }
       }
     }
-    if (act) {
-      u32x4 d;
-      d[0] = (uint32_t)q[0]; d[1] = (uint32_t)q[1]; d[2] = (uint32_t)q[2]; d[3] = (uint32_t)q[3];
-      st4<NTS>(static_cast<u32x4*>(x) + v, d);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const size_t j = tile + (size_t)k * kWave + lane;
+      if (j < W) {
+        if constexpr (NTS) __builtin_nontemporal_store((uint32_t)q[k], x32 + j);
+        else x32[j] = (uint32_t)q[k];
+      }
     }
-    const bool b0 = (uint32_t)(q[0] >> 32) != seq, b1 = (uint32_t)(q[1] >> 32) != seq;
-    const bool b2 = (uint32_t)(q[2] >> 32) != seq, b3 = (uint32_t)(q[3] >> 32) != seq;
-    if (__ballot(b0 | b1 | b2 | b3)) {
-      const uint64_t j = 4 * (uint64_t)v;
-      wave_note(e, b0, j);
-      wave_note(e, b1, j + 1);
-      wave_note(e, b2, j + 2);
-      wave_note(e, b3, j + 3);
+    if (__ballot(!ok)) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const size_t j = tile + (size_t)k * kWave + lane;
+        wave_note(e, (uint32_t)(q[k] >> 32) != seq, (uint64_t)j);
+      }
     }
   }
   wave_flush(e, err);
-  // ragged end: one lane per remaining word, each with its own bounded wait
-  const size_t j = (nvec << 2) + threadIdx.x;
-  if (blockIdx.x == gridDim.x - 1 && j < (n >> 1)) {
-    uint64_t q = ld_word_agent(w + j);
-    for (uint32_t t = 0; (uint32_t)(q >> 32) != seq && t < max_spins; ++t) {
-      __builtin_amdgcn_s_sleep(1);
-      q = ld_word_agent(w + j);
-    }
-    static_cast<uint32_t*>(x)[j] = (uint32_t)q;
-    if ((uint32_t)(q >> 32) != seq) {
-      atomicAdd(reinterpret_cast<unsigned long long*>(err), 1ull);
-      atomicMin(reinterpret_cast<unsigned long long*>(err + 1), (unsigned long long)j);
-    }
-  }
 }
 
 __global__ void k_err_init(uint64_t* err) {
@@ -519,7 +510,8 @@ hipError_t launch_rd_staged(const Launch& L, const WordIn& in, const WordOut& ou
 hipError_t launch_unpack_wait(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,
                               uint32_t max_spins, uint64_t* d_err) {
   const Shape& sh = L.shape[kUnpackWait];
-  const size_t need = cdiv(n >> 3, (size_t)sh.block);
+  // one 256-word tile per wavefront is enough to cover the buffer
+  const size_t need = cdiv(cdiv(n >> 1, (size_t)4 * kWave), (size_t)sh.block / kWave);
   size_t g = (size_t)L.cus * (size_t)(sh.wg_per_cu > 0 ? sh.wg_per_cu : 1);
   if (g > need) g = need;
   if (g == 0) g = 1;
