@@ -9,7 +9,7 @@ credited per call) is written as JSON so that `profsum decode` can label
 the trace's library dispatches by their position.
 
 Usage:
-  python -m tensor_all_reduce_amd.decode_trace --plan gpurun_out/decode_plan.json --reps 200
+  python -m tensor_all_reduce_amd.decode_trace --plan out/decode_plan.json --reps 200
 """
 from __future__ import annotations
 
