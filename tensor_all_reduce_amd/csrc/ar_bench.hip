@@ -116,6 +116,41 @@ __global__ __launch_bounds__(256) void k_readsum(const u32x4* __restrict__ src, 
   if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Grid-stride variant of the fused 8 -> 8 reduce, for the A/B against the
+// library's flat in-order tiles: the same arithmetic (rank-order binary32
+// sums, one nearest-even rounding, non-temporal accesses), but a fixed grid
+// of `grid` workgroups walks the buffer in steps of grid * 256 groups.
+__device__ __forceinline__ uint32_t rne_hi_b(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  return __builtin_isnan(f) ? 0x7FC00000u : r;
+}
+
+struct In8 { const u32x4* p[8]; };
+struct Out8 { u32x4* p[8]; };
+
+__global__ __launch_bounds__(256) void k_gridstride88(In8 in, Out8 out, size_t nvec) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+    u32x4 a[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) a[p] = __builtin_nontemporal_load(in.p[p] + v);
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo = __uint_as_float(a[0][k] << 16), hi = __uint_as_float(a[0][k] & 0xFFFF0000u);
+#pragma unroll
+      for (int p = 1; p < 8; ++p) {
+        lo = lo + __uint_as_float(a[p][k] << 16);
+        hi = hi + __uint_as_float(a[p][k] & 0xFFFF0000u);
+      }
+      r[k] = (rne_hi_b(lo) >> 16) | (rne_hi_b(hi) & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int o = 0; o < 8; ++o) __builtin_nontemporal_store(r, out.p[o] + v);
+  }
+}
+
 // ALU-bound stand-in for the partner ubatch's compute: `iters` rounds of
 // dependent fused multiply-adds on four accumulators per lane; one float out.
 __global__ __launch_bounds__(256) void k_alu(float* out, int iters) {
@@ -293,6 +328,21 @@ double arb_decode_us(const void* const* x, void* const* y, uint64_t* const* w_in
   }
   (void)hipEventRecord(ev.b, s);
   return ev.us_between(iters);
+}
+
+// Grid-stride 8 -> 8 reduce (see k_gridstride88): n elements per buffer, a
+// multiple of 8; buffers 16-byte aligned; `grid` workgroups of 256 lanes.
+int arb_gridstride_reduce8(const void* const* ins, void* const* outs, size_t n, int grid, void* stream) {
+  if (!ins || !outs || (n & 7u) || grid <= 0) return AR_ERR_INVALID;
+  In8 in;
+  Out8 out;
+  for (int p = 0; p < 8; ++p) {
+    if (!ins[p] || !outs[p]) return AR_ERR_INVALID;
+    in.p[p] = static_cast<const u32x4*>(ins[p]);
+    out.p[p] = static_cast<u32x4*>(outs[p]);
+  }
+  hipLaunchKernelGGL(k_gridstride88, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), in, out, n / 8);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
 // Read-only sweep of `bytes` (a multiple of 16, 16-byte aligned); out holds

@@ -7,6 +7,9 @@
   pmc      any counters from one or more --pmc runs of the bench step:
            per row, the mean per dispatch of every counter collected, and
            derived figures (bytes per VMEM instruction, L2 hit rate).
+  kstats   the rocprofv3 --stats per-kernel table (calls, average, min,
+           max) of any run, and per kernel the mean FETCH_SIZE / WRITE_SIZE
+           of a matching --pmc run when one is given.
   decode   kernel-only durations of the decode-size calls that
            decode_trace.py issues, labelled by the plan it writes.
   traffic  HBM bytes per launch from two --pmc runs (FETCH_SIZE, then
@@ -156,6 +159,31 @@ def cmd_decode(a):
               f"{t[(len(t) * 9) // 10]:8.2f} {gb:9.1f}  {' + '.join(uniq)}")
 
 
+def _kname(full: str) -> str:
+    """Kernel name without its argument list, return type or anonymous namespace."""
+    return full.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def cmd_kstats(a):
+    stats = one(os.path.join(a.dir, "*kernel_stats.csv"))
+    cnt = {}
+    for d in a.pmc:
+        f = one(os.path.join(d, "*counter_collection.csv"))
+        for r in csv.DictReader(open(f)):
+            key = (_kname(r["Kernel_Name"]), r["Counter_Name"])
+            cnt.setdefault(key, []).append(float(r["Counter_Value"]))
+    print(f"# {a.title}")
+    for c in a.command:
+        print(f"# command: {c}")
+    print("# kernel                                              calls    avg_ms    min_ms    max_ms" +
+          ("   counters (mean per dispatch, KiB)" if cnt else ""))
+    for r in csv.DictReader(open(stats)):
+        name = _kname(r["Name"])
+        extra = "  ".join(f"{cn}={statistics.mean(v):.0f}" for (kn, cn), v in sorted(cnt.items()) if kn == name)
+        print(f"{name[:50]:50s} {int(r['Calls']):7d} {float(r['AverageNs']) * 1e-6:9.4f} "
+              f"{float(r['MinNs']) * 1e-6:9.4f} {float(r['MaxNs']) * 1e-6:9.4f}   {extra}")
+
+
 def cmd_pmc(a):
     per = {}                                   # counter -> row -> [values]
     for d in a.dirs:
@@ -236,6 +264,11 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--warmup", type=int, default=2)
     s.add_argument("--command", default="")
+    ks = sub.add_parser("kstats")
+    ks.add_argument("dir")
+    ks.add_argument("--pmc", action="append", default=[])
+    ks.add_argument("--title", default="rocprofv3 per-kernel statistics")
+    ks.add_argument("--command", action="append", default=[])
     pm = sub.add_parser("pmc")
     pm.add_argument("dirs", nargs="+")
     pm.add_argument("--command", action="append", default=[])
@@ -250,7 +283,8 @@ def main(argv=None):
     t.add_argument("--command-fetch", default="")
     t.add_argument("--command-write", default="")
     a = ap.parse_args(argv)
-    return {"stats": cmd_stats, "decode": cmd_decode, "traffic": cmd_traffic, "pmc": cmd_pmc}[a.cmd](a)
+    return {"stats": cmd_stats, "decode": cmd_decode, "traffic": cmd_traffic, "pmc": cmd_pmc,
+            "kstats": cmd_kstats}[a.cmd](a)
 
 
 if __name__ == "__main__":
