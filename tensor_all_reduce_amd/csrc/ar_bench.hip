@@ -151,6 +151,27 @@ __global__ __launch_bounds__(256) void k_gridstride88(In8 in, Out8 out, size_t n
   }
 }
 
+// Unpack with per-lane error atomics, for the A/B against the library's
+// wavefront-ballot validation: lane v unpacks payload words 2v and 2v+1
+// (one 16-byte load, one 8-byte store, as the library's unpack does) and
+// every lane whose word carries the wrong sequence number adds 1 to err[0]
+// and lowers err[1] itself.
+__global__ __launch_bounds__(256) void k_unpack_lane_atomics(const u32x4* w, uint64_t* x, size_t nl,
+                                                             uint32_t seq, unsigned long long* err) {
+  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= nl) return;
+  const u32x4 a = __builtin_nontemporal_load(w + v);
+  __builtin_nontemporal_store((uint64_t)a[0] | ((uint64_t)a[2] << 32), x + v);
+  if (a[1] != seq) {
+    atomicAdd(err, 1ull);
+    atomicMin(err + 1, (unsigned long long)(2 * v));
+  }
+  if (a[3] != seq) {
+    atomicAdd(err, 1ull);
+    atomicMin(err + 1, (unsigned long long)(2 * v + 1));
+  }
+}
+
 // ALU-bound stand-in for the partner ubatch's compute: `iters` rounds of
 // dependent fused multiply-adds on four accumulators per lane; one float out.
 __global__ __launch_bounds__(256) void k_alu(float* out, int iters) {
@@ -342,6 +363,20 @@ int arb_gridstride_reduce8(const void* const* ins, void* const* outs, size_t n, 
     out.p[p] = static_cast<u32x4*>(outs[p]);
   }
   hipLaunchKernelGGL(k_gridstride88, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), in, out, n / 8);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+// Per-lane-atomic unpack (see k_unpack_lane_atomics) of n elements (n a
+// multiple of 4), 256-lane workgroups.
+int arb_unpack_lane_atomics(const uint64_t* words, void* x, size_t n, uint32_t seq, uint64_t* d_err,
+                            void* stream) {
+  if (!words || !x || !d_err || (n & 3u)) return AR_ERR_INVALID;
+  const size_t nl = n / 4;
+  const size_t grid = (nl + 255) / 256;
+  if (grid == 0 || grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
+  hipLaunchKernelGGL(k_unpack_lane_atomics, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<const u32x4*>(words), static_cast<uint64_t*>(x), nl, seq,
+                     reinterpret_cast<unsigned long long*>(d_err));
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 

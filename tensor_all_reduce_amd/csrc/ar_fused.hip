@@ -43,10 +43,16 @@ __device__ __forceinline__ void wave_note(WaveErr& e, bool bad, uint64_t idx) {
   }
 }
 
+// One lane adds the wavefront's count and lowers the first index.  The
+// stored minimum only ever decreases, so a relaxed read that already shows a
+// value not above this wavefront's first index (a stale read can only show a
+// larger one) makes the atomic minimum unnecessary: when every word is bad,
+// this removes most of the atomics contending on err[1].
 __device__ __forceinline__ void wave_flush(const WaveErr& e, uint64_t* err) {
   if (e.count && lane_id() == 0) {
     atomicAdd(reinterpret_cast<unsigned long long*>(err), (unsigned long long)e.count);
-    atomicMin(reinterpret_cast<unsigned long long*>(err + 1), (unsigned long long)e.first);
+    if (e.first < __hip_atomic_load(err + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMin(reinterpret_cast<unsigned long long*>(err + 1), (unsigned long long)e.first);
   }
 }
 
