@@ -206,12 +206,19 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 
 /*
  * Launch-shape control (tuning; not a step of the reduction).  Every kernel
- * kind runs on a flat grid of `block`-lane workgroups (64, 128 or 256), each
- * lane handling `vec` 16-byte groups per buffer (1 or 2), with optional
- * non-temporal loads/stores, and at most `wg_per_cu` workgroups per compute
- * unit (0 = no cap; enforced by requesting unused LDS).  Defaults are the
- * fastest shapes measured on MI355X.  A new shape applies to launches made
- * after the call, process-wide; the call is thread-safe.
+ * kind runs on a flat grid of `block`-lane workgroups (64, 128 or 256) with
+ * optional non-temporal loads/stores and at most `wg_per_cu` workgroups per
+ * compute unit (0 = no cap; enforced by requesting unused LDS).  `vec` (1 or
+ * 2) sets how much each lane handles:
+ *   ONESHOT, 2STAGE, UBATCH, UBATCH_FLAGS, RD, QUANT_FP8: vec 16-byte groups
+ *     per buffer, each a contiguous span across the wavefront;
+ *   PACK, UNPACK: 1 -> 8 bytes of bf16 (one 16-byte payload access) per
+ *     lane, 2 -> 16 bytes of bf16 (two adjacent payload accesses);
+ *   REDUCE_FP8, REDUCE_FP8_ALL: 1 -> 8 elements (one 16-byte store per
+ *     output) per lane, 2 -> 16 elements;
+ *   RS, AG, RDSTEP, UNPACK_WAIT: ignored.
+ * Defaults are the fastest shapes measured on MI355X.  A new shape applies
+ * to launches made after the call, process-wide; the call is thread-safe.
  * Returns AR_ERR_INVALID for an unknown kind or out-of-range field.
  */
 #define AR_KERNEL_ONESHOT  0   /* ar_reduce_oneshot                         */
