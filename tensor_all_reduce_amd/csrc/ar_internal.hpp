@@ -20,7 +20,8 @@ namespace ar {
 // the 8 -> 8 patterns.
 struct Shape {
   int block;      // 64, 128 or 256 lanes
-  int vec;        // 16-byte groups per lane per buffer: 1 or 2
+  int vec;        // 1 or 2: work per lane (16-byte groups per buffer for the
+                  // reduces; the lane width for pack, unpack and the fp8 reduce)
   int nt_loads;   // 1: non-temporal loads of streamed inputs
   int nt_stores;  // 1: non-temporal stores of outputs
   int wg_per_cu;  // 0: no cap
