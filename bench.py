@@ -265,6 +265,7 @@ def main():
         "rows": per_row,
         "step_ms_spread": {"p10": round(pct(step_ms, 0.1), 4), "p50": round(pct(step_ms, 0.5), 4),
                            "p90": round(pct(step_ms, 0.9), 4)},
+        "kernel_sources_sha256": sha256_files(KERNEL_SOURCES),
     }
 
     if args.copy_calib:
