@@ -605,6 +605,28 @@ def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
     t_c = timed(lambda: compute(iters))
     t_both = timed(lambda: (reduce(), compute(iters)))
     ov = (t_r + t_c - t_both) / min(t_r, t_c)
+    # the partner ubatch's compute as a real bf16 GEMM (MFMA-bound; plain 2-D
+    # product with contiguous operands) sized to take about as long as the reduce
+    gdim = 4096
+    ga = torch.randn(gdim, gdim, device=dev, dtype=torch.bfloat16)
+    gb = torch.randn(gdim, gdim, device=dev, dtype=torch.bfloat16)
+
+    gc = torch.empty(gdim, gdim, device=dev, dtype=torch.bfloat16)
+
+    def gemm(reps):
+        with torch.cuda.stream(s1):
+            for _ in range(reps):
+                torch.mm(ga, gb, out=gc)
+
+    t_g = timed(lambda: gemm(1))
+    gemm_flop = 2 * gdim ** 3
+    reps_g = max(1, round(t_r / t_g))
+    t_g = timed(lambda: gemm(reps_g))
+    t_gboth = timed(lambda: (reduce(), gemm(reps_g)))
+    ov_g = (t_r + t_g - t_gboth) / min(t_r, t_g)
+    log(f"overlap with a bf16 GEMM: reduce {t_r:.3f} ms, {reps_g} x GEMM {gdim}^3 {t_g:.3f} ms, "
+        f"both {t_gboth:.3f} ms -> {ov_g:.2f}")
+    del ga, gb, gc
     t_rf = timed(lambda: reduce(True))
     t_cons = timed(lambda: consume())           # flags already set: the consumer alone
     t_pipe = timed(lambda: (reduce(True), consume()))
@@ -625,6 +647,10 @@ def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
                             "both_ms": round(t_both, 4), "overlap_fraction": round(ov, 3),
                             "reduce": "two-stage, one ubatch of [8192 x 8192] x 8 ranks, 1 MiB chunks",
                             "compute": f"ALU stand-in, {alu_grid} x 256 lanes, {iters} FMA rounds"},
+            "tbo_overlap_gemm": {"reduce_ms": round(t_r, 4), "gemm_ms": round(t_g, 4),
+                                 "both_ms": round(t_gboth, 4), "overlap_fraction": round(ov_g, 3),
+                                 "gemm": f"{reps_g} x bf16 [{gdim} x {gdim}] x [{gdim} x {gdim}] (torch.mm)",
+                                 "gemm_TFLOPs": round(reps_g * gemm_flop / (t_g * 1e-3) / 1e12, 1)},
             "chunk_pipeline": {"flagged_reduce_ms": round(t_rf, 4), "chunks": nchunks,
                                "copy_consumer": {"alone_ms": round(t_cons, 4),
                                                  "serial_ms": round(t_rf + t_cons, 4),
