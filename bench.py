@@ -128,6 +128,9 @@ def main():
                                  ctypes.POINTER(ctypes.c_double)]
     blib.arb_copy.restype = ctypes.c_int
     blib.arb_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    blib.arb_copy_multi.restype = ctypes.c_int
+    blib.arb_copy_multi.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_int, vp]
     blib.arb_alu.restype = ctypes.c_int
     blib.arb_alu.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
     blib.arb_stream_rot_us.restype = ctypes.c_double
@@ -287,7 +290,10 @@ def main():
         # the same rates against the attainable bandwidth measured in this run
         for r in rows:
             per_row[r]["frac_of_copy"] = round(per_row[r]["GBps"] / result["copy_GBps"], 4)
+        for r in ("2stage", "rd", "ubatch"):       # the rows with the 8 -> 8 access pattern
+            per_row[r]["frac_of_8to8_copy"] = round(per_row[r]["GBps"] / result["copy_8to8_GBps"], 4)
         roofline["frac_of_copy"] = round(achieved / result["copy_GBps"], 4)
+        roofline["frac_of_8to8_copy"] = round(achieved / result["copy_8to8_GBps"], 4)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, np)
     print(json.dumps(result), flush=True)
@@ -336,6 +342,26 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
         gbps = 2 * cb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         best = max(best, gbps)
     res["copy_GBps"] = round(best, 1)
+    # attainable bandwidth of the 8 -> 8 pattern itself: eight 256 MiB buffers
+    # copied side by side into eight others (16 concurrent streams, no
+    # arithmetic), best over groups per lane and the workgroups-per-CU cap
+    best8, shape8 = 0.0, None
+    for vec in (1, 2):
+        for wg in (0, 2, 3, 4, 5, 6, 8):
+            for _ in range(2):
+                if blib.arb_copy_multi(parr(ins), parr(outs), P, 2 * n, vec, wg, sh) != 0:
+                    raise RuntimeError("arb_copy_multi failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main_s)
+            for _ in range(8):
+                blib.arb_copy_multi(parr(ins), parr(outs), P, 2 * n, vec, wg, sh)
+            e1.record(main_s)
+            torch.cuda.synchronize()
+            gbps = 2 * P * 2 * n * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if gbps > best8:
+                best8, shape8 = gbps, {"vec": vec, "wg_per_cu": wg}
+    res["copy_8to8_GBps"] = round(best8, 1)
+    res["copy_8to8_shape"] = shape8
     # attainable read bandwidth: read-only sweep of the same 2 GiB
     sink = torch.empty(cb // 16384 + 1, dtype=torch.int32, device=dev)
     for _ in range(3):
@@ -349,7 +375,7 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     torch.cuda.synchronize()
     res["read_GBps"] = round(cb * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del src, dst, sink
-    log(f"copy bandwidth {best:.0f} GB/s, read-only {res['read_GBps']:.0f} GB/s")
+    log(f"copy bandwidth {best:.0f} GB/s, 8 -> 8 copy {best8:.0f} GB/s, read-only {res['read_GBps']:.0f} GB/s")
 
     # latency at decode sizes: P = 2 at one token ([1 x 8192], 16 KiB), then
     # P = 8 at 128 KiB .. 2 MiB per buffer

@@ -22,6 +22,39 @@ __global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ src, u32
   if (v < nvec) __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
 }
 
+// N buffers copied side by side: out[j] = in[j] for j < N, the same access
+// pattern as an N -> N reduce (N read streams and N write streams at the same
+// offsets) with no arithmetic.  64-lane workgroups; each lane moves V groups
+// of 16 bytes per buffer, strided by the workgroup so that each wavefront
+// instruction covers one contiguous 1 KiB span.  The attainable bandwidth of
+// the pattern, as the plain copy is that of a single stream.
+struct MultiPtrs {
+  const u32x4* in[8];
+  u32x4* out[8];
+};
+
+template <int N, int V>
+__global__ __launch_bounds__(64) void k_copy_multi(MultiPtrs m, size_t nvec) {
+  const size_t b0 = (size_t)blockIdx.x * 64 * V + threadIdx.x;
+  u32x4 a[V][N];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const size_t v = b0 + (size_t)u * 64;
+    if (v < nvec) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) a[u][j] = __builtin_nontemporal_load(m.in[j] + v);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const size_t v = b0 + (size_t)u * 64;
+    if (v < nvec) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) __builtin_nontemporal_store(a[u][j], m.out[j] + v);
+    }
+  }
+}
+
 // Consumer of a flagged chunked reduce.  Persistent grid (no LDS request,
 // at most two workgroups per CU, so the producer's workgroups always fit
 // beside it: a waiting grid that filled every wave slot would keep them
@@ -402,6 +435,49 @@ int arb_copy(const void* src, void* dst, size_t bytes, int block, void* stream) 
   if (grid == 0 || grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
   hipLaunchKernelGGL(k_copy, dim3((unsigned)grid), dim3(block), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), nvec);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+// N -> N side-by-side copy (N in {1, 2, 4, 8}) of `bytes` per buffer (a
+// multiple of 16; 16-byte aligned buffers), V in {1, 2} groups per lane,
+// at most wg_per_cu workgroups per CU through a dynamic LDS request (0: no
+// cap).  Buffers must not overlap one another.
+int arb_copy_multi(const void* const* ins, void* const* outs, int N, size_t bytes, int vec, int wg_per_cu,
+                   void* stream) {
+  if (!ins || !outs || (N != 1 && N != 2 && N != 4 && N != 8) || (vec != 1 && vec != 2) ||
+      (bytes & 15u) || bytes == 0 || wg_per_cu < 0)
+    return AR_ERR_INVALID;
+  MultiPtrs m{};
+  for (int j = 0; j < N; ++j) {
+    if (!ins[j] || !outs[j]) return AR_ERR_INVALID;
+    m.in[j] = static_cast<const u32x4*>(ins[j]);
+    m.out[j] = static_cast<u32x4*>(outs[j]);
+  }
+  unsigned lds = 0;
+  if (wg_per_cu > 0) {
+    int dev = 0, per_cu = 0, per_block = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return AR_ERR_HIP;
+    lds = ((unsigned)per_cu / (unsigned)wg_per_cu) & ~255u;
+    if (lds > (unsigned)per_block) lds = (unsigned)per_block;
+  }
+  const size_t nvec = bytes / 16;
+  const size_t grid = (nvec + 64 * (size_t)vec - 1) / (64 * (size_t)vec);
+  if (grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 g((unsigned)grid), b(64);
+#define ARB_COPY_MULTI(NN)                                                                 \
+  if (N == NN) {                                                                           \
+    if (vec == 2) hipLaunchKernelGGL((k_copy_multi<NN, 2>), g, b, lds, st, m, nvec);       \
+    else hipLaunchKernelGGL((k_copy_multi<NN, 1>), g, b, lds, st, m, nvec);                \
+  }
+  ARB_COPY_MULTI(1)
+  ARB_COPY_MULTI(2)
+  ARB_COPY_MULTI(4)
+  ARB_COPY_MULTI(8)
+#undef ARB_COPY_MULTI
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
