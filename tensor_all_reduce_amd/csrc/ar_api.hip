@@ -134,9 +134,12 @@ struct Span {
   uintptr_t lo, hi;  // [lo, hi)
 };
 
+// A range that would run past the top of the address space (an impossible
+// buffer, but a wrapped end would hide an overlap) ends at the top.
 inline Span span_of(const void* p, size_t bytes) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  return Span{a, a + bytes};
+  const uintptr_t room = ~(uintptr_t)0 - a;
+  return Span{a, bytes > room ? ~(uintptr_t)0 : a + bytes};
 }
 
 inline bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
@@ -369,7 +372,11 @@ int ar_rd_schedule(const uint64_t* const* in_words, uint64_t* const* out_words, 
   if (staged && steps > 1) {
     if (!mailbox) return AR_ERR_INVALID;
     if (!aligned16(mailbox)) return AR_ERR_ALIGN;
-    const size_t words = (size_t)P * (size_t)(steps - 1) * ar::rd_mailbox_stride(n);
+    const size_t stride = ar::rd_mailbox_stride(n);
+    if (mul_overflows((size_t)P * (size_t)(steps - 1), stride) ||
+        mul_overflows((size_t)P * (size_t)(steps - 1) * stride, 8))
+      return AR_ERR_INVALID;
+    const size_t words = (size_t)P * (size_t)(steps - 1) * stride;
     const Span sm = span_of(mailbox, words * 8);
     if ((rc = check_disjoint(sm, si, P)) || (rc = check_disjoint(sm, so, P)) ||
         (rc = check_disjoint(sm, &se, 1)))

@@ -146,6 +146,16 @@ def test_rd_validation():
     assert L.ar_rd_schedule(ins, ins, 4, 0, 0, None, 0, C, None) == tar.AR_OK   # in place
 
 
+def test_ranges_near_top_of_address_space():
+    """A range whose end would wrap past 2^64 still overlaps what lies above
+    its start (the end saturates), so the alias check cannot be bypassed."""
+    L = tar.lib()
+    top = 2 ** 64 - 0x10000
+    n = 2 ** 61                                   # 2n bytes run past the top
+    assert L.ar_reduce_oneshot(arr(top, B), 2, top + 0x8000, n, None) == tar.AR_ERR_ALIAS
+    assert L.ar_pack_fused(top, top + 0x8000, n, 1, None) == tar.AR_ERR_ALIAS
+
+
 def test_ubatch_validation():
     L = tar.lib()
     ins = arr(A, B)
