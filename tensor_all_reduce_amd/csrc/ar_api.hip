@@ -55,11 +55,15 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {64, 2, 1, 1, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
     {128, 1, 1, 1, 8, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)
     {128, 1, 1, 1, 6, 0},   // fp8 reduce, P code streams -> P outputs
+    {128, 1, 0, 1, 0, 0},   // one-shot, n <= AR_SMALL_ELEMS: uncapped, plain loads
+    {128, 1, 0, 1, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
+    {64, 1, 0, 1, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
 };
 constexpr const char* kShapeEnv[ar::kKinds] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
     "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT",
-    "AR_SHAPE_UBATCH_FLAGS", "AR_SHAPE_QUANT_FP8", "AR_SHAPE_REDUCE_FP8", "AR_SHAPE_REDUCE_FP8_ALL"};
+    "AR_SHAPE_UBATCH_FLAGS", "AR_SHAPE_QUANT_FP8", "AR_SHAPE_REDUCE_FP8", "AR_SHAPE_REDUCE_FP8_ALL",
+    "AR_SHAPE_ONESHOT_SMALL", "AR_SHAPE_2STAGE_SMALL", "AR_SHAPE_RD_SMALL"};
 
 std::mutex g_mu;
 DevInfo g_dev[kMaxDevices];

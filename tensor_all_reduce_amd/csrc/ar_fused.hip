@@ -413,7 +413,7 @@ hipError_t rd_fused_v(const Shape& sh, hipStream_t st, const WordIn& in, const W
 template <int P, bool RE>
 hipError_t rd_fused_p(const Launch& L, const WordIn& in, const WordOut& out, size_t W, uint32_t seq0,
                       uint64_t* err) {
-  const Shape& sh = L.shape[kRD];
+  const Shape& sh = shape_for(L, kRD, kRDSmall, 2 * W);
   if (sh.vec == 2) return rd_fused_v<P, 2, RE>(sh, L.stream, in, out, W, seq0, err);
   return rd_fused_v<P, 1, RE>(sh, L.stream, in, out, W, seq0, err);
 }
@@ -463,7 +463,7 @@ hipError_t launch_unpack(const Launch& L, const uint64_t* w, void* x, size_t n, 
 hipError_t launch_rd_fused(const Launch& L, const WordIn& in, const WordOut& out, int P, size_t n,
                            uint32_t seq0, int fp32_carry, uint64_t* d_err) {
   const size_t W = n >> 1;
-  if (!grid_fits(L.shape[kRD], W >> 1)) return hipErrorInvalidConfiguration;
+  if (!grid_fits(shape_for(L, kRD, kRDSmall, n), W >> 1)) return hipErrorInvalidConfiguration;
   if (fp32_carry) {
     switch (P) {
       case 2: return rd_fused_p<2, false>(L, in, out, W, seq0, d_err);

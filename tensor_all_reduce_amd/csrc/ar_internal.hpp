@@ -43,6 +43,9 @@ enum Kind {
   kQuantFp8,     // bf16 -> fp8 codes + block scales, P buffers in one launch
   kReduceFp8,    // P fp8 contributions -> 1 bf16 output
   kReduceFp8All, // P fp8 contributions -> P bf16 outputs
+  kOneshotSmall, // kOneshot for n <= AR_SMALL_ELEMS
+  k2StageSmall,  // k2Stage for n <= AR_SMALL_ELEMS
+  kRDSmall,      // kRD for n <= AR_SMALL_ELEMS
   kKinds
 };
 
@@ -53,6 +56,12 @@ struct Launch {
   Shape shape[kKinds];
   hipStream_t stream;
 };
+
+// The shape of a whole-buffer call over n elements per rank: a message of at
+// most AR_SMALL_ELEMS elements takes its small-message kind.
+inline const Shape& shape_for(const Launch& L, Kind large, Kind small, size_t n) {
+  return n <= (size_t)AR_SMALL_ELEMS ? L.shape[small] : L.shape[large];
+}
 
 // Pointer bundles passed to kernels by value (kernel arguments), so no
 // device-side pointer table and no host->device copy is needed per call.

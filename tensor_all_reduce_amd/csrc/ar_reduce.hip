@@ -242,12 +242,12 @@ hipError_t staged_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_
 hipError_t launch_oneshot(const Launch& L, const InPtrs& in, int P, void* out, size_t n) {
   OutPtrs o{};
   o.p[0] = out;
-  AR_DISPATCH_P(P, (range_p<PP, 1>(L.shape[kOneshot], L.stream, in, o, 0, n, n)))
+  AR_DISPATCH_P(P, (range_p<PP, 1>(shape_for(L, kOneshot, kOneshotSmall, n), L.stream, in, o, 0, n, n)))
 }
 
 hipError_t launch_2stage_fused(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                                size_t n) {
-  AR_DISPATCH_P(P, (range_p<PP, PP>(L.shape[k2Stage], L.stream, in, out, 0, n, n)))
+  AR_DISPATCH_P(P, (range_p<PP, PP>(shape_for(L, k2Stage, k2StageSmall, n), L.stream, in, out, 0, n, n)))
 }
 
 hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,

@@ -11,13 +11,20 @@ shuffled order each round and the median over rounds is reported, so slow
 drift of the device affects all candidates alike.  GB/s counts each input
 read once and each output written once.
 
-With --decode, the one-shot and fused two-stage kernels are instead timed at
-the decode sizes (P = 8, [T x 8192] for T = 8, 32, 128: 128 KiB to 2 MiB per
-buffer) as per-call stream time over 2000 back-to-back calls from the native
-timing loop in libarbench.so, so no Python runs between calls.
+With --decode, the small-message kinds (one-shot, fused two-stage and fused
+recursive doubling for n <= AR_SMALL_ELEMS) are instead timed at the decode
+sizes (P = 8, [T x 8192] for T = 8, 32, 128: 128 KiB to 2 MiB per buffer) as
+per-call stream time over back-to-back calls from the native timing loops in
+libarbench.so, so no Python runs between calls.
+
+With --crossover, the current large-message and small-message default shapes
+of those three kernels are both timed at sizes from 128 KiB to 64 MiB per
+buffer, hot (one buffer set, repeated) and cold (rotating over >= 4 GiB; the
+one-shot and two-stage only), the evidence for the AR_SMALL_ELEMS threshold.
 
 Usage: python -m tensor_all_reduce_amd.tune [--kinds 2stage,rd] [--rounds 3] [--reps 4]
        python -m tensor_all_reduce_amd.tune --decode
+       python -m tensor_all_reduce_amd.tune --crossover
 """
 from __future__ import annotations
 
@@ -41,6 +48,8 @@ KINDS = {
     "ubatch_flags": tar.AR_KERNEL_UBATCH_FLAGS, "quant_fp8": tar.AR_KERNEL_QUANT_FP8,
     "reduce_fp8": tar.AR_KERNEL_REDUCE_FP8_ALL, "reduce_fp8_one": tar.AR_KERNEL_REDUCE_FP8,
 }
+# The prefill sweep times the large-message kinds: at [16384 x 8192] per rank
+# the one-shot, two-stage and RD calls use them, not the ..._SMALL kinds.
 
 
 def candidates(kind: str):
@@ -56,9 +65,13 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=4)
     ap.add_argument("--top", type=int, default=8)
     ap.add_argument("--decode", action="store_true", help="tune the decode-size latency instead")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time the large- and small-message default shapes across sizes")
     args = ap.parse_args(argv)
     if args.decode:
         return decode(args)
+    if args.crossover:
+        return crossover(args)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -172,49 +185,144 @@ def main(argv=None):
     return 0
 
 
-def decode(args):
+def _bench_lib():
     import ctypes
     import os
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     blib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarbench.so"))
     vp = ctypes.c_void_p
+    pp = ctypes.POINTER(vp)
     blib.arb_stream_us.restype = ctypes.c_double
-    blib.arb_stream_us.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
-                                   ctypes.c_size_t, vp, ctypes.c_int, vp]
+    blib.arb_stream_us.argtypes = [ctypes.c_int, pp, pp, ctypes.c_int, ctypes.c_size_t, vp, ctypes.c_int, vp]
+    blib.arb_stream_rot_us.restype = ctypes.c_double
+    blib.arb_stream_rot_us.argtypes = [ctypes.c_int, pp, pp, ctypes.c_int, ctypes.c_size_t, ctypes.c_size_t,
+                                       ctypes.c_int, ctypes.c_int, vp]
+    blib.arb_decode_us.restype = ctypes.c_double
+    blib.arb_decode_us.argtypes = [pp, pp, pp, pp, ctypes.c_int, ctypes.c_size_t, vp, ctypes.c_int, vp,
+                                   ctypes.c_int, ctypes.c_int, vp]
+    return blib, vp
+
+
+def _check_us(us, what):
+    if us < 0:
+        raise RuntimeError(f"{what} failed: {us}")
+    return us
+
+
+def decode(args):
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    blib, vp = _bench_lib()
     sh = torch.cuda.current_stream().cuda_stream
     rng = random.Random(11)
+    mmax = 128 * HIDDEN
+    ins = [t.view(torch.int16) for t in synth.device_rank_buffers("normal", P, mmax, 2, dev)]
+    outs = [torch.empty(mmax, dtype=torch.int16, device=dev) for _ in range(P)]
+    words = [torch.empty(mmax // 2, dtype=torch.int64, device=dev) for _ in range(P)]
+    rdo = [torch.empty(mmax // 2, dtype=torch.int64, device=dev) for _ in range(P)]
+    err = torch.empty(2, dtype=torch.int64, device=dev)
+    for r in range(P):
+        tar.ar_pack_fused(ins[r], words[r], 1)
+    tar.ar_err_init(err)
+    ia = (vp * P)(*[t.data_ptr() for t in ins])
+    oa = (vp * P)(*[t.data_ptr() for t in outs])
+    wa = (vp * P)(*[t.data_ptr() for t in words])
+    ra = (vp * P)(*[t.data_ptr() for t in rdo])
+    cands = list(itertools.product((64, 128, 256), (1, 2), (0, 1), (0, 1), (0, 4, 8)))
     for T in (8, 32, 128):
         m = T * HIDDEN
-        ins = [t.view(torch.int16) for t in synth.device_rank_buffers("normal", P, m, 2, dev)]
-        outs = [torch.empty(m, dtype=torch.int16, device=dev) for _ in range(P)]
-        ia = (vp * P)(*[t.data_ptr() for t in ins])
-        oa = (vp * P)(*[t.data_ptr() for t in outs])
-        for name, which, k in (("oneshot", 0, tar.AR_KERNEL_ONESHOT), ("2stage", 1, tar.AR_KERNEL_2STAGE)):
+        for name, k, fn in (
+                ("oneshot", tar.AR_KERNEL_ONESHOT_SMALL,
+                 lambda: blib.arb_stream_us(0, ia, oa, P, m, None, 2000, sh)),
+                ("2stage", tar.AR_KERNEL_2STAGE_SMALL,
+                 lambda: blib.arb_stream_us(1, ia, oa, P, m, None, 2000, sh)),
+                ("rd", tar.AR_KERNEL_RD_SMALL,
+                 lambda: blib.arb_decode_us(None, None, wa, ra, P, m, None, 0, err.data_ptr(), 0, 1000, sh))):
             default = tar.ar_get_launch_shape(k)
-            cands = list(itertools.product((64, 128, 256), (1, 2), (0, 1), (0, 1), (0,)))
-            if default not in cands:
-                cands.append(default)
-            times = {c: [] for c in cands}
+            cs = cands + ([default] if default not in cands else [])
+            times = {c: [] for c in cs}
             for _ in range(args.rounds):
-                order = cands[:]
+                order = cs[:]
                 rng.shuffle(order)
                 for c in order:
                     tar.ar_set_launch_shape(k, *c)
-                    us = blib.arb_stream_us(which, ia, oa, P, m, None, 2000, sh)
-                    if us < 0:
-                        raise RuntimeError(f"arb_stream_us failed: {us}")
-                    times[c].append(us)
+                    times[c].append(_check_us(fn(), name))
             tar.ar_set_launch_shape(k, *default)
             med = {c: statistics.median(v) for c, v in times.items()}
-            ranked = sorted(cands, key=lambda c: med[c])
-            print(f"== {name} T={T} ({2 * m // 1024} KiB per buffer): per-call stream time")
+            ranked = sorted(cs, key=lambda c: med[c])
+            what = f"{4 * m // 1024} KiB of payload per rank" if name == "rd" else f"{2 * m // 1024} KiB per buffer"
+            print(f"== {name} (small-message kind) T={T} ({what}): per-call stream time")
             print("   rank  block vec ntl nts wg/cu      us")
             for i, c in enumerate(ranked):
                 if i < args.top or c == default:
                     tag = "  <- default" if c == default else ""
                     print(f"   {i + 1:4d}  {c[0]:5d} {c[1]:3d} {c[2]:3d} {c[3]:3d} {c[4]:5d} {med[c]:7.2f}{tag}")
             sys.stdout.flush()
+    torch.cuda.synchronize()
+    if err.cpu().tolist()[0]:
+        raise RuntimeError("recursive doubling saw bad sequence numbers")
+    return 0
+
+
+def crossover(args):
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    blib, vp = _bench_lib()
+    sh = torch.cuda.current_stream().cuda_stream
+    nbuf = 128 << 20                                  # elements per buffer (256 MiB)
+    ins = [t.view(torch.int16) for t in synth.device_rank_buffers("normal", P, nbuf, 6, dev)]
+    outs = [torch.empty(nbuf, dtype=torch.int16, device=dev) for _ in range(P)]
+    ia = (vp * P)(*[t.data_ptr() for t in ins])
+    oa = (vp * P)(*[t.data_ptr() for t in outs])
+    pairs = {"oneshot": (tar.AR_KERNEL_ONESHOT, tar.AR_KERNEL_ONESHOT_SMALL, 0),
+             "2stage": (tar.AR_KERNEL_2STAGE, tar.AR_KERNEL_2STAGE_SMALL, 1),
+             "rd": (tar.AR_KERNEL_RD, tar.AR_KERNEL_RD_SMALL, None)}
+    sizes = [128 << 10, 512 << 10, 2 << 20, 4 << 20, 8 << 20, 16 << 20, 32 << 20, 64 << 20]
+    res = {}
+    words = rdo = None
+    err = torch.empty(2, dtype=torch.int64, device=dev)
+    for name, (kl, ks, which) in pairs.items():
+        shapes = {"large": tar.ar_get_launch_shape(kl), "small": tar.ar_get_launch_shape(ks)}
+        if name == "rd":
+            del ins, outs
+            torch.cuda.empty_cache()
+            words = [torch.full((nbuf // 2,), 1 << 32, dtype=torch.int64, device=dev) for _ in range(P)]
+            rdo = [torch.empty(nbuf // 2, dtype=torch.int64, device=dev) for _ in range(P)]
+            wa = (vp * P)(*[t.data_ptr() for t in words])
+            ra = (vp * P)(*[t.data_ptr() for t in rdo])
+            tar.ar_err_init(err)
+        for _ in range(args.rounds):
+            for S in sizes:
+                n = S // 2
+                iters = max(20, min(2000, int(2e5 // (S >> 10))))
+                nsets = min(nbuf // n, max(2, (4 << 30) // (16 * S)))
+                for label, shp in shapes.items():
+                    tar.ar_set_launch_shape(kl, *shp)        # both kinds take the shape under test
+                    tar.ar_set_launch_shape(ks, *shp)
+                    if which is None:
+                        hot = _check_us(blib.arb_decode_us(None, None, wa, ra, P, n, None, 0, err.data_ptr(), 0,
+                                                           iters, sh), name)
+                        cold = float("nan")
+                    else:
+                        hot = _check_us(blib.arb_stream_us(which, ia, oa, P, n, None, iters, sh), name)
+                        cold = _check_us(blib.arb_stream_rot_us(which, ia, oa, P, n, n, nsets, iters, sh), name)
+                    res.setdefault((name, S, label), []).append((hot, cold))
+        tar.ar_set_launch_shape(kl, *shapes["large"])
+        tar.ar_set_launch_shape(ks, *shapes["small"])
+        print(f"[tune] crossover {name} done", file=sys.stderr, flush=True)
+        print(f"== {name}: us per call, large-message default {tuple(shapes['large'])} vs small-message default "
+              f"{tuple(shapes['small'])}; hot / cold" + (" (RD: bf16 size; payload is twice that)" if which is None else ""))
+        print("    size per buffer      large hot   large cold   small hot   small cold   default used")
+        for S in sizes:
+            lv = res[(name, S, "large")]
+            sv = res[(name, S, "small")]
+            med = lambda v, i: statistics.median(x[i] for x in v)
+            used = "small" if S // 2 <= tar.AR_SMALL_ELEMS else "large"
+            print(f"    {S >> 10:10d} KiB {med(lv, 0):12.2f} {med(lv, 1):12.2f} {med(sv, 0):11.2f} "
+                  f"{med(sv, 1):12.2f}   {used}")
+        sys.stdout.flush()
+    torch.cuda.synchronize()
+    if err.cpu().tolist()[0]:
+        raise RuntimeError("recursive doubling saw bad sequence numbers")
     return 0
 
 

@@ -5,8 +5,11 @@ non-temporal loads / stores, workgroups per CU); each choice is a different
 kernel instantiation or grid.  Here each kind is run under a grid of shapes
 on ragged sizes (tails inside a 16-byte group and inside a tile) and every
 result is compared with the oracle, bit for bit; the default shape is
-restored afterwards.
+restored afterwards.  The one-shot, fused two-stage and fused RD calls pick
+their small-message kind at n <= AR_SMALL_ELEMS and their large-message kind
+above it, so those run at one size on each side of the threshold.
 """
+import functools
 import itertools
 
 import numpy as np
@@ -26,18 +29,37 @@ P = 8
 N = 5 * 4096 + 22          # even; not a multiple of 8 or 16
 ROWS, HIDDEN = 11, 1862    # 20482 elements, odd row count and a hidden size not a multiple of 8
 
+NL = tar.AR_SMALL_ELEMS + 4096 + 22   # above the small-message threshold; not a multiple of 8
+
 XS = synth.rank_buffers("logmag", P, N, 900)
 REF = oracle.reduce_seq(XS)
 
 
-def with_shape(kind, shape, fn):
-    before = tar.ar_get_launch_shape(kind)
-    tar.ar_set_launch_shape(kind, *shape)
+@functools.lru_cache(maxsize=1)
+def large():
+    """Inputs above the threshold and their oracle results (built on first use,
+    not at collection)."""
+    xl = synth.rank_buffers("logmag", P, NL, 901)
+    words = [oracle.pack(x, 9) for x in xl]         # NL / 2 words: odd, so RD's one-lane tail runs
+    return xl, oracle.reduce_seq(xl), words, {carry: oracle.rd(words, 9, carry) for carry in (False, True)}
+
+
+def with_shape(kinds, shape, fn):
+    kinds = kinds if isinstance(kinds, (tuple, list)) else (kinds,)
+    before = [tar.ar_get_launch_shape(k) for k in kinds]
+    for k in kinds:
+        tar.ar_set_launch_shape(k, *shape)
     try:
         fn()
         torch.cuda.synchronize()
     finally:
-        tar.ar_set_launch_shape(kind, *before)
+        for k, b in zip(kinds, before):
+            tar.ar_set_launch_shape(k, *b)
+
+
+ONESHOT_KINDS = (tar.AR_KERNEL_ONESHOT, tar.AR_KERNEL_ONESHOT_SMALL)
+TWOSTAGE_KINDS = (tar.AR_KERNEL_2STAGE, tar.AR_KERNEL_2STAGE_SMALL)
+RD_KINDS = (tar.AR_KERNEL_RD, tar.AR_KERNEL_RD_SMALL)
 
 
 def eq(got, want, what):
@@ -47,16 +69,19 @@ def eq(got, want, what):
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}v{}l{}s{}w{}".format(*s))
 def test_reduce_kinds(shape):
+    xl, refl = large()[:2]
+    for xs, ref, n in ((XS, REF, N), (xl, refl, NL)):
+        ins = [up16(x) for x in xs]
+        note(f"shape {shape}: oneshot n={n}")
+        out = empty16(n)
+        with_shape(ONESHOT_KINDS, shape, lambda: tar.ar_reduce_oneshot(ins, out))
+        eq(down16(out), ref, f"oneshot n={n}")
+        note(f"shape {shape}: 2stage fused n={n}")
+        outs = [empty16(n) for _ in range(P)]
+        with_shape(TWOSTAGE_KINDS, shape, lambda: tar.ar_reduce_2stage(ins, outs))
+        for o in outs:
+            eq(down16(o), ref, f"2stage n={n}")
     ins = [up16(x) for x in XS]
-    note(f"shape {shape}: oneshot")
-    out = empty16(N)
-    with_shape(tar.AR_KERNEL_ONESHOT, shape, lambda: tar.ar_reduce_oneshot(ins, out))
-    eq(down16(out), REF, "oneshot")
-    note(f"shape {shape}: 2stage fused")
-    outs = [empty16(N) for _ in range(P)]
-    with_shape(tar.AR_KERNEL_2STAGE, shape, lambda: tar.ar_reduce_2stage(ins, outs))
-    for o in outs:
-        eq(down16(o), REF, "2stage")
     note(f"shape {shape}: 2stage staged (rs, then ag)")
     for kind in (tar.AR_KERNEL_RS, tar.AR_KERNEL_AG):
         outs = [empty16(N) for _ in range(P)]
@@ -103,7 +128,7 @@ def test_payload_kinds(shape):
     with_shape(tar.AR_KERNEL_PACK, shape, pack_all)
     for w, r in zip(words, words_ref):
         eq(down64(w), r, "pack")
-    for kind, flags, carry in ((tar.AR_KERNEL_RD, 0, False), (tar.AR_KERNEL_RD, tar.AR_RD_FP32_CARRY, True),
+    for kind, flags, carry in ((RD_KINDS, 0, False), (RD_KINDS, tar.AR_RD_FP32_CARRY, True),
                                (tar.AR_KERNEL_RDSTEP, tar.AR_RD_STAGED, False)):
         note(f"shape {shape}: rd kind {kind} flags {flags}")
         outs = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
@@ -125,6 +150,17 @@ def test_payload_kinds(shape):
         with_shape(kind, shape, fn)
         eq(down16(out), xs[2], f"unpack kind {kind}")
         assert err_host(err) == (0, 2 ** 64 - 1)
+    note(f"shape {shape}: fused rd above the small-message threshold (n={NL})")
+    _, _, words_ref_l, rd_l = large()
+    words_l = [up64(w) for w in words_ref_l]
+    for flags, carry in ((0, False), (tar.AR_RD_FP32_CARRY, True)):
+        outs = [torch.empty(NL // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+        err = new_err()
+        with_shape(RD_KINDS, shape, lambda: tar.ar_rd_schedule(words_l, outs, 9, err, flags=flags))
+        want, werr = rd_l[carry]
+        for o, w in zip(outs, want):
+            eq(down64(o), w, f"rd n={NL} carry={carry}")
+        assert err_host(err) == (int(werr[0]), int(werr[1]))
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}v{}l{}s{}w{}".format(*s))
