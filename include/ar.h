@@ -222,13 +222,15 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
  * to launches made after the call, process-wide; the call is thread-safe.
  * Returns AR_ERR_INVALID for an unknown kind or out-of-range field.
  *
- * The one-shot, fused two-stage and fused recursive-doubling kernels have a
- * second kind each (..._SMALL) whose shape applies when a call's element
- * count n is at most AR_SMALL_ELEMS (4 MiB of bf16 per rank: the decode
- * messages).  Such a call moves too little data for the occupancy cap that
- * helps long streams; its time is launch, one memory round trip and the
- * number of workgroup rounds, so its default is uncapped with plain loads,
- * which also keep data that is already on chip there.
+ * The one-shot, fused two-stage, fused recursive-doubling and staged
+ * recursive-doubling-step kernels have a second kind each (..._SMALL) whose
+ * shape applies when a call's element count n is at most AR_SMALL_ELEMS
+ * (4 MiB of bf16 per rank: the decode messages).  Such a call moves too
+ * little data for the occupancy cap that helps long streams; its time is
+ * launch, one memory round trip and the number of workgroup rounds, so its
+ * default is uncapped with plain loads, which also keep data that is already
+ * on chip there (and, for the staged step, plain stores, which keep each
+ * step's mailbox on chip for the next step).
  */
 #define AR_SMALL_ELEMS 2097152
 #define AR_KERNEL_ONESHOT  0   /* ar_reduce_oneshot                         */
@@ -249,6 +251,7 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 #define AR_KERNEL_ONESHOT_SMALL 14 /* ar_reduce_oneshot, n <= AR_SMALL_ELEMS   */
 #define AR_KERNEL_2STAGE_SMALL 15  /* ar_reduce_2stage fused, n <= AR_SMALL_ELEMS */
 #define AR_KERNEL_RD_SMALL 16      /* ar_rd_schedule fused, n <= AR_SMALL_ELEMS */
+#define AR_KERNEL_RDSTEP_SMALL 17  /* ar_rd_schedule staged, n <= AR_SMALL_ELEMS */
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu);
 int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
                         int* wg_per_cu);

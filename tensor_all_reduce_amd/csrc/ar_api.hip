@@ -49,7 +49,7 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {64, 1, 1, 1, 0, 0},    // pack, 1 -> 2 (vec: 16-byte bf16 groups per lane; 1 = 8 bytes)
     {64, 1, 1, 1, 0, 0},    // unpack, 2 -> 1
     {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
-    {64, 1, 1, 1, 8, 0},    // staged recursive-doubling step, 8 -> 8
+    {128, 1, 1, 1, 8, 0},   // staged recursive-doubling step, 8 -> 8
     {256, 1, 0, 1, 2, 0},   // waiting unpack: 2 persistent workgroups (8 waves) per CU
     {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few store waits and counter atomics per chunk
     {64, 2, 1, 1, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
@@ -58,12 +58,13 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {128, 1, 0, 1, 0, 0},   // one-shot, n <= AR_SMALL_ELEMS: uncapped, plain loads
     {128, 1, 0, 1, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
     {64, 1, 0, 1, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
+    {64, 1, 0, 0, 0, 0},    // staged RD step, n <= AR_SMALL_ELEMS: plain stores keep the mailbox on chip
 };
 constexpr const char* kShapeEnv[ar::kKinds] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
     "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT",
     "AR_SHAPE_UBATCH_FLAGS", "AR_SHAPE_QUANT_FP8", "AR_SHAPE_REDUCE_FP8", "AR_SHAPE_REDUCE_FP8_ALL",
-    "AR_SHAPE_ONESHOT_SMALL", "AR_SHAPE_2STAGE_SMALL", "AR_SHAPE_RD_SMALL"};
+    "AR_SHAPE_ONESHOT_SMALL", "AR_SHAPE_2STAGE_SMALL", "AR_SHAPE_RD_SMALL", "AR_SHAPE_RDSTEP_SMALL"};
 
 std::mutex g_mu;
 DevInfo g_dev[kMaxDevices];

@@ -490,7 +490,7 @@ hipError_t launch_rd_staged(const Launch& L, const WordIn& in, const WordOut& ou
   const size_t W = n >> 1;
   const size_t Ws = rd_mailbox_stride(n);
   const int steps = P == 2 ? 1 : (P == 4 ? 2 : 3);
-  const Shape& sh = L.shape[kRDStep];
+  const Shape& sh = shape_for(L, kRDStep, kRDStepSmall, n);
   const size_t tiles = flat_grid(sh, W >> 1);
   if (tiles * (size_t)(P / 2) > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(tiles * (size_t)(P / 2)));

@@ -46,6 +46,7 @@ enum Kind {
   kOneshotSmall, // kOneshot for n <= AR_SMALL_ELEMS
   k2StageSmall,  // k2Stage for n <= AR_SMALL_ELEMS
   kRDSmall,      // kRD for n <= AR_SMALL_ELEMS
+  kRDStepSmall,  // kRDStep for n <= AR_SMALL_ELEMS
   kKinds
 };
 

@@ -11,8 +11,9 @@ shuffled order each round and the median over rounds is reported, so slow
 drift of the device affects all candidates alike.  GB/s counts each input
 read once and each output written once.
 
-With --decode, the small-message kinds (one-shot, fused two-stage and fused
-recursive doubling for n <= AR_SMALL_ELEMS) are instead timed at the decode
+With --decode, the small-message kinds (one-shot, fused two-stage, fused
+recursive doubling and the staged recursive-doubling step, for
+n <= AR_SMALL_ELEMS) are instead timed at the decode
 sizes (P = 8, [T x 8192] for T = 8, 32, 128: 128 KiB to 2 MiB per buffer) as
 per-call stream time over back-to-back calls from the native timing loops in
 libarbench.so, so no Python runs between calls.
@@ -216,6 +217,7 @@ def decode(args):
     rng = random.Random(11)
     mmax = 128 * HIDDEN
     ins = [t.view(torch.int16) for t in synth.device_rank_buffers("normal", P, mmax, 2, dev)]
+    mbox = torch.empty(tar.rd_mailbox_words(P, mmax), dtype=torch.int64, device=dev)
     outs = [torch.empty(mmax, dtype=torch.int16, device=dev) for _ in range(P)]
     words = [torch.empty(mmax // 2, dtype=torch.int64, device=dev) for _ in range(P)]
     rdo = [torch.empty(mmax // 2, dtype=torch.int64, device=dev) for _ in range(P)]
@@ -236,7 +238,10 @@ def decode(args):
                 ("2stage", tar.AR_KERNEL_2STAGE_SMALL,
                  lambda: blib.arb_stream_us(1, ia, oa, P, m, None, 2000, sh)),
                 ("rd", tar.AR_KERNEL_RD_SMALL,
-                 lambda: blib.arb_decode_us(None, None, wa, ra, P, m, None, 0, err.data_ptr(), 0, 1000, sh))):
+                 lambda: blib.arb_decode_us(None, None, wa, ra, P, m, None, 0, err.data_ptr(), 0, 1000, sh)),
+                ("rdstep", tar.AR_KERNEL_RDSTEP_SMALL,
+                 lambda: blib.arb_decode_us(None, None, wa, ra, P, m, mbox.data_ptr(), tar.AR_RD_STAGED,
+                                            err.data_ptr(), 0, 300, sh))):
             default = tar.ar_get_launch_shape(k)
             cs = cands + ([default] if default not in cands else [])
             times = {c: [] for c in cs}
@@ -249,7 +254,8 @@ def decode(args):
             tar.ar_set_launch_shape(k, *default)
             med = {c: statistics.median(v) for c, v in times.items()}
             ranked = sorted(cs, key=lambda c: med[c])
-            what = f"{4 * m // 1024} KiB of payload per rank" if name == "rd" else f"{2 * m // 1024} KiB per buffer"
+            what = (f"{4 * m // 1024} KiB of payload per rank" if name.startswith("rd")
+                    else f"{2 * m // 1024} KiB per buffer")
             print(f"== {name} (small-message kind) T={T} ({what}): per-call stream time")
             print("   rank  block vec ntl nts wg/cu      us")
             for i, c in enumerate(ranked):

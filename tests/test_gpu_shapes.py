@@ -5,9 +5,10 @@ non-temporal loads / stores, workgroups per CU); each choice is a different
 kernel instantiation or grid.  Here each kind is run under a grid of shapes
 on ragged sizes (tails inside a 16-byte group and inside a tile) and every
 result is compared with the oracle, bit for bit; the default shape is
-restored afterwards.  The one-shot, fused two-stage and fused RD calls pick
-their small-message kind at n <= AR_SMALL_ELEMS and their large-message kind
-above it, so those run at one size on each side of the threshold.
+restored afterwards.  The one-shot, fused two-stage, fused RD and staged RD
+calls pick their small-message kind at n <= AR_SMALL_ELEMS and their
+large-message kind above it, so those run at one size on each side of the
+threshold.
 """
 import functools
 import itertools
@@ -60,6 +61,7 @@ def with_shape(kinds, shape, fn):
 ONESHOT_KINDS = (tar.AR_KERNEL_ONESHOT, tar.AR_KERNEL_ONESHOT_SMALL)
 TWOSTAGE_KINDS = (tar.AR_KERNEL_2STAGE, tar.AR_KERNEL_2STAGE_SMALL)
 RD_KINDS = (tar.AR_KERNEL_RD, tar.AR_KERNEL_RD_SMALL)
+RDSTEP_KINDS = (tar.AR_KERNEL_RDSTEP, tar.AR_KERNEL_RDSTEP_SMALL)
 
 
 def eq(got, want, what):
@@ -129,7 +131,7 @@ def test_payload_kinds(shape):
     for w, r in zip(words, words_ref):
         eq(down64(w), r, "pack")
     for kind, flags, carry in ((RD_KINDS, 0, False), (RD_KINDS, tar.AR_RD_FP32_CARRY, True),
-                               (tar.AR_KERNEL_RDSTEP, tar.AR_RD_STAGED, False)):
+                               (RDSTEP_KINDS, tar.AR_RD_STAGED, False)):
         note(f"shape {shape}: rd kind {kind} flags {flags}")
         outs = [torch.empty(n // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
         mbox = torch.empty(tar.rd_mailbox_words(P, n), dtype=torch.int64, device=DEV) if flags & tar.AR_RD_STAGED else None
@@ -150,16 +152,19 @@ def test_payload_kinds(shape):
         with_shape(kind, shape, fn)
         eq(down16(out), xs[2], f"unpack kind {kind}")
         assert err_host(err) == (0, 2 ** 64 - 1)
-    note(f"shape {shape}: fused rd above the small-message threshold (n={NL})")
+    note(f"shape {shape}: fused and staged rd above the small-message threshold (n={NL})")
     _, _, words_ref_l, rd_l = large()
     words_l = [up64(w) for w in words_ref_l]
-    for flags, carry in ((0, False), (tar.AR_RD_FP32_CARRY, True)):
+    mbox_l = torch.empty(tar.rd_mailbox_words(P, NL), dtype=torch.int64, device=DEV)
+    for kinds, flags, carry in ((RD_KINDS, 0, False), (RD_KINDS, tar.AR_RD_FP32_CARRY, True),
+                                (RDSTEP_KINDS, tar.AR_RD_STAGED, False)):
         outs = [torch.empty(NL // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
         err = new_err()
-        with_shape(RD_KINDS, shape, lambda: tar.ar_rd_schedule(words_l, outs, 9, err, flags=flags))
+        mb = mbox_l if flags & tar.AR_RD_STAGED else None
+        with_shape(kinds, shape, lambda: tar.ar_rd_schedule(words_l, outs, 9, err, mailbox=mb, flags=flags))
         want, werr = rd_l[carry]
         for o, w in zip(outs, want):
-            eq(down64(o), w, f"rd n={NL} carry={carry}")
+            eq(down64(o), w, f"rd n={NL} flags={flags}")
         assert err_host(err) == (int(werr[0]), int(werr[1]))
 
 
