@@ -368,8 +368,10 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     res["copy_8to8_GBps"] = round(best8, 1)
     res["copy_8to8_shape"] = shape8
     # the ubatch row's pattern: the same copy split at the middle row, the two
-    # halves on two streams at once (as the two ubatch reduces run)
-    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    # halves on two streams at once (as the two ubatch reduces run), on the
+    # ubatch streams themselves: HIP maps a process's streams onto a few
+    # hardware queues, and two more streams here could put the later
+    # producer / consumer pair on one queue, where they would run in turn
     h = n // 2
     halves = [(parr([x[:h] for x in ins]), parr([o[:h] for o in outs])),
               (parr([x[h:] for x in ins]), parr([o[h:] for o in outs]))]
