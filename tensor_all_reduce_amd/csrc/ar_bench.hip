@@ -184,6 +184,61 @@ __global__ __launch_bounds__(256) void k_gridstride88(In8 in, Out8 out, size_t n
   }
 }
 
+// The fused 8 -> 8 reduce with a chosen access width, for the A/B of 4-,
+// 8- and 16-byte accesses per lane: each 64-lane workgroup owns 1 KiB of
+// every buffer (as the library's one-group-per-lane tiles do) and each lane
+// moves 16 bytes of it per buffer as 16 / WB accesses of WB bytes, access j
+// of the wavefront covering bytes [j * 64 * WB, (j + 1) * 64 * WB) of the
+// tile, so every instruction is one contiguous span and the bytes in flight
+// per lane are the same at every width.  Same arithmetic as the library.
+template <int WB> struct AccessT;
+template <> struct AccessT<4> { typedef uint32_t T; };
+template <> struct AccessT<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
+template <> struct AccessT<16> { typedef u32x4 T; };
+
+struct Bytes8 {
+  const char* in[8];
+  char* out[8];
+};
+
+template <int WB>
+__global__ __launch_bounds__(64) void k_width88(Bytes8 b, size_t nbytes) {
+  typedef typename AccessT<WB>::T T;
+  constexpr int A = 16 / WB;   // accesses per lane per buffer
+  constexpr int NW = WB / 4;   // 32-bit words per access
+  const size_t tile = (size_t)blockIdx.x * 1024;
+  if (tile + 1024 > nbytes) return;   // whole tiles only (the caller passes a multiple of 1 KiB)
+  T a[A][8];
+#pragma unroll
+  for (int j = 0; j < A; ++j)
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      a[j][p] = __builtin_nontemporal_load(reinterpret_cast<const T*>(b.in[p] + tile + (size_t)j * 64 * WB) +
+                                           threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < A; ++j) {
+    uint32_t w[8][NW];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) __builtin_memcpy(w[p], &a[j][p], WB);
+    uint32_t r[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      float lo = __uint_as_float(w[0][k] << 16), hi = __uint_as_float(w[0][k] & 0xFFFF0000u);
+#pragma unroll
+      for (int p = 1; p < 8; ++p) {
+        lo = lo + __uint_as_float(w[p][k] << 16);
+        hi = hi + __uint_as_float(w[p][k] & 0xFFFF0000u);
+      }
+      r[k] = (rne_hi_b(lo) >> 16) | (rne_hi_b(hi) & 0xFFFF0000u);
+    }
+    T v;
+    __builtin_memcpy(&v, r, WB);
+#pragma unroll
+    for (int o = 0; o < 8; ++o)
+      __builtin_nontemporal_store(v, reinterpret_cast<T*>(b.out[o] + tile + (size_t)j * 64 * WB) + threadIdx.x);
+  }
+}
+
 // Unpack with per-lane error atomics, for the A/B against the library's
 // wavefront-ballot validation: lane v unpacks payload words 2v and 2v+1
 // (one 16-byte load, one 8-byte store, as the library's unpack does) and
@@ -396,6 +451,39 @@ int arb_gridstride_reduce8(const void* const* ins, void* const* outs, size_t n, 
     out.p[p] = static_cast<u32x4*>(outs[p]);
   }
   hipLaunchKernelGGL(k_gridstride88, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), in, out, n / 8);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+// Fused 8 -> 8 reduce with `width`-byte accesses (4, 8 or 16; see
+// k_width88): n elements per buffer, a multiple of 512; buffers 16-byte
+// aligned; 64-lane workgroups, at most wg_per_cu per CU through a dynamic
+// LDS request (0: no cap).
+int arb_width_reduce8(const void* const* ins, void* const* outs, size_t n, int width, int wg_per_cu,
+                      void* stream) {
+  if (!ins || !outs || (n & 511u) || n == 0 || (width != 4 && width != 8 && width != 16) || wg_per_cu < 0)
+    return AR_ERR_INVALID;
+  Bytes8 b{};
+  for (int p = 0; p < 8; ++p) {
+    if (!ins[p] || !outs[p]) return AR_ERR_INVALID;
+    b.in[p] = static_cast<const char*>(ins[p]);
+    b.out[p] = static_cast<char*>(outs[p]);
+  }
+  unsigned lds = 0;
+  if (wg_per_cu > 0) {
+    int dev = 0, per_cu = 0, per_block = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return AR_ERR_HIP;
+    lds = ((unsigned)per_cu / (unsigned)wg_per_cu) & ~255u;
+    if (lds > (unsigned)per_block) lds = (unsigned)per_block;
+  }
+  const size_t nbytes = n * 2, grid = nbytes / 1024;
+  if (grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (width == 4) hipLaunchKernelGGL(k_width88<4>, dim3((unsigned)grid), dim3(64), lds, st, b, nbytes);
+  else if (width == 8) hipLaunchKernelGGL(k_width88<8>, dim3((unsigned)grid), dim3(64), lds, st, b, nbytes);
+  else hipLaunchKernelGGL(k_width88<16>, dim3((unsigned)grid), dim3(64), lds, st, b, nbytes);
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 

@@ -176,7 +176,7 @@ def cmd_kstats(a):
     for c in a.command:
         print(f"# command: {c}")
     print("# kernel                                              calls    avg_ms    min_ms    max_ms" +
-          ("   counters (mean per dispatch, KiB)" if cnt else ""))
+          ("   counters (mean per dispatch; FETCH_SIZE and WRITE_SIZE in KiB)" if cnt else ""))
     for r in csv.DictReader(open(stats)):
         name = _kname(r["Name"])
         extra = "  ".join(f"{cn}={statistics.mean(v):.0f}" for (kn, cn), v in sorted(cnt.items()) if kn == name)
