@@ -803,6 +803,18 @@ def fp8(tar, torch, dev, main_s, ins, outs):
     return {"fp8": res}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, np):
     """The oracle (single-threaded C, as it stands) on a bounded sample of the
     same step: the first `rows_s` rows of the [16384 x 8192] workload."""
@@ -841,7 +853,7 @@ def cpu_baseline(args, np):
     res = {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"one full step (all six rows) of the oracle on the first {rows_s} of 16384 rows "
                      f"(P=8, hidden 8192, N(0,1)); {dt:.1f} s on one host core; credited bytes as the GPU step",
-           "seconds": round(dt, 2)}
+           "seconds": round(dt, 2), "cpu_model": cpu_model()}
     if args.no_cpu_all_cores:
         return res
     # the same oracle on all host cores (at most 16): the step's rows split
