@@ -60,7 +60,10 @@ def test_decode_configs(P, n):
         check_full(o, ref, "2stage staged")
 
 
-RAGGED = [1, 2, 7, 8, 9, 15, 17, 255, 1000, 2049, 65536 + 3, 300001, 4 * 1024 * 1024 + 5]
+# the last three sit on and around the element count at which the one-shot and
+# two-stage calls switch from their small-message launch shape to the large one
+RAGGED = [1, 2, 7, 8, 9, 15, 17, 255, 1000, 2049, 65536 + 3, 300001, 4 * 1024 * 1024 + 5,
+          tar.AR_SMALL_ELEMS - 1, tar.AR_SMALL_ELEMS, tar.AR_SMALL_ELEMS + 1]
 
 
 @pytest.mark.parametrize("n", RAGGED)
@@ -187,7 +190,8 @@ def _rd_case(P, n, seq0, kind="normal", cfg=3):
 
 
 @pytest.mark.parametrize("seq0", [1, 0xFFFFFFFE])
-@pytest.mark.parametrize("P,n", [(8, 128 * HIDDEN), (2, 20002), (4, 65538), (8, 6)])
+@pytest.mark.parametrize("P,n", [(8, 128 * HIDDEN), (2, 20002), (4, 65538), (8, 6),
+                                 (8, tar.AR_SMALL_ELEMS), (8, tar.AR_SMALL_ELEMS + 2)])
 def test_pack_rd_unpack(P, n, seq0):
     """Pack on the GPU, recursive doubling (fused R1, staged R1, fused R2),
     unpack with validation; payload words, data and counts vs the oracle."""
