@@ -19,7 +19,8 @@ Inputs are resident in HBM before the timed region.
 Also reported (not part of `value`): per-call latency of one-shot and
 two-stage at 128 KiB / 512 KiB / 2 MiB per buffer (native timing loop, no
 Python in the loop), the staged two-stage at the prefill size, the ubatch
-reduce at its own [16384 x 16384] shape, attainable copy bandwidth (a plain
+reduce at its own [16384 x 16384] shape, the waiting unpack (on ready payloads
+and as a producer -> consumer handoff), attainable copy bandwidth (a plain
 copy, and eight buffers copied side by side: the 8 -> 8 pattern of the
 two-stage, RD and ubatch rows, for the ubatch split over two streams), and
 the CPU oracle on a bounded sample of the same step (`cpu_baseline`).
@@ -142,6 +143,9 @@ def main():
     blib.arb_decode_us.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                    ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t, vp, ctypes.c_int, vp,
                                    ctypes.c_int, ctypes.c_int, vp]
+    blib.arb_handoff_us.restype = ctypes.c_double
+    blib.arb_handoff_us.argtypes = [vp, vp, vp, ctypes.c_size_t, ctypes.c_uint32, vp, ctypes.c_int, ctypes.c_int,
+                                    vp, vp]
     blib.arb_readsum.restype = ctypes.c_int
     blib.arb_readsum.argtypes = [vp, ctypes.c_size_t, vp, vp]
     blib.arb_consume_chunks.restype = ctypes.c_int
@@ -543,6 +547,7 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     log("graph latency measured")
 
     res.update(overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1))
+    res.update(wait_receive(tar, blib, torch, dev, main_s, ins, outs, s0, s1))
     res.update(fp8(tar, torch, dev, main_s, ins, outs))
 
     # ubatch reduce at its own shape: [16384 x 16384] per rank, 2 streams, 1 MiB chunks
@@ -725,6 +730,72 @@ def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
                                                     "serial_ms": round(t_rf + t_w, 4),
                                                     "pipelined_ms": round(t_wpipe, 4),
                                                     "overlap_fraction": round(ov_w, 3)}}}
+
+
+def wait_receive(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
+    """The waiting unpack (ar_unpack_fused_wait).
+
+    prefill: all 8 rank payloads of the [16384 x 8192] batch already carry
+    the expected sequence number; the waiting unpack against the plain one
+    (3 B per element each: payload read, bf16 written).
+    decode_handoff: one rank's [128 x 8192] message through the native loop
+    arb_handoff_us: the producer packs it on s0 with a new sequence number
+    each time and the consumer, queued after it on s1 with no dependency on
+    it, polls until its words carry that number.  Median time from before the
+    pack to after the unpack, against the same pack and a plain unpack one
+    after the other on one stream; every handoff must complete with no stale
+    word."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(reps):
+            fn()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    n = ROWS * HIDDEN
+    err = torch.empty(2, dtype=torch.int64, device=dev)
+    tar.ar_err_init(err, stream=main_s)
+    words = [torch.empty(n // 2, dtype=torch.int64, device=dev) for _ in range(P)]
+    for r in range(P):
+        tar.ar_pack_fused(ins[r], words[r], 7)
+    b = P * 3 * 2 * n
+    t_plain = timed(lambda: [tar.ar_unpack_fused(words[r], outs[r], 7, err) for r in range(P)], 5)
+    t_wait = timed(lambda: [tar.ar_unpack_fused_wait(words[r], outs[r], 7, err) for r in range(P)], 5)
+    del words
+    torch.cuda.empty_cache()
+    m = 128 * HIDDEN
+    w1 = torch.empty(m // 2, dtype=torch.int64, device=dev)
+    x1 = torch.empty(m, dtype=torch.int16, device=dev)
+    x0 = ins[0][:m]
+    torch.cuda.synchronize()
+
+    def handoff(serial, seq0):
+        us = blib.arb_handoff_us(x0.data_ptr(), w1.data_ptr(), x1.data_ptr(), m, seq0, err.data_ptr(), 300,
+                                 serial, (main_s if serial else s0).cuda_stream, s1.cuda_stream)
+        if us < 0:
+            raise RuntimeError(f"arb_handoff_us failed: {us}")
+        return us
+
+    t_hand = handoff(0, 1000)
+    t_ser = handoff(1, 5000)
+    torch.cuda.synchronize()
+    stale = int(err[0].item())
+    if stale:
+        raise RuntimeError(f"waiting unpack left {stale} stale payload words")
+    if not torch.equal(x1, x0):
+        raise RuntimeError("waiting unpack: data differs from the packed input")
+    g = lambda t: round(b / (t * 1e-3) / 1e9, 1)
+    log(f"waiting unpack: prefill {t_wait:.3f} ms vs plain {t_plain:.3f} ms; decode handoff {t_hand:.2f} us "
+        f"(pack then plain unpack on one stream {t_ser:.2f} us)")
+    return {"wait_receive": {
+        "prefill": {"wait_ms": round(t_wait, 4), "wait_GBps": g(t_wait), "plain_ms": round(t_plain, 4),
+                    "plain_GBps": g(t_plain), "unpacks": P},
+        "decode_handoff_128x8192": {"waiting_us": round(t_hand, 2), "serial_pack_unpack_us": round(t_ser, 2),
+                                    "measure": "median, event before the pack to event after the unpack"}}}
 
 
 def fp8(tar, torch, dev, main_s, ins, outs):

@@ -128,6 +128,13 @@ __global__ __launch_bounds__(256) void k_consume(const uint32_t* done, uint32_t 
   if constexpr (WORK) sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = total;
 }
 
+// One wavefront that sleeps `rounds` times (about 64 * 127 clocks each): a
+// bounded delay at the head of a stream, so that the host can queue work
+// behind it before the GPU reaches that work.
+__global__ void k_delay(int rounds) {
+  for (int i = 0; i < rounds; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 // Read-only sweep: every lane loads 16-byte groups (non-temporal) and folds
 // them with xor; one word per workgroup is written so the loads stay live.
 // Measures the attainable read bandwidth beside the copy's read+write rate.
@@ -437,6 +444,65 @@ double arb_decode_us(const void* const* x, void* const* y, uint64_t* const* w_in
   }
   (void)hipEventRecord(ev.b, s);
   return ev.us_between(iters);
+}
+
+// Decode-size handoff through the waiting unpack.  Handoff i records an
+// event on stream sa, packs x with sequence number seq0 + i + 1 on sa, then,
+// queued after it, unpacks on stream sb with ar_unpack_fused_wait, which
+// polls until its words carry that number (the consumer is launched with no
+// dependency on its producer), and records an event on sb.  Handoff i + 1
+// waits for handoff i's unpack (it overwrites the words that unpack reads);
+// that wait lies between handoffs, outside what is timed.  serial != 0: the
+// pack and a plain unpack one after the other on sa.  Returns the median
+// microseconds from the first event to the second over `iters` handoffs
+// (after 10 untimed ones), or a negative status.
+double arb_handoff_us(const void* x, uint64_t* words, void* y, size_t n, uint32_t seq0, uint64_t* d_err,
+                      int iters, int serial, void* sa, void* sb) {
+  if (iters < 1 || iters > 100000 || !x || !words || !y || !d_err || (!serial && !sb)) return AR_ERR_INVALID;
+  hipStream_t a = static_cast<hipStream_t>(sa);
+  hipStream_t b = serial ? a : static_cast<hipStream_t>(sb);
+  const int total = iters + 10;
+  std::vector<hipEvent_t> e0(total, nullptr), e1(total, nullptr);
+  int rc = AR_OK;
+  for (int i = 0; i < total && rc == AR_OK; ++i)
+    if (hipEventCreate(&e0[i]) != hipSuccess || hipEventCreate(&e1[i]) != hipSuccess) rc = AR_ERR_HIP;
+  // a delay at the head of both streams (about 7 ms), so every handoff is
+  // queued before the GPU reaches it and no host enqueue gap lands between
+  // a pair of events
+  hipEvent_t head = nullptr;
+  if (rc == AR_OK && hipEventCreateWithFlags(&head, hipEventDisableTiming) != hipSuccess) rc = AR_ERR_HIP;
+  if (rc == AR_OK) {
+    hipLaunchKernelGGL(k_delay, dim3(1), dim3(64), 0, a, 2000);
+    if (hipGetLastError() != hipSuccess || hipEventRecord(head, a) != hipSuccess ||
+        hipStreamWaitEvent(b, head, 0) != hipSuccess)
+      rc = AR_ERR_HIP;
+  }
+  uint32_t seq = seq0;
+  for (int i = 0; i < total && rc == AR_OK; ++i) {
+    ++seq;
+    if (i > 0 && !serial && hipStreamWaitEvent(a, e1[i - 1], 0) != hipSuccess) rc = AR_ERR_HIP;
+    if (rc == AR_OK && hipEventRecord(e0[i], a) != hipSuccess) rc = AR_ERR_HIP;
+    if (rc == AR_OK) rc = ar_pack_fused(x, words, n, seq, sa);
+    if (rc == AR_OK)
+      rc = serial ? ar_unpack_fused(words, y, n, seq, d_err, sa)
+                  : ar_unpack_fused_wait(words, y, n, seq, 1u << 20, d_err, sb);
+    if (rc == AR_OK && hipEventRecord(e1[i], b) != hipSuccess) rc = AR_ERR_HIP;
+  }
+  if (hipStreamSynchronize(a) != hipSuccess || hipStreamSynchronize(b) != hipSuccess) rc = rc ? rc : AR_ERR_HIP;
+  std::vector<double> us;
+  for (int i = 10; i < total && rc == AR_OK; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e0[i], e1[i]) != hipSuccess) rc = AR_ERR_HIP;
+    us.push_back(1000.0 * ms);
+  }
+  for (int i = 0; i < total; ++i) {
+    if (e0[i]) (void)hipEventDestroy(e0[i]);
+    if (e1[i]) (void)hipEventDestroy(e1[i]);
+  }
+  if (head) (void)hipEventDestroy(head);
+  if (rc != AR_OK) return (double)rc;
+  std::nth_element(us.begin(), us.begin() + us.size() / 2, us.end());
+  return us[us.size() / 2];
 }
 
 // Grid-stride 8 -> 8 reduce (see k_gridstride88): n elements per buffer, a
