@@ -153,7 +153,16 @@ template <int P, int NOUT, int EPL, bool NTL, bool NTS>
 __global__ __launch_bounds__(kMaxBlock) void k_reduce_fp8(ByteIn codes, ByteIn scales, OutPtrs out,
                                                           size_t n) {
   constexpr int NW = EPL / 4;
-  const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // Workgroups reach the 8 XCDs round-robin.  Within every run of 32
+  // workgroups, XCD x takes the 4 consecutive tiles 4x .. 4x + 3, so the
+  // tiles that share a 128-byte line of scale bytes (4 at 128 lanes x 8
+  // elements) meet in one XCD's L2 instead of fetching it once per XCD.  The
+  // last, partial run keeps the identity order; every tile is still taken
+  // exactly once.
+  size_t tile = blockIdx.x;
+  if ((size_t)(blockIdx.x / 32 + 1) * 32 <= gridDim.x)
+    tile = (size_t)(blockIdx.x / 32) * 32 + (blockIdx.x % 8) * 4 + (blockIdx.x / 8) % 4;
+  const size_t g = tile * blockDim.x + threadIdx.x;
   const size_t i0 = g * EPL;
   if (i0 >= n) return;
   if (i0 + EPL <= n) {
