@@ -105,7 +105,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         msg = (f"bench.py measures one GPU only (got --gpus {args.gpus}): the simulated ranks live "
-               "in one GPU's HBM and this build runs no collective between GPUs")
+               "in one GPU's HBM and no collective between GPUs is run")
         print(msg, file=sys.stderr)
         print(json.dumps({"error": msg, "n_gpus": args.gpus}))
         return 2
