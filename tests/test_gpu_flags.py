@@ -119,6 +119,47 @@ def test_consumer_follows_flags():
         check(o, ref, "flagged outputs")
 
 
+def test_consumer_over_many_epochs_reuses_the_arrays():
+    """Twelve producer -> consumer rounds on one pair of flag and counter
+    arrays, never re-zeroed: each round's flags carry its own epoch and the
+    counters must be back at zero for the next.  Inputs alternate between
+    two data sets and the watched output is reset to a sentinel before every
+    round, so a chunk taken on a stale flag, or read before it was complete,
+    would show up in the copy."""
+    P, rows, hidden = 8, 512, 8192
+    n = rows * hidden
+    chunk = (1 << 20) - 4096 + 16                  # chunks that do not divide the rows evenly
+    sets = []
+    for seed in (93, 94):
+        xs = synth.rank_buffers("logmag", P, n, seed)
+        sets.append(([up16(x) for x in xs], oracle.reduce_seq(xs)))
+    outs = [empty16(n) for _ in range(P)]
+    dst = empty16(n)
+    nchunks = tar.ubatch_chunk_count(rows, hidden, 1, None, chunk)   # one ubatch: chunk g starts at g * chunk
+    done, tiles = u32(nchunks), u32(nchunks)
+    timeouts = u32(1)
+    B = bench_lib()
+    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+    for epoch in range(1, 13):
+        ins, ref = sets[epoch % 2]
+        outs[5].fill_(0x5A5A)
+        dst.fill_(0x1111)
+        prod.wait_stream(torch.cuda.current_stream())
+        cons.wait_stream(torch.cuda.current_stream())
+        note(f"flags epoch {epoch} of 12")
+        tar.ar_reduce_ubatch_flags(ins, outs, rows, hidden, done, tiles, epoch, 1, None, chunk,
+                                   tar.AR_VARIANT_2STAGE, [prod])
+        rc = B.arb_consume_chunks(done.data_ptr(), epoch, outs[5].data_ptr(), dst.data_ptr(), n, chunk // 2, 0,
+                                  1 << 22, timeouts.data_ptr(), 0, None, 256, cons.cuda_stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        assert int(timeouts.item()) == 0, f"epoch {epoch}"
+        check(dst, ref, f"consumer copy, epoch {epoch}")
+        for o in outs:
+            check(o, ref, f"flagged outputs, epoch {epoch}")
+        assert np.all(done.cpu().numpy() == epoch) and not tiles.cpu().numpy().any(), f"epoch {epoch}"
+
+
 def test_compute_consumer_ragged_chunks():
     """Two ubatches on two streams, chunks that are not a whole number of
     consumer tiles and a ragged last chunk per ubatch; the consumer (on a

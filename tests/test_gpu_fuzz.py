@@ -45,7 +45,7 @@ def eq(got, want, msg):
     assert bad.size == 0, f"{msg}: {bad.size} mismatches, first at {bad[0]}: got {got[bad[0]]:#x} want {want[bad[0]]:#x}"
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(80))
 def test_fuzz_reduce_family(seed):
     rng = np.random.default_rng([991, seed])
     P = int(rng.integers(1, 9))
@@ -84,7 +84,7 @@ def test_fuzz_reduce_family(seed):
             eq(down16(o), ref, f"{tag} ubatch")
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(80))
 def test_fuzz_payload_family(seed):
     rng = np.random.default_rng([992, seed])
     P = int(rng.choice([2, 4, 8]))
@@ -118,7 +118,7 @@ def test_fuzz_payload_family(seed):
     eq(down16(out)[:n], oracle.unpack(want[P - 1], (seq0 + L) & 0xFFFFFFFF)[0], f"{tag} unpack")
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", range(60))
 def test_fuzz_fp8_family(seed):
     rng = np.random.default_rng([993, seed])
     P = int(rng.integers(1, 9))
