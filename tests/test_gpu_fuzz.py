@@ -4,8 +4,11 @@ Each case draws the rank count, the element count (tiny, ragged, or a few
 tiles), the value mix (normal, log-uniform, integers, or specials mixed in),
 and the operation's own knobs (chunk size, ubatch split, sequence number,
 output count), then compares every output with the oracle bit for bit.  The
-seed of a failing case is in the assertion message.
+seed of a failing case is in the assertion message.  AR_FUZZ_SEEDS=<k> in
+the environment runs k seeds per family.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +19,11 @@ from tensor_all_reduce_amd import synth
 from gpu_util import DEV, note, up16, down16, up64, down64, empty16, new_err, err_host
 
 pytestmark = pytest.mark.gpu
+
+# seeds per family; AR_FUZZ_SEEDS=<k> runs k seeds of every family instead
+# (a longer soak), starting where the default range starts
+_K = os.environ.get("AR_FUZZ_SEEDS")
+N_REDUCE, N_PAYLOAD, N_FP8 = (int(_K),) * 3 if _K else (80, 80, 60)
 
 SPECIALS = np.array([0x7FC0, 0xFFC1, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x807F, 0x7F7F, 0xFF7F, 0x0080],
                     dtype=np.uint16)
@@ -45,7 +53,7 @@ def eq(got, want, msg):
     assert bad.size == 0, f"{msg}: {bad.size} mismatches, first at {bad[0]}: got {got[bad[0]]:#x} want {want[bad[0]]:#x}"
 
 
-@pytest.mark.parametrize("seed", range(80))
+@pytest.mark.parametrize("seed", range(N_REDUCE))
 def test_fuzz_reduce_family(seed):
     rng = np.random.default_rng([991, seed])
     P = int(rng.integers(1, 9))
@@ -84,7 +92,7 @@ def test_fuzz_reduce_family(seed):
             eq(down16(o), ref, f"{tag} ubatch")
 
 
-@pytest.mark.parametrize("seed", range(80))
+@pytest.mark.parametrize("seed", range(N_PAYLOAD))
 def test_fuzz_payload_family(seed):
     rng = np.random.default_rng([992, seed])
     P = int(rng.choice([2, 4, 8]))
@@ -118,7 +126,7 @@ def test_fuzz_payload_family(seed):
     eq(down16(out)[:n], oracle.unpack(want[P - 1], (seq0 + L) & 0xFFFFFFFF)[0], f"{tag} unpack")
 
 
-@pytest.mark.parametrize("seed", range(60))
+@pytest.mark.parametrize("seed", range(N_FP8))
 def test_fuzz_fp8_family(seed):
     rng = np.random.default_rng([993, seed])
     P = int(rng.integers(1, 9))
