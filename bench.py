@@ -129,6 +129,9 @@ def main():
                                  ctypes.c_size_t, vp, ctypes.c_int, vp,
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                  ctypes.POINTER(ctypes.c_double)]
+    blib.arb_enqueue_us.restype = ctypes.c_double
+    blib.arb_enqueue_us.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                    ctypes.c_size_t, vp, ctypes.c_int, vp]
     blib.arb_copy.restype = ctypes.c_int
     blib.arb_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
     blib.arb_copy_multi.restype = ctypes.c_int
@@ -449,9 +452,17 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
             if rc != 0:
                 raise RuntimeError(f"arb_wall_us failed: {rc}")
             cred = (P + 1) * 2 * m if which == 0 else 2 * P * 2 * m
+            enq = blib.arb_enqueue_us(which, parr(xi), parr(xo), P, m, sc.data_ptr(), 5000, sh)
+            if enq < 0:
+                raise RuntimeError(f"arb_enqueue_us failed: {enq}")
             lat[key][name] = {"stream_us": round(us, 2), "wall_us_p50": round(p50.value, 2),
-                              "wall_us_p90": round(p90.value, 2),
+                              "wall_us_p90": round(p90.value, 2), "host_enqueue_us": round(enq, 2),
                               "GBps_hot": round(cred / (us * 1e-6) / 1e9, 1)}
+    # host cost of a launch itself: empty kernels with no, 8 or 192 bytes of
+    # arguments (the library's kernels take about 180 bytes)
+    lat["empty_kernel_host_enqueue_us"] = {
+        k: round(blib.arb_enqueue_us(w, None, None, 0, 0, None, 5000, sh), 2)
+        for k, w in (("no_arguments", -1), ("8_byte_argument", -2), ("192_byte_argument", -3))}
     res["latency"] = lat
     log("latency measured")
 

@@ -135,6 +135,14 @@ __global__ void k_delay(int rounds) {
   for (int i = 0; i < rounds; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
+// Empty kernels with 0, 8 or 192 bytes of arguments: the host cost of a
+// launch itself, against which the library's per-call host cost is read.
+struct Arg8 { uint64_t a; };
+struct Arg192 { uint64_t a[24]; };
+__global__ void k_noarg() {}
+__global__ void k_arg8(Arg8) {}
+__global__ void k_arg192(Arg192) {}
+
 // Read-only sweep: every lane loads 16-byte groups (non-temporal) and folds
 // them with xor; one word per workgroup is written so the loads stay live.
 // Measures the attainable read bandwidth beside the copy's read+write rate.
@@ -358,6 +366,36 @@ double arb_stream_us(int which, const void* const* ins, void* const* outs, int P
   }
   (void)hipEventRecord(ev.b, s);
   return ev.us_between(iters);
+}
+
+// Host time per call of `iters` back-to-back calls, the enqueue only (steady
+// clock around the loop, no synchronisation inside it; the stream is drained
+// before and after).  which 0..2 as for arb_stream_us; which = -1, -2, -3:
+// an empty kernel with no, 8 or 192 bytes of arguments.
+double arb_enqueue_us(int which, const void* const* ins, void* const* outs, int P, size_t n, void* scratch,
+                      int iters, void* stream) {
+  if (iters < 1 || which < -3 || which > 2) return AR_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto one = [&]() -> int {
+    if (which >= 0) return call(which, ins, outs, P, n, scratch, stream);
+    if (which == -1) hipLaunchKernelGGL(k_noarg, dim3(1), dim3(64), 0, s);
+    else if (which == -2) hipLaunchKernelGGL(k_arg8, dim3(1), dim3(64), 0, s, Arg8{0});
+    else hipLaunchKernelGGL(k_arg192, dim3(1), dim3(64), 0, s, Arg192{});
+    return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+  };
+  for (int i = 0; i < 20; ++i) {
+    int rc = one();
+    if (rc) return rc;
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) return AR_ERR_HIP;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < iters; ++i) {
+    int rc = one();
+    if (rc) return rc;
+  }
+  const auto t1 = std::chrono::steady_clock::now();
+  if (hipStreamSynchronize(s) != hipSuccess) return AR_ERR_HIP;
+  return std::chrono::duration<double, std::micro>(t1 - t0).count() / iters;
 }
 
 // Single-call wall latency: C-ABI call -> hipStreamSynchronize return,
