@@ -463,6 +463,32 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     lat["empty_kernel_host_enqueue_us"] = {
         k: round(blib.arb_enqueue_us(w, None, None, 0, 0, None, 5000, sh), 2)
         for k, w in (("no_arguments", -1), ("8_byte_argument", -2), ("192_byte_argument", -3))}
+    # the same enqueue with this thread pinned to each core it may use, in
+    # turn: on a virtual machine the cost depends on which virtual core the
+    # launching thread runs on, so one unpinned figure can land anywhere in
+    # this range
+    m = 8 * HIDDEN
+    xi, xo = [x[:m] for x in ins], [o[:m] for o in outs]
+    allowed = sorted(os.sched_getaffinity(0))
+    per_core = {}
+    try:
+        for c in allowed:
+            os.sched_setaffinity(0, {c})
+            per_core[c] = (blib.arb_enqueue_us(-3, None, None, 0, 0, None, 2000, sh),
+                           blib.arb_enqueue_us(0, parr(xi), parr(xo), P, m, None, 2000, sh))
+    finally:
+        os.sched_setaffinity(0, allowed)
+    if any(v < 0 for pair in per_core.values() for v in pair):
+        raise RuntimeError("arb_enqueue_us failed")
+
+    def spread(vals):
+        vals = sorted(vals)
+        return {"min": round(vals[0], 2), "median": round(vals[len(vals) // 2], 2), "max": round(vals[-1], 2)}
+    fastest = min(per_core, key=lambda c: per_core[c][1])
+    lat["host_enqueue_us_by_core"] = {
+        "cores": len(per_core), "fastest_core": fastest,
+        "empty_kernel_192_byte_argument": spread(v[0] for v in per_core.values()),
+        "oneshot_128KiB": spread(v[1] for v in per_core.values())}
     res["latency"] = lat
     log("latency measured")
 
