@@ -3,9 +3,9 @@
 The bandwidth of the 8-stream kernels depends on where the P rank buffers
 sit relative to one another, and the best launch shape for one placement
 can lose badly on another.  This sweep times candidate shapes of the
-one-shot, fused two-stage, ubatch and fused recursive-doubling kernels on
-the bench workload (P = 8, bf16 [16384 x 8192] per rank, N(0,1)) with the
-buffers placed four ways:
+one-shot, fused two-stage, ubatch and fused recursive-doubling kernels, and
+of the fp8 quantise and fp8 reduces, on the bench workload (P = 8, bf16
+[16384 x 8192] per rank, N(0,1)) with the buffers placed four ways:
 
 * ``separate`` -- one allocation per buffer (as bench.py allocates them);
 * ``pow2``     -- one allocation, buffer p at p * (buffer size): a
@@ -14,13 +14,16 @@ buffers placed four ways:
 * ``half``     -- the first half of P buffers twice as large (the shape of a
   ubatch split: each ubatch's rows are a part of a larger tensor).
 
-Outputs are placed the same way as inputs.  Each shape is set with
+Outputs are placed the same way as inputs (fp8 codes and scale bytes
+too).  Each shape is set with
 ar_set_launch_shape and timed with HIP events around `reps` back-to-back
 calls, in a shuffled order per round; the median over rounds is reported per
 placement, with the minimum and the mean over placements.  GB/s counts each
-input read once and each output written once (payload words for RD).
+input read once and each output written once (payload words for RD; codes
+and scale bytes for fp8).
 
-Usage: python -m tensor_all_reduce_amd.placement [--kinds oneshot,2stage,rd,ubatch] [--rounds 3]
+Usage: python -m tensor_all_reduce_amd.placement [--kinds oneshot,2stage,rd,ubatch,quant,fp8r1,fp8rp]
+       [--rounds 3]
 """
 from __future__ import annotations
 
@@ -36,7 +39,9 @@ import tensor_all_reduce_amd as tar
 P, ROWS, HIDDEN = 8, 16384, 8192
 PLACEMENTS = ("separate", "pow2", "skew", "half")
 KINDS = {"oneshot": tar.AR_KERNEL_ONESHOT, "2stage": tar.AR_KERNEL_2STAGE, "ubatch": tar.AR_KERNEL_UBATCH,
-         "rd": tar.AR_KERNEL_RD}
+         "rd": tar.AR_KERNEL_RD, "quant": tar.AR_KERNEL_QUANT_FP8, "fp8r1": tar.AR_KERNEL_REDUCE_FP8,
+         "fp8rp": tar.AR_KERNEL_REDUCE_FP8_ALL}
+FP8_KINDS = ("quant", "fp8r1", "fp8rp")
 # (block, vec, nt_loads, nt_stores, wg_per_cu): the leaders of the single-placement sweeps
 SHAPES = {
     "oneshot": [(256, 1, 1, 1, 2), (64, 1, 1, 1, 8), (64, 1, 1, 0, 16), (64, 1, 1, 0, 8), (64, 1, 1, 1, 16),
@@ -47,6 +52,12 @@ SHAPES = {
                (64, 1, 1, 1, 5)],
     "rd": [(64, 1, 1, 1, 8), (64, 1, 1, 1, 6), (64, 1, 1, 1, 10), (64, 1, 1, 1, 5), (64, 1, 0, 1, 8),
            (128, 1, 1, 1, 4)],
+    "quant": [(64, 2, 1, 1, 0), (64, 1, 1, 1, 0), (128, 2, 1, 1, 0), (256, 1, 1, 1, 0), (64, 2, 1, 0, 0),
+              (64, 2, 0, 1, 0), (64, 2, 1, 1, 8), (64, 2, 1, 1, 4), (128, 1, 1, 1, 4)],
+    "fp8r1": [(128, 1, 1, 1, 8), (64, 1, 1, 1, 8), (128, 2, 1, 1, 8), (128, 1, 1, 1, 4), (256, 1, 1, 1, 4),
+              (128, 1, 1, 0, 8), (128, 1, 1, 1, 0)],
+    "fp8rp": [(128, 1, 1, 1, 6), (64, 1, 1, 1, 6), (128, 1, 1, 1, 4), (128, 1, 1, 1, 8), (256, 1, 1, 1, 3),
+              (128, 2, 1, 1, 6), (128, 1, 1, 1, 0)],
 }
 
 
@@ -130,7 +141,16 @@ def main(argv=None):
         fns = {"oneshot": ((P + 1) * 2 * n, lambda: tar.ar_reduce_oneshot(ins, outs[0])),
                "2stage": (2 * P * 2 * n, lambda: tar.ar_reduce_2stage(ins, outs)),
                "ubatch": (2 * P * 2 * n, ubatch)}
-        sweep(fns, [k for k in kinds if k != "rd"], args.rounds, args.reps, how, res, rng)
+        sweep(fns, [k for k in kinds if k in fns], args.rounds, args.reps, how, res, rng)
+        if any(k in FP8_KINDS for k in kinds):
+            nb = tar.fp8_scale_count(n)
+            codes, scales = place(torch.uint8, n, how, dev), place(torch.uint8, nb, how, dev)
+            tar.ar_quantize_fp8(ins, codes, scales)
+            fp8_fns = {"quant": (P * (3 * n + nb), lambda: tar.ar_quantize_fp8(ins, codes, scales)),
+                       "fp8r1": (P * (n + nb) + 2 * n, lambda: tar.ar_reduce_fp8(codes, scales, outs[:1])),
+                       "fp8rp": (P * (n + nb) + P * 2 * n, lambda: tar.ar_reduce_fp8(codes, scales, outs))}
+            sweep(fp8_fns, [k for k in kinds if k in FP8_KINDS], args.rounds, args.reps, how, res, rng)
+            del codes, scales
         del outs
         torch.cuda.empty_cache()
         if "rd" in kinds:
