@@ -54,7 +54,7 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few store waits and counter atomics per chunk
     {64, 2, 1, 1, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
     {128, 1, 1, 1, 8, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)
-    {128, 1, 1, 1, 6, 0},   // fp8 reduce, P code streams -> P outputs
+    {128, 1, 1, 1, 5, 0},   // fp8 reduce, P code streams -> P outputs
     {128, 1, 0, 1, 0, 0},   // one-shot, n <= AR_SMALL_ELEMS: uncapped, plain loads
     {128, 1, 0, 1, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
     {64, 1, 0, 1, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
