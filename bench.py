@@ -21,8 +21,9 @@ two-stage at 128 KiB / 512 KiB / 2 MiB per buffer (native timing loop, no
 Python in the loop), the staged two-stage at the prefill size, the ubatch
 reduce at its own [16384 x 16384] shape, the waiting unpack (on ready payloads
 and as a producer -> consumer handoff), attainable copy bandwidth (a plain
-copy, and eight buffers copied side by side: the 8 -> 8 pattern of the
-two-stage, RD and ubatch rows, for the ubatch split over two streams), and
+copy; eight buffers copied side by side: the 8 -> 8 pattern of the
+two-stage, RD and ubatch rows, for the ubatch split over two streams; and
+eight buffers gathered into one by XOR: the one-shot's 8 -> 1 pattern), and
 the CPU oracle on a bounded sample of the same step (`cpu_baseline`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -134,6 +135,9 @@ def main():
                                     ctypes.c_size_t, vp, ctypes.c_int, vp]
     blib.arb_copy.restype = ctypes.c_int
     blib.arb_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    blib.arb_gather_xor.restype = ctypes.c_int
+    blib.arb_gather_xor.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    vp]
     blib.arb_copy_multi.restype = ctypes.c_int
     blib.arb_copy_multi.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t,
                                     ctypes.c_int, ctypes.c_int, vp]
@@ -299,9 +303,10 @@ def main():
         # the same rates against the attainable bandwidth measured in this run
         for r in rows:
             per_row[r]["frac_of_copy"] = round(per_row[r]["GBps"] / result["copy_GBps"], 4)
-        # the rows with the 8 -> 8 access pattern, against a plain copy with the
-        # same pattern: one stream over whole buffers, or two over the halves
-        for r, ref in (("2stage", "copy_8to8_GBps"), ("rd", "copy_8to8_GBps"),
+        # the one-shot, two-stage, RD and ubatch rows against a plain copy with
+        # the same access pattern: 8 -> 1 for the one-shot; 8 -> 8 on one
+        # stream over whole buffers, or on two over the halves, for the others
+        for r, ref in (("oneshot", "copy_8to1_GBps"), ("2stage", "copy_8to8_GBps"), ("rd", "copy_8to8_GBps"),
                        ("ubatch", "copy_8to8_two_streams_GBps")):
             per_row[r]["frac_of_pattern_copy"] = round(per_row[r]["GBps"] / result[ref], 4)
         roofline["frac_of_copy"] = round(achieved / result["copy_GBps"], 4)
@@ -374,6 +379,26 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
                 best8, shape8 = gbps, {"vec": vec, "wg_per_cu": wg}
     res["copy_8to8_GBps"] = round(best8, 1)
     res["copy_8to8_shape"] = shape8
+    # the one-shot row's pattern: eight 256 MiB buffers read, their XOR
+    # written to one output (the one-shot's tiling, no float arithmetic),
+    # best over store kind and the workgroups-per-CU cap
+    best1, shape1 = 0.0, None
+    for nts in (0, 1):
+        for wg in (0, 4, 8, 12, 16):
+            for _ in range(2):
+                if blib.arb_gather_xor(parr(ins), P, out1.data_ptr(), 2 * n, nts, wg, sh) != 0:
+                    raise RuntimeError("arb_gather_xor failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main_s)
+            for _ in range(8):
+                blib.arb_gather_xor(parr(ins), P, out1.data_ptr(), 2 * n, nts, wg, sh)
+            e1.record(main_s)
+            torch.cuda.synchronize()
+            gbps = (P + 1) * 2 * n * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if gbps > best1:
+                best1, shape1 = gbps, {"nt_stores": nts, "wg_per_cu": wg}
+    res["copy_8to1_GBps"] = round(best1, 1)
+    res["copy_8to1_shape"] = shape1
     # the ubatch row's pattern: the same copy split at the middle row, the two
     # halves on two streams at once (as the two ubatch reduces run), on the
     # ubatch streams themselves: HIP maps a process's streams onto a few

@@ -55,6 +55,23 @@ __global__ __launch_bounds__(64) void k_copy_multi(MultiPtrs m, size_t nvec) {
   }
 }
 
+// The one-shot's access pattern without its arithmetic: N buffers read
+// (non-temporal loads), their XOR written to one output, with the one-shot's
+// tiling (64-lane workgroups, 1 KiB of every buffer each).
+template <int N, bool NTS>
+__global__ __launch_bounds__(64) void k_gather_xor(MultiPtrs m, size_t nvec) {
+  const size_t v = (size_t)blockIdx.x * 64 + threadIdx.x;
+  if (v >= nvec) return;
+  u32x4 a[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) a[j] = __builtin_nontemporal_load(m.in[j] + v);
+  u32x4 r = a[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) r ^= a[j];
+  if constexpr (NTS) __builtin_nontemporal_store(r, m.out[0] + v);
+  else m.out[0][v] = r;
+}
+
 // Consumer of a flagged chunked reduce.  Persistent grid (no LDS request,
 // at most two workgroups per CU, so the producer's workgroups always fit
 // beside it: a waiting grid that filled every wave slot would keep them
@@ -670,6 +687,47 @@ int arb_copy_multi(const void* const* ins, void* const* outs, int N, size_t byte
   ARB_COPY_MULTI(4)
   ARB_COPY_MULTI(8)
 #undef ARB_COPY_MULTI
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+// N -> 1 gather (N in {2, 4, 8}): out = XOR of the N inputs, `bytes` per
+// buffer (a multiple of 16; 16-byte aligned buffers), non-temporal stores
+// when nts != 0, at most wg_per_cu workgroups per CU (0: no cap).  The
+// output must not overlap an input.
+int arb_gather_xor(const void* const* ins, int N, void* out, size_t bytes, int nts, int wg_per_cu,
+                   void* stream) {
+  if (!ins || !out || (N != 2 && N != 4 && N != 8) || (bytes & 15u) || bytes == 0 || wg_per_cu < 0)
+    return AR_ERR_INVALID;
+  MultiPtrs m{};
+  for (int j = 0; j < N; ++j) {
+    if (!ins[j]) return AR_ERR_INVALID;
+    m.in[j] = static_cast<const u32x4*>(ins[j]);
+  }
+  m.out[0] = static_cast<u32x4*>(out);
+  unsigned lds = 0;
+  if (wg_per_cu > 0) {
+    int dev = 0, per_cu = 0, per_block = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return AR_ERR_HIP;
+    lds = ((unsigned)per_cu / (unsigned)wg_per_cu) & ~255u;
+    if (lds > (unsigned)per_block) lds = (unsigned)per_block;
+  }
+  const size_t nvec = bytes / 16;
+  const size_t grid = (nvec + 63) / 64;
+  if (grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 g((unsigned)grid), b(64);
+#define ARB_GATHER(NN)                                                               \
+  if (N == NN) {                                                                     \
+    if (nts) hipLaunchKernelGGL((k_gather_xor<NN, true>), g, b, lds, st, m, nvec);   \
+    else hipLaunchKernelGGL((k_gather_xor<NN, false>), g, b, lds, st, m, nvec);      \
+  }
+  ARB_GATHER(2)
+  ARB_GATHER(4)
+  ARB_GATHER(8)
+#undef ARB_GATHER
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
