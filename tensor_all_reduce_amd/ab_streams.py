@@ -3,8 +3,11 @@ copied side by side into N others (out[j] = in[j], no arithmetic; the bench
 library's arb_copy_multi) for N = 1, 2, 4 and 8, 4 GiB moved per call
 whatever N, uncapped and at several workgroups-per-CU caps.  The 8 -> 8 case
 is the access pattern of the fused two-stage and recursive-doubling kernels;
-the 1 -> 1 case is a plain copy.  Prints GB/s per case (medians of
-interleaved rounds).
+the 1 -> 1 case is a plain copy.  Then the one-shot's 8 -> 1 pattern: eight
+256 MiB buffers gathered into one by XOR (the bench library's
+arb_gather_xor: the one-shot's tiling, no float work) over store kind and
+cap, with the library's one-shot on the same buffers beside it.  Prints GB/s
+per case (medians of interleaved rounds).
 
 Usage:
   python -m tensor_all_reduce_amd.ab_streams [--rounds 3]
@@ -35,6 +38,9 @@ def main(argv=None):
     blib.arb_copy_multi.restype = ctypes.c_int
     blib.arb_copy_multi.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t,
                                     ctypes.c_int, ctypes.c_int, vp]
+    blib.arb_gather_xor.restype = ctypes.c_int
+    blib.arb_gather_xor.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    vp]
     dev = torch.device("cuda:0")
     total = 4 << 30                                  # bytes moved per call (read + write)
     s = torch.cuda.current_stream()
@@ -72,6 +78,39 @@ def main(argv=None):
     print("all cases (GB/s, median):")
     for c in cases:
         print(f"  {c[0]} -> {c[0]}  vec {c[1]}  wg/cu {c[2]:2d}  {statistics.median(res[c]):7.1f}")
+    del bufs
+    torch.cuda.empty_cache()
+    # 8 -> 1: the one-shot's pattern, P = 8 buffers of bf16 [16384 x 8192]
+    P, n = 8, 16384 * 8192
+    ins = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(P)]
+    for j, t in enumerate(ins):
+        t.fill_(j + 1)
+    out = torch.empty(n, dtype=torch.int16, device=dev)
+    ip = (vp * P)(*[t.data_ptr() for t in ins])
+    moved = (P + 1) * 2 * n
+    gcases = [("gather", nts, wg) for nts in (0, 1) for wg in (0, 4, 8, 12, 16)] + [("one-shot", None, None)]
+    gres = {c: [] for c in gcases}
+    for _ in range(a.rounds):
+        for c in gcases:
+            if c[0] == "gather":
+                def f(c=c):
+                    if blib.arb_gather_xor(ip, P, out.data_ptr(), 2 * n, c[1], c[2], s.cuda_stream) != 0:
+                        raise RuntimeError("arb_gather_xor failed")
+            else:
+                def f():
+                    tar.ar_reduce_oneshot(ins, out)
+            f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(5):
+                f()
+            e1.record(s)
+            e1.synchronize()
+            gres[c].append(moved / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9)
+    print(f"8 -> 1 (GB/s, median; one-shot shape {tuple(tar.ar_get_launch_shape(tar.AR_KERNEL_ONESHOT))}):")
+    for c in gcases:
+        name = "library one-shot" if c[0] == "one-shot" else f"gather  nt_stores {c[1]}  wg/cu {c[2]:2d}"
+        print(f"  {name:34s} {statistics.median(gres[c]):7.1f}", flush=True)
     return 0
 
 
