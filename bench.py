@@ -564,6 +564,52 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     e = derr.cpu().tolist()
     if e[0] != 0:
         raise RuntimeError(f"decode chain saw {e[0]} bad sequence numbers")
+    # the whole chain captured in a HIP graph (20 chains per graph, every
+    # chain packs with seq0 = 1, so each replay checks its own sequence
+    # numbers): the chain's GPU time without the 2P + 2 host launches
+    gside = torch.cuda.Stream()
+    gside.wait_stream(main_s)
+
+    def chain(st, staged):
+        for p in range(P):
+            tar.ar_pack_fused(xi[p], win[p], 1, stream=st)
+        tar.ar_err_init(derr, stream=st)
+        if staged:
+            tar.ar_rd_schedule(win, wout, 1, derr, mailbox=mbox, flags=tar.AR_RD_STAGED, stream=st)
+        else:
+            tar.ar_rd_schedule(win, wout, 1, derr, stream=st)
+        for p in range(P):
+            tar.ar_unpack_fused(wout[p], yo[p], 1 + 3, derr, stream=st)
+
+    for name, staged in (("chain_fused_R1", False), ("chain_staged_R1", True)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gside):
+            chain(gside, staged)
+            gside.synchronize()
+            ref = [y.clone() for y in yo]
+            with torch.cuda.graph(g, stream=gside):
+                for _ in range(20):
+                    chain(gside, staged)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for y in yo:
+                y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(y, r) for y, r in zip(yo, ref)):
+                raise RuntimeError(f"{name}: a graph replay differs from the eager chain")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(main_s)
+        for _ in range(10):
+            g.replay()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        dec[name]["hip_graph_us"] = round(e0.elapsed_time(e1) * 1e3 / 200, 2)
+        bad = int(derr[0].item())
+        if bad or not all(torch.equal(y, r) for y, r in zip(yo, ref)):
+            raise RuntimeError(f"{name}: the graph's last chain saw {bad} bad sequence numbers or wrong data")
+        del g, ref
     res["decode_fused_payload_128x8192"] = dec
     del win, wout, mbox
     log("decode chain measured")

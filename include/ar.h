@@ -210,11 +210,12 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
  * optional non-temporal loads/stores and at most `wg_per_cu` workgroups per
  * compute unit (0 = no cap; enforced by requesting unused LDS).  `vec` (1 or
  * 2) sets how much each lane handles:
- *   ONESHOT, 2STAGE, UBATCH, UBATCH_FLAGS, RD, QUANT_FP8 and the _SMALL
+ *   ONESHOT, 2STAGE, UBATCH, UBATCH_FLAGS, RD, QUANT_FP8 and their _SMALL
  *     kinds: vec 16-byte groups per buffer, each a contiguous span across
  *     the wavefront;
- *   PACK, UNPACK: 1 -> 8 bytes of bf16 (one 16-byte payload access) per
- *     lane, 2 -> 16 bytes of bf16 (two adjacent payload accesses);
+ *   PACK, UNPACK and their _SMALL kinds: 1 -> 8 bytes of bf16 (one 16-byte
+ *     payload access) per lane, 2 -> 16 bytes of bf16 (two adjacent payload
+ *     accesses);
  *   REDUCE_FP8, REDUCE_FP8_ALL: 1 -> 8 elements (one 16-byte store per
  *     output) per lane, 2 -> 16 elements;
  *   RS, AG, RDSTEP, UNPACK_WAIT: ignored.
@@ -222,10 +223,11 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
  * to launches made after the call, process-wide; the call is thread-safe.
  * Returns AR_ERR_INVALID for an unknown kind or out-of-range field.
  *
- * The one-shot, fused two-stage, fused recursive-doubling and staged
- * recursive-doubling-step kernels have a second kind each (..._SMALL) whose
- * shape applies when a call's element count n is at most AR_SMALL_ELEMS
- * (4 MiB of bf16 per rank: the decode messages).  Such a call moves too
+ * The one-shot, fused two-stage, fused recursive-doubling, staged
+ * recursive-doubling-step, pack and unpack kernels have a second kind each
+ * (..._SMALL) whose shape applies when a call's element count n is at most
+ * AR_SMALL_ELEMS (4 MiB of bf16 per rank: the decode messages).  Such a
+ * call moves too
  * little data for the occupancy cap that helps long streams; its time is
  * launch, one memory round trip and the number of workgroup rounds, so its
  * default is uncapped with plain loads, which also keep data that is already
@@ -252,6 +254,8 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 #define AR_KERNEL_2STAGE_SMALL 15  /* ar_reduce_2stage fused, n <= AR_SMALL_ELEMS */
 #define AR_KERNEL_RD_SMALL 16      /* ar_rd_schedule fused, n <= AR_SMALL_ELEMS */
 #define AR_KERNEL_RDSTEP_SMALL 17  /* ar_rd_schedule staged, n <= AR_SMALL_ELEMS */
+#define AR_KERNEL_PACK_SMALL 18    /* ar_pack_fused, n <= AR_SMALL_ELEMS        */
+#define AR_KERNEL_UNPACK_SMALL 19  /* ar_unpack_fused, n <= AR_SMALL_ELEMS      */
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu);
 int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
                         int* wg_per_cu);

@@ -29,6 +29,7 @@ __all__ = [
     "AR_KERNEL_UBATCH_FLAGS", "ar_unpack_fused_wait", "ar_reduce_ubatch_flags", "ubatch_chunk_count",
     "AR_KERNEL_QUANT_FP8", "AR_KERNEL_REDUCE_FP8", "AR_KERNEL_REDUCE_FP8_ALL", "ar_quantize_fp8", "ar_reduce_fp8", "fp8_scale_count",
     "AR_KERNEL_ONESHOT_SMALL", "AR_KERNEL_2STAGE_SMALL", "AR_KERNEL_RD_SMALL", "AR_KERNEL_RDSTEP_SMALL",
+    "AR_KERNEL_PACK_SMALL", "AR_KERNEL_UNPACK_SMALL",
     "AR_SMALL_ELEMS",
     "FP8_BLOCK",
 ]
@@ -62,6 +63,8 @@ AR_KERNEL_ONESHOT_SMALL = 14
 AR_KERNEL_2STAGE_SMALL = 15
 AR_KERNEL_RD_SMALL = 16
 AR_KERNEL_RDSTEP_SMALL = 17
+AR_KERNEL_PACK_SMALL = 18
+AR_KERNEL_UNPACK_SMALL = 19
 AR_SMALL_ELEMS = 2097152
 FP8_BLOCK = 32                  # elements per power-of-two scale
 

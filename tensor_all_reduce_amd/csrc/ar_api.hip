@@ -40,7 +40,7 @@ struct DevInfo {
 // from one allocation, or halves of larger tensors), the pick is the shape
 // with the best worst case over placements, within 1% of the best for
 // separately allocated buffers.
-constexpr ar::Shape kDefaultShape[ar::kKinds] = {
+constexpr ar::Shape kDefaultShape[] = {
     {64, 1, 1, 1, 8, 0},    // one-shot, 8 -> 1
     {64, 1, 1, 1, 6, 0},    // fused two-stage, 8 -> 8
     {64, 1, 1, 1, 6, 0},    // ubatch, 8 -> 8 on two streams
@@ -59,12 +59,30 @@ constexpr ar::Shape kDefaultShape[ar::kKinds] = {
     {128, 1, 0, 1, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
     {64, 1, 0, 1, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
     {64, 1, 0, 0, 0, 0},    // staged RD step, n <= AR_SMALL_ELEMS: plain stores keep the mailbox on chip
+    {256, 1, 0, 1, 0, 0},   // pack, n <= AR_SMALL_ELEMS: plain loads, uncapped
+    {256, 1, 0, 1, 0, 0},   // unpack, n <= AR_SMALL_ELEMS
 };
-constexpr const char* kShapeEnv[ar::kKinds] = {
+constexpr const char* kShapeEnv[] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
     "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT",
     "AR_SHAPE_UBATCH_FLAGS", "AR_SHAPE_QUANT_FP8", "AR_SHAPE_REDUCE_FP8", "AR_SHAPE_REDUCE_FP8_ALL",
-    "AR_SHAPE_ONESHOT_SMALL", "AR_SHAPE_2STAGE_SMALL", "AR_SHAPE_RD_SMALL", "AR_SHAPE_RDSTEP_SMALL"};
+    "AR_SHAPE_ONESHOT_SMALL", "AR_SHAPE_2STAGE_SMALL", "AR_SHAPE_RD_SMALL", "AR_SHAPE_RDSTEP_SMALL",
+    "AR_SHAPE_PACK_SMALL", "AR_SHAPE_UNPACK_SMALL"};
+// one default and one override name per kind, in the order of ar.h's kind
+// numbers
+static_assert(sizeof(kDefaultShape) / sizeof(kDefaultShape[0]) == ar::kKinds, "a default shape per kind");
+static_assert(sizeof(kShapeEnv) / sizeof(kShapeEnv[0]) == ar::kKinds, "an override name per kind");
+static_assert(ar::kOneshot == AR_KERNEL_ONESHOT && ar::k2Stage == AR_KERNEL_2STAGE &&
+                  ar::kUbatch == AR_KERNEL_UBATCH && ar::kRS == AR_KERNEL_RS && ar::kAG == AR_KERNEL_AG &&
+                  ar::kPack == AR_KERNEL_PACK && ar::kUnpack == AR_KERNEL_UNPACK && ar::kRD == AR_KERNEL_RD &&
+                  ar::kRDStep == AR_KERNEL_RDSTEP && ar::kUnpackWait == AR_KERNEL_UNPACK_WAIT &&
+                  ar::kUbatchFlags == AR_KERNEL_UBATCH_FLAGS && ar::kQuantFp8 == AR_KERNEL_QUANT_FP8 &&
+                  ar::kReduceFp8 == AR_KERNEL_REDUCE_FP8 && ar::kReduceFp8All == AR_KERNEL_REDUCE_FP8_ALL &&
+                  ar::kOneshotSmall == AR_KERNEL_ONESHOT_SMALL && ar::k2StageSmall == AR_KERNEL_2STAGE_SMALL &&
+                  ar::kRDSmall == AR_KERNEL_RD_SMALL && ar::kRDStepSmall == AR_KERNEL_RDSTEP_SMALL &&
+                  ar::kPackSmall == AR_KERNEL_PACK_SMALL && ar::kUnpackSmall == AR_KERNEL_UNPACK_SMALL &&
+                  ar::kKinds == AR_KERNEL_UNPACK_SMALL + 1,
+              "kind numbers match ar.h");
 
 std::mutex g_mu;
 DevInfo g_dev[kMaxDevices];

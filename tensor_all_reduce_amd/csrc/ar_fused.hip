@@ -448,14 +448,14 @@ hipError_t unpack_w(const Shape& sh, hipStream_t st, const uint64_t* w, void* x,
 // For pack and unpack the shape's vec counts 16-byte groups of bf16 per lane:
 // 1 -> 2 data words (8 bytes) per lane, 2 -> 4 data words (16 bytes).
 hipError_t launch_pack(const Launch& L, const void* x, uint64_t* w, size_t n, uint32_t seq) {
-  const Shape& sh = L.shape[kPack];
+  const Shape& sh = shape_for(L, kPack, kPackSmall, n);
   if (sh.vec == 2) return pack_w<4>(sh, L.stream, x, w, n, seq);
   return pack_w<2>(sh, L.stream, x, w, n, seq);
 }
 
 hipError_t launch_unpack(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,
                          uint64_t* d_err) {
-  const Shape& sh = L.shape[kUnpack];
+  const Shape& sh = shape_for(L, kUnpack, kUnpackSmall, n);
   if (sh.vec == 2) return unpack_w<4>(sh, L.stream, w, x, n, seq, d_err);
   return unpack_w<2>(sh, L.stream, w, x, n, seq, d_err);
 }

@@ -47,6 +47,8 @@ enum Kind {
   k2StageSmall,  // k2Stage for n <= AR_SMALL_ELEMS
   kRDSmall,      // kRD for n <= AR_SMALL_ELEMS
   kRDStepSmall,  // kRDStep for n <= AR_SMALL_ELEMS
+  kPackSmall,    // kPack for n <= AR_SMALL_ELEMS
+  kUnpackSmall,  // kUnpack for n <= AR_SMALL_ELEMS
   kKinds
 };
 

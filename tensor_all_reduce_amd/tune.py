@@ -12,11 +12,12 @@ drift of the device affects all candidates alike.  GB/s counts each input
 read once and each output written once.
 
 With --decode, the small-message kinds (one-shot, fused two-stage, fused
-recursive doubling and the staged recursive-doubling step, for
-n <= AR_SMALL_ELEMS) are instead timed at the decode
-sizes (P = 8, [T x 8192] for T = 8, 32, 128: 128 KiB to 2 MiB per buffer) as
-per-call stream time over back-to-back calls from the native timing loops in
-libarbench.so, so no Python runs between calls.
+recursive doubling, the staged recursive-doubling step, pack and unpack, for
+n <= AR_SMALL_ELEMS) are instead timed at the decode sizes (P = 8, [T x 8192]
+for T = 8, 32, 128: 128 KiB to 2 MiB per buffer) as per-call time inside a
+HIP graph (50 calls captured, replayed): at these sizes back-to-back eager
+calls are bound by the host's launch cost, which would hide the kernels'
+differences.
 
 With --crossover, the current large-message and small-message default shapes
 of those three kernels are both timed at sizes from 128 KiB to 64 MiB per
@@ -24,7 +25,7 @@ buffer, hot (one buffer set, repeated) and cold (rotating over >= 4 GiB; the
 one-shot and two-stage only), the evidence for the AR_SMALL_ELEMS threshold.
 
 Usage: python -m tensor_all_reduce_amd.tune [--kinds 2stage,rd] [--rounds 3] [--reps 4]
-       python -m tensor_all_reduce_amd.tune --decode
+       python -m tensor_all_reduce_amd.tune --decode [--kinds pack,unpack]
        python -m tensor_all_reduce_amd.tune --crossover
 """
 from __future__ import annotations
@@ -61,7 +62,9 @@ def candidates(kind: str):
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--kinds", default="oneshot,2stage,ubatch,pack,unpack,rd")
+    ap.add_argument("--kinds", default=None,
+                    help="kinds to sweep (default oneshot,2stage,ubatch,pack,unpack,rd; with --decode, "
+                         "any of oneshot,2stage,rd,rdstep,pack,unpack, default all)")
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--reps", type=int, default=4)
     ap.add_argument("--top", type=int, default=8)
@@ -69,6 +72,9 @@ def main(argv=None):
     ap.add_argument("--crossover", action="store_true",
                     help="time the large- and small-message default shapes across sizes")
     args = ap.parse_args(argv)
+    args.kinds_given = args.kinds is not None
+    if args.kinds is None:
+        args.kinds = "oneshot,2stage,ubatch,pack,unpack,rd"
     if args.decode:
         return decode(args)
     if args.crossover:
@@ -209,11 +215,33 @@ def _check_us(us, what):
     return us
 
 
+def _graph_us(body, per_graph: int = 50, replays: int = 8) -> float:
+    """Per-call GPU time of body(stream): `per_graph` calls captured in one
+    HIP graph, replayed `replays` times (after one untimed replay)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        body(side)
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(per_graph):
+                body(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * per_graph)
+
+
 def decode(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    blib, vp = _bench_lib()
-    sh = torch.cuda.current_stream().cuda_stream
     rng = random.Random(11)
     mmax = 128 * HIDDEN
     ins = [t.view(torch.int16) for t in synth.device_rank_buffers("normal", P, mmax, 2, dev)]
@@ -222,26 +250,35 @@ def decode(args):
     words = [torch.empty(mmax // 2, dtype=torch.int64, device=dev) for _ in range(P)]
     rdo = [torch.empty(mmax // 2, dtype=torch.int64, device=dev) for _ in range(P)]
     err = torch.empty(2, dtype=torch.int64, device=dev)
-    for r in range(P):
-        tar.ar_pack_fused(ins[r], words[r], 1)
     tar.ar_err_init(err)
-    ia = (vp * P)(*[t.data_ptr() for t in ins])
-    oa = (vp * P)(*[t.data_ptr() for t in outs])
-    wa = (vp * P)(*[t.data_ptr() for t in words])
-    ra = (vp * P)(*[t.data_ptr() for t in rdo])
     cands = list(itertools.product((64, 128, 256), (1, 2), (0, 1), (0, 1), (0, 4, 8)))
+    only = set(args.kinds.split(",")) if args.kinds_given else None
+    totals = {}          # name -> {shape: summed per-call us over the decode sizes}
     for T in (8, 32, 128):
         m = T * HIDDEN
-        for name, k, fn in (
-                ("oneshot", tar.AR_KERNEL_ONESHOT_SMALL,
-                 lambda: blib.arb_stream_us(0, ia, oa, P, m, None, 2000, sh)),
-                ("2stage", tar.AR_KERNEL_2STAGE_SMALL,
-                 lambda: blib.arb_stream_us(1, ia, oa, P, m, None, 2000, sh)),
-                ("rd", tar.AR_KERNEL_RD_SMALL,
-                 lambda: blib.arb_decode_us(None, None, wa, ra, P, m, None, 0, err.data_ptr(), 0, 1000, sh)),
+        xi, xo = [x[:m] for x in ins], [o[:m] for o in outs]
+        wi, wo = [w[:m // 2] for w in words], [w[:m // 2] for w in rdo]
+        for p in range(P):
+            tar.ar_pack_fused(xi[p], wi[p], 1)
+
+        def pack_all(st):
+            for p in range(P):
+                tar.ar_pack_fused(xi[p], wi[p], 1, stream=st)
+
+        def unpack_all(st):
+            for p in range(P):
+                tar.ar_unpack_fused(wi[p], xo[p], 1, err, stream=st)
+        # (name, kind, body, calls per body)
+        for name, k, body, per in (
+                ("oneshot", tar.AR_KERNEL_ONESHOT_SMALL, lambda st: tar.ar_reduce_oneshot(xi, xo[0], stream=st), 1),
+                ("2stage", tar.AR_KERNEL_2STAGE_SMALL, lambda st: tar.ar_reduce_2stage(xi, xo, stream=st), 1),
+                ("rd", tar.AR_KERNEL_RD_SMALL, lambda st: tar.ar_rd_schedule(wi, wo, 1, err, stream=st), 1),
                 ("rdstep", tar.AR_KERNEL_RDSTEP_SMALL,
-                 lambda: blib.arb_decode_us(None, None, wa, ra, P, m, mbox.data_ptr(), tar.AR_RD_STAGED,
-                                            err.data_ptr(), 0, 300, sh))):
+                 lambda st: tar.ar_rd_schedule(wi, wo, 1, err, mailbox=mbox, flags=tar.AR_RD_STAGED, stream=st), 1),
+                ("pack", tar.AR_KERNEL_PACK_SMALL, pack_all, P),
+                ("unpack", tar.AR_KERNEL_UNPACK_SMALL, unpack_all, P)):
+            if only is not None and name not in only:
+                continue
             default = tar.ar_get_launch_shape(k)
             cs = cands + ([default] if default not in cands else [])
             times = {c: [] for c in cs}
@@ -250,22 +287,36 @@ def decode(args):
                 rng.shuffle(order)
                 for c in order:
                     tar.ar_set_launch_shape(k, *c)
-                    times[c].append(_check_us(fn(), name))
-            tar.ar_set_launch_shape(k, *default)
+                    try:
+                        times[c].append(_graph_us(body, per_graph=max(1, 50 // per)) / per)
+                    finally:
+                        tar.ar_set_launch_shape(k, *default)
             med = {c: statistics.median(v) for c, v in times.items()}
+            tot = totals.setdefault(name, {"default": default})
+            for c, v in med.items():
+                tot[c] = tot.get(c, 0.0) + v
             ranked = sorted(cs, key=lambda c: med[c])
             what = (f"{4 * m // 1024} KiB of payload per rank" if name.startswith("rd")
                     else f"{2 * m // 1024} KiB per buffer")
-            print(f"== {name} (small-message kind) T={T} ({what}): per-call stream time")
+            print(f"== {name} (small-message kind) T={T} ({what}): per-call time in a HIP graph")
             print("   rank  block vec ntl nts wg/cu      us")
             for i, c in enumerate(ranked):
                 if i < args.top or c == default:
                     tag = "  <- default" if c == default else ""
                     print(f"   {i + 1:4d}  {c[0]:5d} {c[1]:3d} {c[2]:3d} {c[3]:3d} {c[4]:5d} {med[c]:7.2f}{tag}")
             sys.stdout.flush()
+    for name, tot in totals.items():
+        default = tot.pop("default")
+        ranked = sorted(tot, key=lambda c: tot[c])
+        print(f"== {name} (small-message kind): summed per-call time over 128 KiB, 512 KiB and 2 MiB")
+        print("   rank  block vec ntl nts wg/cu      us")
+        for i, c in enumerate(ranked):
+            if i < args.top or c == default:
+                tag = "  <- default" if c == default else ""
+                print(f"   {i + 1:4d}  {c[0]:5d} {c[1]:3d} {c[2]:3d} {c[3]:3d} {c[4]:5d} {tot[c]:7.2f}{tag}")
     torch.cuda.synchronize()
     if err.cpu().tolist()[0]:
-        raise RuntimeError("recursive doubling saw bad sequence numbers")
+        raise RuntimeError("recursive doubling or unpack saw bad sequence numbers")
     return 0
 
 

@@ -239,13 +239,13 @@ def test_binding_raises_on_error():
 
 def test_launch_shape_roundtrip_and_validation():
     L = tar.lib()
-    for kind in range(18):
+    for kind in range(20):
         before = tar.ar_get_launch_shape(kind)
         tar.ar_set_launch_shape(kind, 128, 2, 0, 1, 7)
         assert tar.ar_get_launch_shape(kind) == (128, 2, 0, 1, 7)
         tar.ar_set_launch_shape(kind, *before)
         assert tar.ar_get_launch_shape(kind) == before
-    assert L.ar_set_launch_shape(18, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(20, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 96, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 3, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 1, 2, 1, 0) == tar.AR_ERR_INVALID

@@ -5,10 +5,10 @@ non-temporal loads / stores, workgroups per CU); each choice is a different
 kernel instantiation or grid.  Here each kind is run under a grid of shapes
 on ragged sizes (tails inside a 16-byte group and inside a tile) and every
 result is compared with the oracle, bit for bit; the default shape is
-restored afterwards.  The one-shot, fused two-stage, fused RD and staged RD
-calls pick their small-message kind at n <= AR_SMALL_ELEMS and their
-large-message kind above it, so those run at one size on each side of the
-threshold.
+restored afterwards.  The one-shot, fused two-stage, fused RD, staged RD,
+pack and unpack calls pick their small-message kind at n <= AR_SMALL_ELEMS
+and their large-message kind above it, so those run at one size on each side
+of the threshold.
 """
 import functools
 import itertools
@@ -62,6 +62,8 @@ ONESHOT_KINDS = (tar.AR_KERNEL_ONESHOT, tar.AR_KERNEL_ONESHOT_SMALL)
 TWOSTAGE_KINDS = (tar.AR_KERNEL_2STAGE, tar.AR_KERNEL_2STAGE_SMALL)
 RD_KINDS = (tar.AR_KERNEL_RD, tar.AR_KERNEL_RD_SMALL)
 RDSTEP_KINDS = (tar.AR_KERNEL_RDSTEP, tar.AR_KERNEL_RDSTEP_SMALL)
+PACK_KINDS = (tar.AR_KERNEL_PACK, tar.AR_KERNEL_PACK_SMALL)
+UNPACK_KINDS = (tar.AR_KERNEL_UNPACK, tar.AR_KERNEL_UNPACK_SMALL)
 
 
 def eq(got, want, what):
@@ -127,7 +129,7 @@ def test_payload_kinds(shape):
     def pack_all():
         for i in range(P):
             tar.ar_pack_fused(ins[i], words[i], 9)
-    with_shape(tar.AR_KERNEL_PACK, shape, pack_all)
+    with_shape(PACK_KINDS, shape, pack_all)
     for w, r in zip(words, words_ref):
         eq(down64(w), r, "pack")
     for kind, flags, carry in ((RD_KINDS, 0, False), (RD_KINDS, tar.AR_RD_FP32_CARRY, True),
@@ -142,10 +144,10 @@ def test_payload_kinds(shape):
             eq(down64(o), w, f"rd kind {kind}")
         assert err_host(err) == (int(werr[0]), int(werr[1]))
     note(f"shape {shape}: unpack and waiting unpack")
-    for kind in (tar.AR_KERNEL_UNPACK, tar.AR_KERNEL_UNPACK_WAIT):
+    for kind in (UNPACK_KINDS, tar.AR_KERNEL_UNPACK_WAIT):
         out = empty16(n)
         err = new_err()
-        if kind == tar.AR_KERNEL_UNPACK:
+        if kind == UNPACK_KINDS:
             fn = lambda: tar.ar_unpack_fused(words[2], out, 9, err)
         else:
             fn = lambda: tar.ar_unpack_fused_wait(words[2], out, 9, err, max_spins=100)
@@ -166,6 +168,17 @@ def test_payload_kinds(shape):
         for o, w in zip(outs, want):
             eq(down64(o), w, f"rd n={NL} flags={flags}")
         assert err_host(err) == (int(werr[0]), int(werr[1]))
+    note(f"shape {shape}: pack and unpack above the small-message threshold (n={NL})")
+    xl = large()[0]
+    xin = up16(xl[3])
+    wl = torch.empty(NL // 2, dtype=torch.int64, device=DEV)
+    with_shape(PACK_KINDS, shape, lambda: tar.ar_pack_fused(xin, wl, 9))
+    eq(down64(wl), words_ref_l[3], f"pack n={NL}")
+    out = empty16(NL)
+    err = new_err()
+    with_shape(UNPACK_KINDS, shape, lambda: tar.ar_unpack_fused(words_l[5], out, 9, err))
+    eq(down16(out), xl[5], f"unpack n={NL}")
+    assert err_host(err) == (0, 2 ** 64 - 1)
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}v{}l{}s{}w{}".format(*s))
