@@ -619,3 +619,91 @@ def test_graph_capture_replays():
         check_full(x, want, f"graph replay {rep} rd")
         assert err_host(err) == (0, 2 ** 64 - 1)
         check_full(scratch_out, oracle.reduce_seq(xs[::-1]), "eager between replays")
+
+
+def test_graph_capture_replays_other_calls():
+    """The remaining entry points captured in one HIP graph: the staged
+    two-stage (scratch), staged recursive doubling (mailbox), the waiting
+    unpack on payloads the graph itself produced, the two-stream ubatch
+    reduce without and with completion flags (the ubatch streams forked from
+    the capture stream and joined back), and the fp8 quantise and reduce.
+    Replayed with fresh inputs, cleared outputs and flags, and eager library
+    work between replays; every replay is checked against the oracle."""
+    P, rows = 8, 24
+    n = rows * HIDDEN
+    chunk = 64 * 1024 + 16                     # bytes: chunks end off the row boundaries
+
+    def i64(k):
+        return torch.empty(k, dtype=torch.int64, device=DEV)
+    ins = [empty16(n) for _ in range(P)]
+    st_outs, ub_outs, fl_outs, f8_outs = ([empty16(n) for _ in range(P)] for _ in range(4))
+    scratch, xw = empty16(n), empty16(n)
+    words, rdo = [i64(n // 2) for _ in range(P)], [i64(n // 2) for _ in range(P)]
+    mbox = i64(tar.rd_mailbox_words(P, n))
+    nflags = tar.ubatch_chunk_count(rows, HIDDEN, 2, None, chunk)
+    done = torch.zeros(nflags, dtype=torch.int32, device=DEV)
+    tiles = torch.zeros(nflags, dtype=torch.int32, device=DEV)
+    codes = [torch.empty(n, dtype=torch.uint8, device=DEV) for _ in range(P)]
+    scales = [torch.empty(tar.fp8_scale_count(n), dtype=torch.uint8, device=DEV) for _ in range(P)]
+    err = torch.empty(2, dtype=torch.int64, device=DEV)
+    side, s0, s1 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+
+    def body():
+        tar.ar_err_init(err, stream=side)
+        tar.ar_reduce_2stage(ins, st_outs, scratch=scratch, stream=side)
+        for r in range(P):
+            tar.ar_pack_fused(ins[r], words[r], 21, stream=side)
+        tar.ar_rd_schedule(words, rdo, 21, err, mailbox=mbox, flags=tar.AR_RD_STAGED, stream=side)
+        tar.ar_unpack_fused_wait(rdo[6], xw, 24, err, max_spins=1000, stream=side)
+        s0.wait_stream(side)
+        s1.wait_stream(side)
+        tar.ar_reduce_ubatch(ins, ub_outs, rows, HIDDEN, 2, None, chunk, tar.AR_VARIANT_2STAGE, streams=[s0, s1])
+        tar.ar_reduce_ubatch_flags(ins, fl_outs, rows, HIDDEN, done, tiles, 5, 2, None, chunk,
+                                   tar.AR_VARIANT_ONESHOT, streams=[s0, s1])
+        side.wait_stream(s0)
+        side.wait_stream(s1)
+        tar.ar_quantize_fp8(ins, codes, scales, stream=side)
+        tar.ar_reduce_fp8(codes, scales, f8_outs, stream=side)
+
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    note("graph capture of the remaining entry points")
+    with torch.cuda.stream(side):
+        body()                                 # eager once: one-time initialisation outside the capture
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            body()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xs = synth.rank_buffers("normal", P, n, 61, rep)
+        for t, h in zip(ins, xs):
+            t.copy_(up16(h))
+        for t in st_outs + ub_outs + fl_outs + f8_outs + [scratch, xw]:
+            t.zero_()
+        done.zero_()
+        scratch_out = empty16(n)
+        tar.ar_reduce_oneshot(ins[::-1], scratch_out)
+        torch.cuda.synchronize()
+        note(f"graph replay {rep} of the remaining entry points")
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.reduce_seq(xs)
+        check_full(scratch, ref, f"replay {rep} staged scratch")
+        for o in st_outs + ub_outs:
+            check_full(o, ref, f"replay {rep} staged two-stage / ubatch")
+        check_full(fl_outs[0], ref, f"replay {rep} flagged ubatch")
+        assert bool((done == 5).all()) and not bool(tiles.any()), f"replay {rep}: chunk flags or counters"
+        rw, _ = oracle.rd([oracle.pack(v, 21) for v in xs], 21)
+        for o, w in zip(rdo, rw):
+            assert np.array_equal(down64(o), w), f"replay {rep}: staged RD payload"
+        want, _ = oracle.unpack(rw[6], 24)
+        check_full(xw, want, f"replay {rep} waiting unpack")
+        assert err_host(err) == (0, 2 ** 64 - 1)
+        q = [oracle.quant_fp8(v) for v in xs]
+        for t, (c, sc), t2 in zip(codes, q, scales):
+            assert np.array_equal(t.cpu().numpy(), c) and np.array_equal(t2.cpu().numpy(), sc), \
+                f"replay {rep}: fp8 codes or scales"
+        f8 = oracle.reduce_fp8([c for c, _ in q], [sc for _, sc in q])
+        for o in f8_outs:
+            check_full(o, f8, f"replay {rep} fp8 reduce")
+        check_full(scratch_out, oracle.reduce_seq(xs[::-1]), "eager between replays")
