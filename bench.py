@@ -651,6 +651,28 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
             torch.cuda.synchronize()
             glat[key][name] = {"us_per_call": round(e0.elapsed_time(e1) * 1e3 / 2000, 2)}
             del g
+    # the floor of one graph node on this machine: the same capture of a
+    # one-workgroup kernel (torch's fill of 64 floats)
+    tiny = torch.zeros(64, dtype=torch.float32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        tiny.fill_(1.0)
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(100):
+                tiny.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(main_s)
+    for _ in range(20):
+        g.replay()
+    e1.record(main_s)
+    torch.cuda.synchronize()
+    glat["node_floor_one_workgroup_us"] = round(e0.elapsed_time(e1) * 1e3 / 2000, 2)
+    del g
     res["latency_hip_graph"] = glat
     log("graph latency measured")
 
