@@ -1044,11 +1044,19 @@ def cpu_baseline(args, np):
             return t0, t1, cred
         return t1 - t0, cred
 
-    dt, _ = step(16)
-    rows_s = int(min(ROWS, max(16, 16 * args.cpu_seconds / max(dt, 1e-3))))
+    # size the sample from a 128-row run, then once more from the sample
+    # itself if that came out under half the target: the cost per row grows
+    # once the rows no longer fit the host's caches, and a short run is noisy
+    dt, _ = step(128)
+    rows_s = int(min(ROWS, max(128, 128 * args.cpu_seconds / max(dt, 1e-3))))
     rows_s -= rows_s % 2
-    log(f"cpu oracle: calibration 16 rows took {dt:.2f} s; timing {rows_s} rows")
+    log(f"cpu oracle: calibration 128 rows took {dt:.2f} s; timing {rows_s} rows")
     dt, cred = step(rows_s)
+    if dt < 0.5 * args.cpu_seconds and rows_s < ROWS:
+        rows_s = int(min(ROWS, rows_s * args.cpu_seconds / max(dt, 1e-3)))
+        rows_s -= rows_s % 2
+        log(f"cpu oracle: {dt:.1f} s, under half the target; timing {rows_s} rows")
+        dt, cred = step(rows_s)
     gbps = cred / dt / 1e9
     res = {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"one full step (all six rows) of the oracle on the first {rows_s} of 16384 rows "
