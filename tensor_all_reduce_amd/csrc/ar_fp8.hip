@@ -153,15 +153,20 @@ template <int P, int NOUT, int EPL, bool NTL, bool NTS>
 __global__ __launch_bounds__(kMaxBlock) void k_reduce_fp8(ByteIn codes, ByteIn scales, OutPtrs out,
                                                           size_t n) {
   constexpr int NW = EPL / 4;
-  // Workgroups reach the 8 XCDs round-robin.  Within every run of 32
-  // workgroups, XCD x takes the 4 consecutive tiles 4x .. 4x + 3, so the
-  // tiles that share a 128-byte line of scale bytes (4 at 128 lanes x 8
-  // elements) meet in one XCD's L2 instead of fetching it once per XCD.  The
-  // last, partial run keeps the identity order; every tile is still taken
-  // exactly once.
+  // Workgroups reach the 8 XCDs round-robin.  A 128-byte line of scale bytes
+  // covers G = 4096 / (blockDim.x * EPL) consecutive tiles (8 at 64 lanes x
+  // 8 elements, 4 at 128 lanes, 2 at 256).  Within every run of 8 G
+  // workgroups, XCD x takes the G consecutive tiles x G .. x G + G - 1, so
+  // the tiles that share a scale line meet in one XCD's L2 instead of
+  // fetching it once per XCD.  The last, partial run keeps the identity
+  // order; every tile is still taken exactly once.
+  const unsigned G = 4096u / (blockDim.x * (unsigned)EPL);
   size_t tile = blockIdx.x;
-  if ((size_t)(blockIdx.x / 32 + 1) * 32 <= gridDim.x)
-    tile = (size_t)(blockIdx.x / 32) * 32 + (blockIdx.x % 8) * 4 + (blockIdx.x / 8) % 4;
+  if (G > 1) {
+    const size_t R = 8 * (size_t)G;
+    if ((size_t)(blockIdx.x / R + 1) * R <= gridDim.x)
+      tile = (size_t)(blockIdx.x / R) * R + (blockIdx.x % 8) * G + (blockIdx.x / 8) % G;
+  }
   const size_t g = tile * blockDim.x + threadIdx.x;
   const size_t i0 = g * EPL;
   if (i0 >= n) return;

@@ -54,10 +54,10 @@ SHAPES = {
            (128, 1, 1, 1, 4)],
     "quant": [(64, 2, 1, 1, 0), (64, 1, 1, 1, 0), (128, 2, 1, 1, 0), (256, 1, 1, 1, 0), (64, 2, 1, 0, 0),
               (64, 2, 0, 1, 0), (64, 2, 1, 1, 8), (64, 2, 1, 1, 4), (128, 1, 1, 1, 4)],
-    "fp8r1": [(128, 1, 1, 1, 8), (64, 1, 1, 1, 8), (128, 2, 1, 1, 8), (128, 1, 1, 1, 4), (256, 1, 1, 1, 4),
-              (128, 1, 1, 0, 8), (128, 1, 1, 1, 0)],
-    "fp8rp": [(128, 1, 1, 1, 5), (128, 1, 1, 1, 6), (64, 1, 1, 1, 6), (128, 1, 1, 1, 4), (128, 1, 1, 1, 8),
-              (256, 1, 1, 1, 3), (128, 2, 1, 1, 6), (128, 1, 1, 1, 0)],
+    "fp8r1": [(128, 1, 1, 1, 8), (128, 1, 1, 1, 10), (64, 1, 1, 1, 8), (64, 1, 1, 1, 16), (128, 2, 1, 1, 8),
+              (128, 1, 1, 1, 4), (256, 1, 1, 1, 4), (128, 1, 1, 0, 8), (128, 1, 1, 1, 0)],
+    "fp8rp": [(128, 1, 1, 1, 5), (128, 1, 1, 1, 6), (128, 1, 1, 1, 4), (64, 1, 1, 1, 6), (64, 1, 1, 1, 8),
+              (128, 1, 1, 1, 8), (256, 1, 1, 1, 3), (128, 2, 1, 1, 6), (128, 1, 1, 1, 0)],
 }
 
 
