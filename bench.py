@@ -66,7 +66,7 @@ def parse():
                     help="time the oracle on one core only (skip the all-cores run)")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps (for profiler runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, run 3 plain copies of exactly 1 GiB (counter calibration)")
