@@ -24,8 +24,13 @@
  *   pointers into kernel arguments, so the host arrays may be freed on return.
  * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  * - The caller owns every buffer.  The library keeps no pointer after return.
- * - All argument checks happen before any launch: an error return means no
- *   work was queued.  n == 0 queues nothing and returns AR_OK.
+ * - All argument checks, and the size check of every launch grid, happen
+ *   before the first launch: AR_ERR_INVALID, AR_ERR_ALIGN, AR_ERR_ALIAS and
+ *   AR_ERR_UNSUPPORTED mean no work was queued.  AR_ERR_HIP reports a
+ *   failure of the HIP runtime itself; from an entry point that makes
+ *   several launches (the staged two-stage, the staged recursive doubling,
+ *   the ubatch reduces) it may leave the launches before the failing one
+ *   queued.  n == 0 queues nothing and returns AR_OK.
  * - Aliasing: an output may be exactly the same buffer as an input (in
  *   place); any partial overlap between an output and another buffer, or
  *   between two outputs, is AR_ERR_ALIAS.  Inputs may alias each other.
@@ -36,9 +41,11 @@
  *   that the models run in bf16 ([NVRAR] Methodology 1, "Models"); this
  *   accumulation order and rounding are this library's stated reading.
  * - Thread safety: every entry point may be called concurrently from several
- *   host threads on different streams.  The only global state is a per-device
- *   attribute cache filled once under a lock (lazy initialisation raced by two
- *   ubatch threads is the hazard [TBO-AR] review comments describe).
+ *   host threads on different streams.  The only global state is one
+ *   immutable launch table per device (CU count and launch shapes), built
+ *   once under a lock by the first call on that device -- lazy
+ *   initialisation raced by two ubatch threads is the hazard [TBO-AR] review
+ *   comments describe -- and read without a lock by every later call.
  */
 #ifndef AR_H_
 #define AR_H_
@@ -207,9 +214,12 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 /*
  * Launch-shape control (tuning; not a step of the reduction).  Every kernel
  * kind runs on a flat grid of `block`-lane workgroups (64, 128 or 256) with
- * optional non-temporal loads/stores and at most `wg_per_cu` workgroups per
- * compute unit (0 = no cap; enforced by requesting unused LDS).  `vec` (1 or
- * 2) sets how much each lane handles:
+ * optional non-temporal loads (`nt_loads` 0 or 1), an output store policy
+ * `stores` -- 0 plain, 1 non-temporal, 2 written through past the compute
+ * die's L2 (SC1), 3 SC1 + non-temporal; UNPACK_WAIT uses only the
+ * non-temporal bit, UBATCH_FLAGS always writes through -- and at most
+ * `wg_per_cu` workgroups per compute unit (0 = no cap; enforced by
+ * requesting unused LDS).  `vec` (1 or 2) sets how much each lane handles:
  *   ONESHOT, 2STAGE, UBATCH, UBATCH_FLAGS, RD, QUANT_FP8 and their _SMALL
  *     kinds: vec 16-byte groups per buffer, each a contiguous span across
  *     the wavefront;
@@ -256,8 +266,8 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 #define AR_KERNEL_RDSTEP_SMALL 17  /* ar_rd_schedule staged, n <= AR_SMALL_ELEMS */
 #define AR_KERNEL_PACK_SMALL 18    /* ar_pack_fused, n <= AR_SMALL_ELEMS        */
 #define AR_KERNEL_UNPACK_SMALL 19  /* ar_unpack_fused, n <= AR_SMALL_ELEMS      */
-int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu);
-int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
+int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int stores, int wg_per_cu);
+int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* stores,
                         int* wg_per_cu);
 
 /*

@@ -356,15 +356,17 @@ def ar_err_init(d_err, stream=None) -> None:
     _check(lib().ar_err_init(ep, _stream(stream)), "ar_err_init")
 
 
-def ar_set_launch_shape(kind: int, block: int, vec: int, nt_loads: int, nt_stores: int,
+def ar_set_launch_shape(kind: int, block: int, vec: int, nt_loads: int, stores: int,
                         wg_per_cu: int) -> None:
-    """Set the launch shape of one kernel kind (tuning; process-wide)."""
+    """Set the launch shape of one kernel kind (tuning; process-wide).  `stores`
+    is the output store policy: 0 plain, 1 non-temporal, 2 SC1 write-through,
+    3 SC1 write-through + non-temporal."""
     _check(lib().ar_set_launch_shape(int(kind), int(block), int(vec), int(nt_loads),
-                                     int(nt_stores), int(wg_per_cu)), "ar_set_launch_shape")
+                                     int(stores), int(wg_per_cu)), "ar_set_launch_shape")
 
 
 def ar_get_launch_shape(kind: int) -> tuple:
-    """(block, vec, nt_loads, nt_stores, wg_per_cu) of one kernel kind."""
+    """(block, vec, nt_loads, stores, wg_per_cu) of one kernel kind."""
     v = [ctypes.c_int() for _ in range(5)]
     _check(lib().ar_get_launch_shape(int(kind), *[ctypes.byref(x) for x in v]), "ar_get_launch_shape")
     return tuple(x.value for x in v)

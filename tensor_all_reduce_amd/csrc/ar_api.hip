@@ -1,14 +1,18 @@
 // C-ABI of the all-reduce core (declared in include/ar.h): argument checks,
 // the per-device attribute cache, tuning knobs, and dispatch to the kernels.
 //
-// Every check runs before the first launch, so an error return never leaves
-// partial work queued.  The only global state is the device cache, filled
-// once per device under a mutex: two host threads (one per ubatch) racing the
-// first call must not both initialise it -- the lazy-initialisation race the
-// review of "[DSV4] perf(tbo): overlap pure-TP all_reduce on TBO + Delay TP"
-// flags for its per-ubatch communicators.
+// Every argument check and every grid-size check runs before the first
+// launch, so an argument error never leaves partial work queued.  The only
+// global state is one immutable launch table per device (CU count and the
+// resolved launch shapes), built on the first call on that device under a
+// mutex and published through an atomic pointer: two host threads (one per
+// ubatch) racing the first call must not both initialise it -- the
+// lazy-initialisation race the review of "[DSV4] perf(tbo): overlap pure-TP
+// all_reduce on TBO + Delay TP" flags for its per-ubatch communicators --
+// and after that first call no call takes a lock.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -26,35 +30,29 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int kMaxUbatch = 16;
 
-struct DevInfo {
-  bool ready = false;
-  int cus = 0;
-  int lds_per_cu = 0;
-  int lds_per_block = 0;
-};
-
 // Default launch shapes: the fastest settings measured on MI355X for each
-// kernel's stream pattern (block, vec, nt_loads, nt_stores, wg_per_cu).  For
+// kernel's stream pattern (block, vec, nt_loads, stores, wg_per_cu; stores is
+// the output store policy of st16: 0 plain, 1 NT, 2 SC1, 3 SC1 + NT).  For
 // the one-shot and fused two-stage kernels, whose best shape for one
 // placement of the rank buffers can lose 15-20% on another (buffers carved
 // from one allocation, or halves of larger tensors), the pick is the shape
 // with the best worst case over placements, within 1% of the best for
 // separately allocated buffers.
 constexpr ar::Shape kDefaultShape[] = {
-    {64, 1, 1, 1, 8, 0},    // one-shot, 8 -> 1
-    {64, 1, 1, 1, 6, 0},    // fused two-stage, 8 -> 8
-    {64, 1, 1, 1, 6, 0},    // ubatch, 8 -> 8 on two streams
-    {256, 1, 1, 1, 5, 0},   // staged reduce-scatter, 8 -> 1
-    {64, 1, 1, 1, 3, 0},    // staged all-gather, 1 -> 8
+    {64, 1, 1, 2, 16, 0},   // one-shot, 8 -> 1
+    {64, 1, 1, 2, 6, 0},    // fused two-stage, 8 -> 8
+    {64, 1, 1, 3, 6, 0},    // ubatch, 8 -> 8 on two streams
+    {64, 1, 1, 2, 10, 0},   // staged reduce-scatter, 8 -> 1
+    {64, 1, 0, 1, 3, 0},    // staged all-gather, 1 -> 8 (plain loads of scratch)
     {64, 1, 1, 1, 0, 0},    // pack, 1 -> 2 (vec: 16-byte bf16 groups per lane; 1 = 8 bytes)
-    {64, 1, 1, 1, 0, 0},    // unpack, 2 -> 1
-    {64, 1, 1, 1, 8, 0},    // fused recursive doubling, 8 -> 8
-    {128, 1, 1, 1, 8, 0},   // staged recursive-doubling step, 8 -> 8
+    {64, 1, 1, 3, 0, 0},    // unpack, 2 -> 1
+    {64, 1, 1, 3, 8, 0},    // fused recursive doubling, 8 -> 8
+    {64, 1, 1, 2, 16, 0},   // staged recursive-doubling step, 8 -> 8
     {256, 1, 0, 1, 2, 0},   // waiting unpack: 2 persistent workgroups (8 waves) per CU
-    {256, 2, 1, 1, 2, 0},   // flagged ubatch: big tiles, few store waits and counter atomics per chunk
-    {64, 2, 1, 1, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
-    {128, 1, 1, 1, 8, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)
-    {128, 1, 1, 1, 5, 0},   // fp8 reduce, P code streams -> P outputs
+    {256, 1, 1, 3, 3, 0},   // flagged ubatch: big tiles, few store waits and counter atomics per chunk
+    {64, 2, 1, 3, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
+    {256, 1, 1, 1, 6, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)
+    {256, 1, 1, 3, 3, 0},   // fp8 reduce, P code streams -> P outputs
     {128, 1, 0, 1, 0, 0},   // one-shot, n <= AR_SMALL_ELEMS: uncapped, plain loads
     {128, 1, 0, 1, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
     {64, 1, 0, 1, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
@@ -84,17 +82,32 @@ static_assert(ar::kOneshot == AR_KERNEL_ONESHOT && ar::k2Stage == AR_KERNEL_2STA
                   ar::kKinds == AR_KERNEL_UNPACK_SMALL + 1,
               "kind numbers match ar.h");
 
-std::mutex g_mu;
-DevInfo g_dev[kMaxDevices];
-bool g_shapes_ready = false;
-ar::Shape g_shape[ar::kKinds];
+// What one device's calls read: its CU count and the launch shapes with
+// their LDS requests resolved for it.  Never modified once published.
+struct Table {
+  int cus;
+  ar::Shape shape[ar::kKinds];
+};
 
-bool shape_ok(int block, int vec, int ntl, int nts, int wg) {
+struct DevAttr {
+  int cus = 0, lds_per_cu = 0, lds_per_block = 0;
+};
+
+std::mutex g_mu;                              // initialisation and shape changes
+bool g_base_ready = false;                    // guarded by g_mu
+ar::Shape g_base[ar::kKinds];                 // defaults + overrides; guarded by g_mu
+DevAttr g_attr[kMaxDevices];                  // guarded by g_mu
+// Published tables are never freed: a call may still be reading a table that
+// ar_set_launch_shape has replaced.  One table per device, plus one per
+// device for each ar_set_launch_shape call (a tuning knob), ~500 bytes each.
+std::atomic<const Table*> g_table[kMaxDevices];
+
+bool shape_ok(int block, int vec, int ntl, int stores, int wg) {
   return (block == 64 || block == 128 || block == 256) && vec >= 1 && vec <= 2 && ntl >= 0 &&
-         ntl <= 1 && nts >= 0 && nts <= 1 && wg >= 0 && wg <= 64;
+         ntl <= 1 && stores >= 0 && stores <= 3 && wg >= 0 && wg <= 64;
 }
 
-// "block,vec,nt_loads,nt_stores,wg_per_cu"; an invalid string keeps the default.
+// "block,vec,nt_loads,stores,wg_per_cu"; an invalid string keeps the default.
 void parse_shape(const char* name, ar::Shape* s) {
   const char* e = std::getenv(name);
   if (!e || !*e) return;
@@ -105,48 +118,62 @@ void parse_shape(const char* name, ar::Shape* s) {
 }
 
 // Caller holds g_mu.
-void init_shapes_locked() {
-  if (g_shapes_ready) return;
+void init_base_locked() {
+  if (g_base_ready) return;
   for (int k = 0; k < ar::kKinds; ++k) {
-    g_shape[k] = kDefaultShape[k];
-    parse_shape(kShapeEnv[k], &g_shape[k]);
+    g_base[k] = kDefaultShape[k];
+    parse_shape(kShapeEnv[k], &g_base[k]);
   }
-  g_shapes_ready = true;
+  g_base_ready = true;
 }
 
-// Resolve the launch policy for the current device: CU count and LDS sizes
-// (cached once per device) and the per-kernel shapes (defaults above,
-// overridable once per process through AR_SHAPE_<KIND> for A/B measurement).
-int resolve(ar::Launch* L, void* stream) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AR_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_mu);
-  init_shapes_locked();
-  DevInfo& d = g_dev[dev];
-  if (!d.ready) {
-    int cus = 0, lcu = 0, lblk = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&lcu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-            hipSuccess ||
-        hipDeviceGetAttribute(&lblk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-        cus <= 0)
-      return AR_ERR_HIP;
-    d.cus = cus;
-    d.lds_per_cu = lcu;
-    d.lds_per_block = lblk;
-    d.ready = true;
-  }
-  L->cus = d.cus;
+// Build and publish device `dev`'s table from g_base.  Caller holds g_mu and
+// has filled g_attr[dev].
+const Table* publish_locked(int dev) {
+  const DevAttr& d = g_attr[dev];
+  Table* t = new Table;
+  t->cus = d.cus;
   for (int k = 0; k < ar::kKinds; ++k) {
-    ar::Shape s = g_shape[k];
+    ar::Shape s = g_base[k];
     unsigned lds = 0;
     if (s.wg_per_cu > 0 && d.lds_per_cu > 0) {
       lds = ((unsigned)d.lds_per_cu / (unsigned)s.wg_per_cu) & ~255u;
       if (lds > (unsigned)d.lds_per_block) lds = (unsigned)d.lds_per_block;
     }
     s.lds = lds;
-    L->shape[k] = s;
+    t->shape[k] = s;
   }
+  g_table[dev].store(t, std::memory_order_release);
+  return t;
+}
+
+// Resolve the launch policy for the current device.  The first call on a
+// device queries its attributes and builds its table under g_mu; every later
+// call is one acquire load.  Shapes come from the defaults above, overridable
+// once per process through AR_SHAPE_<KIND> or at any time through
+// ar_set_launch_shape.
+int resolve(ar::Launch* L, void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AR_ERR_HIP;
+  const Table* t = g_table[dev].load(std::memory_order_acquire);
+  if (!t) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    t = g_table[dev].load(std::memory_order_relaxed);
+    if (!t) {
+      int cus = 0, lcu = 0, lblk = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipDeviceGetAttribute(&lcu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+              hipSuccess ||
+          hipDeviceGetAttribute(&lblk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+          cus <= 0)
+        return AR_ERR_HIP;
+      g_attr[dev] = DevAttr{cus, lcu, lblk};
+      init_base_locked();
+      t = publish_locked(dev);
+    }
+  }
+  L->cus = t->cus;
+  L->shape = t->shape;
   L->stream = static_cast<hipStream_t>(stream);
   return AR_OK;
 }
@@ -466,7 +493,14 @@ int ubatch_impl(const void* const* ins, void* const* outs, int P, size_t rows, s
   if (n == 0) return AR_OK;
   ar::Launch L;
   if ((rc = resolve(&L, nullptr))) return rc;
+  // every ubatch's grid is checked before the first launch
   size_t row0 = 0, chunk0 = 0;
+  for (int u = 0; u < n_ubatch; ++u) {
+    const size_t e0 = row0 * hidden, e1 = (row0 + split[u]) * hidden;
+    row0 += split[u];
+    if (e1 > e0 && !ar::chunked_fits(L, e0, e1, chunk, nout > 1 ? 1 : 0, done != nullptr)) return AR_ERR_INVALID;
+  }
+  row0 = 0;
   for (int u = 0; u < n_ubatch; ++u) {
     const size_t e0 = row0 * hidden, e1 = (row0 + split[u]) * hidden;
     row0 += split[u];
@@ -500,26 +534,29 @@ int ar_reduce_ubatch_flags(const void* const* ins, void* const* outs, int P, siz
                      chunk_done, chunk_tiles, n_flags, epoch);
 }
 
-int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int nt_stores, int wg_per_cu) {
-  if (kind < 0 || kind >= ar::kKinds || !shape_ok(block, vec, nt_loads, nt_stores, wg_per_cu))
+int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int stores, int wg_per_cu) {
+  if (kind < 0 || kind >= ar::kKinds || !shape_ok(block, vec, nt_loads, stores, wg_per_cu))
     return AR_ERR_INVALID;
   std::lock_guard<std::mutex> lock(g_mu);
-  init_shapes_locked();
-  g_shape[kind] = ar::Shape{block, vec, nt_loads, nt_stores, wg_per_cu, 0};
+  init_base_locked();
+  g_base[kind] = ar::Shape{block, vec, nt_loads, stores, wg_per_cu, 0};
+  // republish every device already in use; later calls see the new shape
+  for (int d = 0; d < kMaxDevices; ++d)
+    if (g_table[d].load(std::memory_order_relaxed)) publish_locked(d);
   return AR_OK;
 }
 
-int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* nt_stores,
+int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* stores,
                         int* wg_per_cu) {
-  if (kind < 0 || kind >= ar::kKinds || !block || !vec || !nt_loads || !nt_stores || !wg_per_cu)
+  if (kind < 0 || kind >= ar::kKinds || !block || !vec || !nt_loads || !stores || !wg_per_cu)
     return AR_ERR_INVALID;
   std::lock_guard<std::mutex> lock(g_mu);
-  init_shapes_locked();
-  const ar::Shape& s = g_shape[kind];
+  init_base_locked();
+  const ar::Shape& s = g_base[kind];
   *block = s.block;
   *vec = s.vec;
   *nt_loads = s.nt_loads;
-  *nt_stores = s.nt_stores;
+  *stores = s.stores;
   *wg_per_cu = s.wg_per_cu;
   return AR_OK;
 }

@@ -181,117 +181,6 @@ __global__ __launch_bounds__(256) void k_readsum(const u32x4* __restrict__ src, 
   if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
-// Grid-stride variant of the fused 8 -> 8 reduce, for the A/B against the
-// library's flat in-order tiles: the same arithmetic (rank-order binary32
-// sums, one nearest-even rounding, non-temporal accesses), but a fixed grid
-// of `grid` workgroups walks the buffer in steps of grid * 256 groups.
-__device__ __forceinline__ uint32_t rne_hi_b(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
-  return __builtin_isnan(f) ? 0x7FC00000u : r;
-}
-
-struct In8 { const u32x4* p[8]; };
-struct Out8 { u32x4* p[8]; };
-
-__global__ __launch_bounds__(256) void k_gridstride88(In8 in, Out8 out, size_t nvec) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    u32x4 a[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) a[p] = __builtin_nontemporal_load(in.p[p] + v);
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float lo = __uint_as_float(a[0][k] << 16), hi = __uint_as_float(a[0][k] & 0xFFFF0000u);
-#pragma unroll
-      for (int p = 1; p < 8; ++p) {
-        lo = lo + __uint_as_float(a[p][k] << 16);
-        hi = hi + __uint_as_float(a[p][k] & 0xFFFF0000u);
-      }
-      r[k] = (rne_hi_b(lo) >> 16) | (rne_hi_b(hi) & 0xFFFF0000u);
-    }
-#pragma unroll
-    for (int o = 0; o < 8; ++o) __builtin_nontemporal_store(r, out.p[o] + v);
-  }
-}
-
-// The fused 8 -> 8 reduce with a chosen access width, for the A/B of 4-,
-// 8- and 16-byte accesses per lane: each 64-lane workgroup owns 1 KiB of
-// every buffer (as the library's one-group-per-lane tiles do) and each lane
-// moves 16 bytes of it per buffer as 16 / WB accesses of WB bytes, access j
-// of the wavefront covering bytes [j * 64 * WB, (j + 1) * 64 * WB) of the
-// tile, so every instruction is one contiguous span and the bytes in flight
-// per lane are the same at every width.  Same arithmetic as the library.
-template <int WB> struct AccessT;
-template <> struct AccessT<4> { typedef uint32_t T; };
-template <> struct AccessT<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
-template <> struct AccessT<16> { typedef u32x4 T; };
-
-struct Bytes8 {
-  const char* in[8];
-  char* out[8];
-};
-
-template <int WB>
-__global__ __launch_bounds__(64) void k_width88(Bytes8 b, size_t nbytes) {
-  typedef typename AccessT<WB>::T T;
-  constexpr int A = 16 / WB;   // accesses per lane per buffer
-  constexpr int NW = WB / 4;   // 32-bit words per access
-  const size_t tile = (size_t)blockIdx.x * 1024;
-  if (tile + 1024 > nbytes) return;   // whole tiles only (the caller passes a multiple of 1 KiB)
-  T a[A][8];
-#pragma unroll
-  for (int j = 0; j < A; ++j)
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-      a[j][p] = __builtin_nontemporal_load(reinterpret_cast<const T*>(b.in[p] + tile + (size_t)j * 64 * WB) +
-                                           threadIdx.x);
-#pragma unroll
-  for (int j = 0; j < A; ++j) {
-    uint32_t w[8][NW];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) __builtin_memcpy(w[p], &a[j][p], WB);
-    uint32_t r[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      float lo = __uint_as_float(w[0][k] << 16), hi = __uint_as_float(w[0][k] & 0xFFFF0000u);
-#pragma unroll
-      for (int p = 1; p < 8; ++p) {
-        lo = lo + __uint_as_float(w[p][k] << 16);
-        hi = hi + __uint_as_float(w[p][k] & 0xFFFF0000u);
-      }
-      r[k] = (rne_hi_b(lo) >> 16) | (rne_hi_b(hi) & 0xFFFF0000u);
-    }
-    T v;
-    __builtin_memcpy(&v, r, WB);
-#pragma unroll
-    for (int o = 0; o < 8; ++o)
-      __builtin_nontemporal_store(v, reinterpret_cast<T*>(b.out[o] + tile + (size_t)j * 64 * WB) + threadIdx.x);
-  }
-}
-
-// Unpack with per-lane error atomics, for the A/B against the library's
-// wavefront-ballot validation: lane v unpacks payload words 2v and 2v+1
-// (one 16-byte load, one 8-byte store, as the library's unpack does) and
-// every lane whose word carries the wrong sequence number adds 1 to err[0]
-// and lowers err[1] itself.
-__global__ __launch_bounds__(256) void k_unpack_lane_atomics(const u32x4* w, uint64_t* x, size_t nl,
-                                                             uint32_t seq, unsigned long long* err) {
-  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= nl) return;
-  const u32x4 a = __builtin_nontemporal_load(w + v);
-  __builtin_nontemporal_store((uint64_t)a[0] | ((uint64_t)a[2] << 32), x + v);
-  if (a[1] != seq) {
-    atomicAdd(err, 1ull);
-    atomicMin(err + 1, (unsigned long long)(2 * v));
-  }
-  if (a[3] != seq) {
-    atomicAdd(err, 1ull);
-    atomicMin(err + 1, (unsigned long long)(2 * v + 1));
-  }
-}
-
 // ALU-bound stand-in for the partner ubatch's compute: `iters` rounds of
 // dependent fused multiply-adds on four accumulators per lane; one float out.
 __global__ __launch_bounds__(256) void k_alu(float* out, int iters) {
@@ -558,68 +447,6 @@ double arb_handoff_us(const void* x, uint64_t* words, void* y, size_t n, uint32_
   if (rc != AR_OK) return (double)rc;
   std::nth_element(us.begin(), us.begin() + us.size() / 2, us.end());
   return us[us.size() / 2];
-}
-
-// Grid-stride 8 -> 8 reduce (see k_gridstride88): n elements per buffer, a
-// multiple of 8; buffers 16-byte aligned; `grid` workgroups of 256 lanes.
-int arb_gridstride_reduce8(const void* const* ins, void* const* outs, size_t n, int grid, void* stream) {
-  if (!ins || !outs || (n & 7u) || grid <= 0) return AR_ERR_INVALID;
-  In8 in;
-  Out8 out;
-  for (int p = 0; p < 8; ++p) {
-    if (!ins[p] || !outs[p]) return AR_ERR_INVALID;
-    in.p[p] = static_cast<const u32x4*>(ins[p]);
-    out.p[p] = static_cast<u32x4*>(outs[p]);
-  }
-  hipLaunchKernelGGL(k_gridstride88, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), in, out, n / 8);
-  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
-}
-
-// Fused 8 -> 8 reduce with `width`-byte accesses (4, 8 or 16; see
-// k_width88): n elements per buffer, a multiple of 512; buffers 16-byte
-// aligned; 64-lane workgroups, at most wg_per_cu per CU through a dynamic
-// LDS request (0: no cap).
-int arb_width_reduce8(const void* const* ins, void* const* outs, size_t n, int width, int wg_per_cu,
-                      void* stream) {
-  if (!ins || !outs || (n & 511u) || n == 0 || (width != 4 && width != 8 && width != 16) || wg_per_cu < 0)
-    return AR_ERR_INVALID;
-  Bytes8 b{};
-  for (int p = 0; p < 8; ++p) {
-    if (!ins[p] || !outs[p]) return AR_ERR_INVALID;
-    b.in[p] = static_cast<const char*>(ins[p]);
-    b.out[p] = static_cast<char*>(outs[p]);
-  }
-  unsigned lds = 0;
-  if (wg_per_cu > 0) {
-    int dev = 0, per_cu = 0, per_block = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      return AR_ERR_HIP;
-    lds = ((unsigned)per_cu / (unsigned)wg_per_cu) & ~255u;
-    if (lds > (unsigned)per_block) lds = (unsigned)per_block;
-  }
-  const size_t nbytes = n * 2, grid = nbytes / 1024;
-  if (grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (width == 4) hipLaunchKernelGGL(k_width88<4>, dim3((unsigned)grid), dim3(64), lds, st, b, nbytes);
-  else if (width == 8) hipLaunchKernelGGL(k_width88<8>, dim3((unsigned)grid), dim3(64), lds, st, b, nbytes);
-  else hipLaunchKernelGGL(k_width88<16>, dim3((unsigned)grid), dim3(64), lds, st, b, nbytes);
-  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
-}
-
-// Per-lane-atomic unpack (see k_unpack_lane_atomics) of n elements (n a
-// multiple of 4), 256-lane workgroups.
-int arb_unpack_lane_atomics(const uint64_t* words, void* x, size_t n, uint32_t seq, uint64_t* d_err,
-                            void* stream) {
-  if (!words || !x || !d_err || (n & 3u)) return AR_ERR_INVALID;
-  const size_t nl = n / 4;
-  const size_t grid = (nl + 255) / 256;
-  if (grid == 0 || grid > 0x7FFFFFFFull) return AR_ERR_INVALID;
-  hipLaunchKernelGGL(k_unpack_lane_atomics, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     reinterpret_cast<const u32x4*>(words), static_cast<uint64_t*>(x), nl, seq,
-                     reinterpret_cast<unsigned long long*>(d_err));
-  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
 // Read-only sweep of `bytes` (a multiple of 16, 16-byte aligned); out holds

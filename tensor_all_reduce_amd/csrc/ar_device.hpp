@@ -44,20 +44,44 @@ __device__ __forceinline__ void st8(uint64_t* p, uint64_t v) {
   else *p = v;
 }
 
-// Device-coherent 16-byte store for data that a completion flag will cover.
-// The buffer store carries the SC1 cache policy (aux bit 4; bit 1 adds the
-// streaming NT hint): it is written through to the level every XCD's L2
-// sees, so once the wave's store counter drains no dirty copy sits in one
-// XCD's L2 and the flag can be published without an L2 writeback (the
-// writeback an agent-scope release fence performs costs more than the
-// reduce itself).  `base` is the wave-uniform start of the written span,
-// `bytes` its length (the buffer descriptor's range), `off` this lane's
-// byte offset in it.  Descriptor word 3 = 0x00020000 selects the 32-bit
-// data format (any nonzero format works for untyped access).
-template <bool NT>
-__device__ __forceinline__ void st4_coherent(u32x4* base, uint32_t bytes, uint32_t off, u32x4 v) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, NT ? (16 | 2) : 16);
+// Output store policy, the launch shape's `stores` field:
+//   0  plain store (write-back through the XCD's L2);
+//   1  non-temporal (streaming hint);
+//   2  SC1: written through past the XCD's L2 to the level every XCD sees;
+//   3  SC1 + non-temporal.
+// Policies 2 and 3 are buffer stores carrying the cache-policy bits (aux bit
+// 4 = SC1, bit 1 = NT).  They measured faster than the plain and
+// non-temporal forms for every streamed output on MI355X (e.g. the fused
+// 8 -> 8 reduce at 256 MiB per buffer 684.6 -> 674.2 us, the 8 -> 1 one-shot
+// 380 -> 366 us), and they are what makes data covered by a completion flag
+// visible to another XCD without an L2 writeback: once the wave's store
+// counter drains, no dirty copy sits in one XCD's L2.
+//
+// Every helper takes the wave-uniform start of the written span (`base`),
+// its length in bytes (the buffer descriptor's range) and this lane's byte
+// offset in it; policies 0 and 1 simply store to base + off.  Descriptor
+// word 3 = 0x00020000 selects the 32-bit data format (any nonzero format
+// works for untyped access).
+template <int SP>
+__device__ __forceinline__ void st16(void* base, uint32_t bytes, uint32_t off, u32x4 v) {
+  if constexpr (SP >= 2) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, SP == 3 ? (16 | 2) : 16);
+  } else {
+    st4<SP == 1>(reinterpret_cast<u32x4*>(static_cast<char*>(base) + off), v);
+  }
+}
+
+template <int SP>
+__device__ __forceinline__ void st8p(void* base, uint32_t bytes, uint32_t off, uint64_t v) {
+  if constexpr (SP >= 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+    const u32x2 w = {(uint32_t)v, (uint32_t)(v >> 32)};
+    __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off, 0, SP == 3 ? (16 | 2) : 16);
+  } else {
+    st8<SP == 1>(reinterpret_cast<uint64_t*>(static_cast<char*>(base) + off), v);
+  }
 }
 
 // s_waitcnt with vmcnt = 0 and expcnt / lgkmcnt left at their maxima (gfx9

@@ -70,7 +70,7 @@ __device__ __forceinline__ uint32_t codes4(const uint32_t* b, int k) {
 // Workgroup b quantises tile b % tiles of buffer b / tiles; a tile is
 // V * blockDim groups of 8 elements.  Lanes past the end take part in the
 // quad maximum with zeros and store nothing.
-template <int V, bool NTL, bool NTS>
+template <int V, bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_quant_fp8(InPtrs xs, ByteOut codes, ByteOut scales,
                                                          size_t n, unsigned tiles) {
   const unsigned p = blockIdx.x / tiles;
@@ -107,9 +107,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_quant_fp8(InPtrs xs, ByteOut code
     const uint32_t lo = codes4(b, k), hi = codes4(b + 4, k);
     if (i0 + 8 <= n) {
       const uint64_t c = (uint64_t)lo | ((uint64_t)hi << 32);
-      uint64_t* dst = reinterpret_cast<uint64_t*>(cp + i0);
-      if constexpr (NTS) __builtin_nontemporal_store(c, dst);
-      else *dst = c;
+      st8p<SP>(reinterpret_cast<uint64_t*>(cp) + tile0 + (size_t)u * blockDim.x, blockDim.x * 8u, threadIdx.x * 8u, c);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -149,7 +147,7 @@ __device__ __forceinline__ void load_codes(const uint8_t* c, size_t g, uint32_t 
   }
 }
 
-template <int P, int NOUT, int EPL, bool NTL, bool NTS>
+template <int P, int NOUT, int EPL, bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_reduce_fp8(ByteIn codes, ByteIn scales, OutPtrs out,
                                                           size_t n) {
   constexpr int NW = EPL / 4;
@@ -197,7 +195,9 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce_fp8(ByteIn codes, ByteIn s
       r.z = pack_bf16x2(acc[8 * h + 4], acc[8 * h + 5]);
       r.w = pack_bf16x2(acc[8 * h + 6], acc[8 * h + 7]);
 #pragma unroll
-      for (int o = 0; o < NOUT; ++o) st4<NTS>(static_cast<u32x4*>(out.p[o]) + (EPL / 8) * g + h, r);
+      for (int o = 0; o < NOUT; ++o)
+        st16<SP>(static_cast<u32x4*>(out.p[o]) + (EPL / 8) * tile * blockDim.x, (EPL / 8) * blockDim.x * 16u,
+                 ((EPL / 8) * threadIdx.x + h) * 16u, r);
     }
   } else {
     for (size_t i = i0; i < n; ++i) {
@@ -223,11 +223,10 @@ hipError_t quant_v(const Shape& sh, hipStream_t st, const InPtrs& xs, const Byte
   if (tiles * (size_t)P > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
   const unsigned g = (unsigned)(tiles * P), t = (unsigned)tiles;
   const dim3 blk(sh.block);
-  if (sh.nt_loads && sh.nt_stores)
-    return launch_k(k_quant_fp8<V, true, true>, g, blk, sh.lds, st, xs, codes, scales, n, t);
-  if (sh.nt_loads) return launch_k(k_quant_fp8<V, true, false>, g, blk, sh.lds, st, xs, codes, scales, n, t);
-  if (sh.nt_stores) return launch_k(k_quant_fp8<V, false, true>, g, blk, sh.lds, st, xs, codes, scales, n, t);
-  return launch_k(k_quant_fp8<V, false, false>, g, blk, sh.lds, st, xs, codes, scales, n, t);
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_quant_fp8<V, decltype(ntl)::value, decltype(sp)::value>, g, blk, sh.lds, st, xs, codes, scales,
+                    n, t);
+  });
 }
 
 template <int P, int NOUT, int EPL>
@@ -237,13 +236,10 @@ hipError_t reduce_e(const Shape& sh, hipStream_t st, const ByteIn& codes, const 
   if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
   const unsigned g = (unsigned)blocks;
   const dim3 blk(sh.block);
-  if (sh.nt_loads && sh.nt_stores)
-    return launch_k(k_reduce_fp8<P, NOUT, EPL, true, true>, g, blk, sh.lds, st, codes, scales, out, n);
-  if (sh.nt_loads)
-    return launch_k(k_reduce_fp8<P, NOUT, EPL, true, false>, g, blk, sh.lds, st, codes, scales, out, n);
-  if (sh.nt_stores)
-    return launch_k(k_reduce_fp8<P, NOUT, EPL, false, true>, g, blk, sh.lds, st, codes, scales, out, n);
-  return launch_k(k_reduce_fp8<P, NOUT, EPL, false, false>, g, blk, sh.lds, st, codes, scales, out, n);
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_reduce_fp8<P, NOUT, EPL, decltype(ntl)::value, decltype(sp)::value>, g, blk, sh.lds, st, codes,
+                    scales, out, n);
+  });
 }
 
 // The shape's vec counts 16-byte output groups per lane: 1 -> 8 elements,

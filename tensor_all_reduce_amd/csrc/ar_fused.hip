@@ -70,24 +70,25 @@ __device__ __forceinline__ void wave_flush(const WaveErr& e, uint64_t* err) {
 // every wavefront store instruction one contiguous 1 KiB: with WPL = 4 each
 // lane stores two adjacent 16-byte groups, so each instruction covers a
 // 2 KiB span half-filled, and that measured 8% slower.
-template <int WPL, bool NTL, bool NTS>
+template <int WPL, bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_pack(const void* x, uint64_t* w, size_t n, uint32_t seq) {
   const size_t nl = (n >> 1) / WPL;
-  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t v0 = (size_t)blockIdx.x * blockDim.x;  // the workgroup's first lane
+  const size_t v = v0 + threadIdx.x;
   if (v < nl) {
     u32x4* dst = reinterpret_cast<u32x4*>(w);
     if constexpr (WPL == 2) {
       const uint64_t d = ld8<NTL>(static_cast<const uint64_t*>(x) + v);
       u32x4 a;
       a[0] = (uint32_t)d; a[1] = seq; a[2] = (uint32_t)(d >> 32); a[3] = seq;
-      st4<NTS>(dst + v, a);
+      st16<SP>(dst + v0, blockDim.x * 16u, threadIdx.x * 16u, a);
     } else {
       const u32x4 d = ld4<NTL>(static_cast<const u32x4*>(x) + v);
       u32x4 a, b;
       a[0] = d[0]; a[1] = seq; a[2] = d[1]; a[3] = seq;
       b[0] = d[2]; b[1] = seq; b[2] = d[3]; b[3] = seq;
-      st4<NTS>(dst + 2 * v, a);
-      st4<NTS>(dst + 2 * v + 1, b);
+      st16<SP>(dst + 2 * v0, blockDim.x * 32u, threadIdx.x * 32u, a);
+      st16<SP>(dst + 2 * v0, blockDim.x * 32u, threadIdx.x * 32u + 16u, b);
     }
   }
   // tail: n is even, so fewer than WPL whole data words remain
@@ -101,24 +102,26 @@ __global__ __launch_bounds__(kMaxBlock) void k_pack(const void* x, uint64_t* w, 
 // Unpack + validate: lane v reads payload words [WPL*v, WPL*v + WPL) and
 // writes their data words (WPL = 2: one 16-byte load, one 8-byte store, each
 // wavefront instruction contiguous; WPL = 4: two adjacent 16-byte loads).
-template <int WPL, bool NTL, bool NTS>
+template <int WPL, bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_unpack(const uint64_t* w, void* x, size_t n, uint32_t seq,
                                                      uint64_t* err) {
   const size_t nl = (n >> 1) / WPL;
-  const size_t v = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t v0 = (size_t)blockIdx.x * blockDim.x;
+  const size_t v = v0 + threadIdx.x;
   const bool act = v < nl;
   const u32x4* src = reinterpret_cast<const u32x4*>(w);
   u32x4 a = {0u, seq, 0u, seq}, b = {0u, seq, 0u, seq};
   if (act) {
     if constexpr (WPL == 2) {
       a = ld4<NTL>(src + v);
-      st8<NTS>(static_cast<uint64_t*>(x) + v, (uint64_t)a[0] | ((uint64_t)a[2] << 32));
+      st8p<SP>(static_cast<uint64_t*>(x) + v0, blockDim.x * 8u, threadIdx.x * 8u,
+               (uint64_t)a[0] | ((uint64_t)a[2] << 32));
     } else {
       a = ld4<NTL>(src + 2 * v);
       b = ld4<NTL>(src + 2 * v + 1);
       u32x4 d;
       d[0] = a[0]; d[1] = a[2]; d[2] = b[0]; d[3] = b[2];
-      st4<NTS>(static_cast<u32x4*>(x) + v, d);
+      st16<SP>(static_cast<u32x4*>(x) + v0, blockDim.x * 16u, threadIdx.x * 16u, d);
     }
   }
   const bool b0 = a[1] != seq, b1 = a[3] != seq, b2 = b[1] != seq, b3 = b[3] != seq;
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_unpack(const uint64_t* w, void* x
 // once per element and stored to all P outputs.  ROUND_EACH: every internal
 // node is rounded to bf16, as the exchanged payload is bf16; otherwise the
 // partials stay binary32 and are rounded once.
-template <int P, int V, bool ROUND_EACH, bool NTL, bool NTS>
+template <int P, int V, bool ROUND_EACH, bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_rd_fused(WordIn in, WordOut out, size_t W, uint32_t seq0,
                                                        uint64_t* err) {
   constexpr uint32_t L = P == 2 ? 1 : (P == 4 ? 2 : 3);
@@ -161,7 +164,8 @@ __global__ __launch_bounds__(kMaxBlock) void k_rd_fused(WordIn in, WordOut out, 
   const size_t nvec = W >> 1;
   // a workgroup owns V * blockDim consecutive groups; all V * P loads are
   // issued before any arithmetic
-  const size_t base = (size_t)blockIdx.x * V * blockDim.x + threadIdx.x;
+  const size_t wg0 = (size_t)blockIdx.x * V * blockDim.x;  // the workgroup's first group
+  const size_t base = wg0 + threadIdx.x;
   u32x4 a[V][P];
   bool any = false;
 #pragma unroll
@@ -216,7 +220,9 @@ __global__ __launch_bounds__(kMaxBlock) void k_rd_fused(WordIn in, WordOut out, 
       o[2] = pack_bf16x2(f[0][2], f[0][3]);
       o[3] = seq_out;
 #pragma unroll
-      for (int p = 0; p < P; ++p) st4<NTS>(reinterpret_cast<u32x4*>(out.p[p]) + v, o);
+      for (int p = 0; p < P; ++p)
+        st16<SP>(reinterpret_cast<u32x4*>(out.p[p]) + wg0, (uint32_t)V * blockDim.x * 16u,
+                 (uint32_t)(v - wg0) * 16u, o);
     }
   }
   // odd word count: the last word, one lane
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_rd_fused(WordIn in, WordOut out, 
 // by exactly one partner, so each is checked once), adds, rounds, and writes
 // the new payload to both ranks' destinations.  One lane per pair makes
 // exact in-place aliasing safe.
-template <bool NTL, bool NTS>
+template <bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_rd_step(WordIn src, WordOut dst, int P, int k, size_t W,
                                                       uint32_t seq_in, uint64_t* err) {
   const unsigned npairs = (unsigned)P >> 1;
@@ -287,8 +293,9 @@ __global__ __launch_bounds__(kMaxBlock) void k_rd_step(WordIn src, WordOut dst, 
     o[1] = seq_out;
     o[2] = pack_bf16x2(lo_f32(a[2]) + lo_f32(b[2]), hi_f32(a[2]) + hi_f32(b[2]));
     o[3] = seq_out;
-    st4<NTS>(reinterpret_cast<u32x4*>(dst.p[r]) + v, o);
-    st4<NTS>(reinterpret_cast<u32x4*>(dst.p[q]) + v, o);
+    const size_t t0 = tile * blockDim.x;
+    st16<SP>(reinterpret_cast<u32x4*>(dst.p[r]) + t0, blockDim.x * 16u, threadIdx.x * 16u, o);
+    st16<SP>(reinterpret_cast<u32x4*>(dst.p[q]) + t0, blockDim.x * 16u, threadIdx.x * 16u, o);
   }
   if (tile == ntiles - 1 && threadIdx.x == 0 && (W & 1)) {
     const size_t j = W - 1;
@@ -403,11 +410,10 @@ hipError_t rd_fused_v(const Shape& sh, hipStream_t st, const WordIn& in, const W
   const size_t gs = cdiv(W >> 1, (size_t)V * sh.block);
   const unsigned g = (unsigned)(gs ? gs : 1);
   const dim3 b(sh.block);
-  if (sh.nt_loads && sh.nt_stores)
-    return launch_k(k_rd_fused<P, V, RE, true, true>, g, b, sh.lds, st, in, out, W, seq0, err);
-  if (sh.nt_loads) return launch_k(k_rd_fused<P, V, RE, true, false>, g, b, sh.lds, st, in, out, W, seq0, err);
-  if (sh.nt_stores) return launch_k(k_rd_fused<P, V, RE, false, true>, g, b, sh.lds, st, in, out, W, seq0, err);
-  return launch_k(k_rd_fused<P, V, RE, false, false>, g, b, sh.lds, st, in, out, W, seq0, err);
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_rd_fused<P, V, RE, decltype(ntl)::value, decltype(sp)::value>, g, b, sh.lds, st, in, out, W,
+                    seq0, err);
+  });
 }
 
 template <int P, bool RE>
@@ -426,10 +432,9 @@ hipError_t pack_w(const Shape& sh, hipStream_t st, const void* x, uint64_t* w, s
   if (!grid_fits(sh, nl)) return hipErrorInvalidConfiguration;
   const unsigned g = flat_grid(sh, nl);
   const dim3 b(sh.block);
-  if (sh.nt_loads && sh.nt_stores) return launch_k(k_pack<WPL, true, true>, g, b, sh.lds, st, x, w, n, seq);
-  if (sh.nt_loads) return launch_k(k_pack<WPL, true, false>, g, b, sh.lds, st, x, w, n, seq);
-  if (sh.nt_stores) return launch_k(k_pack<WPL, false, true>, g, b, sh.lds, st, x, w, n, seq);
-  return launch_k(k_pack<WPL, false, false>, g, b, sh.lds, st, x, w, n, seq);
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_pack<WPL, decltype(ntl)::value, decltype(sp)::value>, g, b, sh.lds, st, x, w, n, seq);
+  });
 }
 
 template <int WPL>
@@ -439,10 +444,9 @@ hipError_t unpack_w(const Shape& sh, hipStream_t st, const uint64_t* w, void* x,
   if (!grid_fits(sh, nl)) return hipErrorInvalidConfiguration;
   const unsigned g = flat_grid(sh, nl);
   const dim3 b(sh.block);
-  if (sh.nt_loads && sh.nt_stores) return launch_k(k_unpack<WPL, true, true>, g, b, sh.lds, st, w, x, n, seq, d_err);
-  if (sh.nt_loads) return launch_k(k_unpack<WPL, true, false>, g, b, sh.lds, st, w, x, n, seq, d_err);
-  if (sh.nt_stores) return launch_k(k_unpack<WPL, false, true>, g, b, sh.lds, st, w, x, n, seq, d_err);
-  return launch_k(k_unpack<WPL, false, false>, g, b, sh.lds, st, w, x, n, seq, d_err);
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_unpack<WPL, decltype(ntl)::value, decltype(sp)::value>, g, b, sh.lds, st, w, x, n, seq, d_err);
+  });
 }
 
 // For pack and unpack the shape's vec counts 16-byte groups of bf16 per lane:
@@ -503,11 +507,10 @@ hipError_t launch_rd_staged(const Launch& L, const WordIn& in, const WordOut& ou
       d.p[r] = k == steps - 1 ? out.p[r] : mailbox + ((size_t)k * P + r) * Ws;
     }
     const uint32_t sk = seq0 + (uint32_t)k;
-    hipError_t e;
-    if (sh.nt_loads && sh.nt_stores) e = launch_k(k_rd_step<true, true>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
-    else if (sh.nt_loads) e = launch_k(k_rd_step<true, false>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
-    else if (sh.nt_stores) e = launch_k(k_rd_step<false, true>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
-    else e = launch_k(k_rd_step<false, false>, grid, b, sh.lds, L.stream, s, d, P, k, W, sk, d_err);
+    const hipError_t e = with_policy(sh, [&](auto ntl, auto sp) {
+      return launch_k(k_rd_step<decltype(ntl)::value, decltype(sp)::value>, grid, b, sh.lds, L.stream, s, d, P, k, W,
+                      sk, d_err);
+    });
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -523,7 +526,7 @@ hipError_t launch_unpack_wait(const Launch& L, const uint64_t* w, void* x, size_
   if (g == 0) g = 1;
   const dim3 b(sh.block);
   // no LDS request here: the producer's workgroups must always fit beside these
-  if (sh.nt_stores) return launch_k(k_unpack_wait<true>, (unsigned)g, b, 0, L.stream, w, x, n, seq, max_spins, d_err);
+  if (sh.stores & 1) return launch_k(k_unpack_wait<true>, (unsigned)g, b, 0, L.stream, w, x, n, seq, max_spins, d_err);
   return launch_k(k_unpack_wait<false>, (unsigned)g, b, 0, L.stream, w, x, n, seq, max_spins, d_err);
 }
 

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ar.h"
 
 namespace ar {
@@ -23,7 +25,7 @@ struct Shape {
   int vec;        // 1 or 2: work per lane (16-byte groups per buffer for the
                   // reduces; the lane width for pack, unpack and the fp8 reduce)
   int nt_loads;   // 1: non-temporal loads of streamed inputs
-  int nt_stores;  // 1: non-temporal stores of outputs
+  int stores;     // output store policy: 0 plain, 1 NT, 2 SC1, 3 SC1 + NT (st16)
   int wg_per_cu;  // 0: no cap
   unsigned lds;   // resolved dynamic LDS bytes per workgroup
 };
@@ -56,7 +58,7 @@ enum Kind {
 // cache and the shape table (read once).
 struct Launch {
   int cus;             // compute units on the current device
-  Shape shape[kKinds];
+  const Shape* shape;  // kKinds resolved shapes (an immutable per-device table)
   hipStream_t stream;
 };
 
@@ -64,6 +66,32 @@ struct Launch {
 // most AR_SMALL_ELEMS elements takes its small-message kind.
 inline const Shape& shape_for(const Launch& L, Kind large, Kind small, size_t n) {
   return n <= (size_t)AR_SMALL_ELEMS ? L.shape[small] : L.shape[large];
+}
+
+// Calls f(NTL, SP) with the shape's load hint and store policy as
+// compile-time constants (std::integral_constant), so a launcher picks the
+// kernel instantiation in one place.
+template <int S> using SPc = std::integral_constant<int, S>;
+template <typename F>
+inline hipError_t with_policy(bool nt_loads, int stores, F&& f) {
+  if (nt_loads) {
+    switch (stores) {
+      case 0: return f(std::true_type{}, SPc<0>{});
+      case 1: return f(std::true_type{}, SPc<1>{});
+      case 2: return f(std::true_type{}, SPc<2>{});
+      default: return f(std::true_type{}, SPc<3>{});
+    }
+  }
+  switch (stores) {
+    case 0: return f(std::false_type{}, SPc<0>{});
+    case 1: return f(std::false_type{}, SPc<1>{});
+    case 2: return f(std::false_type{}, SPc<2>{});
+    default: return f(std::false_type{}, SPc<3>{});
+  }
+}
+template <typename F>
+inline hipError_t with_policy(const Shape& sh, F&& f) {
+  return with_policy(sh.nt_loads != 0, sh.stores, static_cast<F&&>(f));
 }
 
 // Pointer bundles passed to kernels by value (kernel arguments), so no
@@ -91,6 +119,9 @@ hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                           size_t e0, size_t e1, size_t chunk_elems, int two_stage,
                           const ChunkSignal& sig);
+// Whether launch_chunked's grid for [e0, e1) fits a launch (checked by the
+// API layer before any launch of a multi-launch call).
+bool chunked_fits(const Launch& L, size_t e0, size_t e1, size_t chunk_elems, int two_stage, bool flags);
 
 hipError_t launch_quant_fp8(const Launch& L, const InPtrs& xs, const ByteOut& codes,
                             const ByteOut& scales, int P, size_t n);

@@ -39,8 +39,9 @@ namespace ar {
 // (write mode).  Every group is reduced by exactly one lane, which reads it
 // from every input before writing it, so an output equal to an input is safe.
 //
-// SIG: the workgroups of a chunk also publish its completion.  Every output
-// store is device-coherent (written through past the XCD's L2), each wave
+// Outputs are stored with policy SP (st16).  SIG: the workgroups of a chunk
+// also publish its completion.  Every output store is then device-coherent
+// (SP is 2 or 3: written through past the XCD's L2), each wave
 // waits until its stores are acknowledged, the workgroup meets at a barrier,
 // and one lane adds 1 to the chunk's tile counter; the workgroup that
 // completes the count resets the counter to zero (ready for the next call)
@@ -50,7 +51,7 @@ namespace ar {
 // increment follows its workgroup's acknowledged stores, so a consumer that
 // acquire-loads done[chunk] == epoch (which invalidates its own L2 and L1
 // copies) sees the whole chunk of every output.
-template <int P, int NOUT, int V, bool NTL, bool NTS, bool SIG>
+template <int P, int NOUT, int V, bool NTL, int SP, bool SIG>
 __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, size_t e0, size_t e1,
                                                      size_t chunk, unsigned bpc, ChunkSignal sig) {
   const size_t span = (size_t)V * blockDim.x * 8;
@@ -62,6 +63,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
   if (b0 >= c1) return;
   const size_t b1 = b0 + span < c1 ? b0 + span : c1;
   const size_t vb0 = (b0 + 7) >> 3, vb1 = b1 >> 3;
+  static_assert(!SIG || SP >= 2, "completion flags need write-through stores");
 
   u32x4 x[V][P];
 #pragma unroll
@@ -78,13 +80,8 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
     if (v < vb1) {
       const u32x4 r = reduce8<P>(x[u]);
 #pragma unroll
-      for (int o = 0; o < NOUT; ++o) {
-        if constexpr (SIG)
-          st4_coherent<NTS>(static_cast<u32x4*>(out.p[o]) + vb0, (uint32_t)((vb1 - vb0) * 16),
-                            (uint32_t)((v - vb0) * 16), r);
-        else
-          st4<NTS>(static_cast<u32x4*>(out.p[o]) + v, r);
-      }
+      for (int o = 0; o < NOUT; ++o)
+        st16<SP>(static_cast<u32x4*>(out.p[o]) + vb0, (uint32_t)((vb1 - vb0) * 16), (uint32_t)((v - vb0) * 16), r);
     }
   }
   // element-wise head [b0, min(8*vb0, b1)) and tail [max(8*vb1, 8*vb0), b1)
@@ -126,18 +123,24 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
 // 8 XCDs round-robin, so with P = 8 shard s is reduced (and later gathered)
 // by XCD s alone -- the one-GPU picture of "rank s owns shard s" -- and the
 // gather re-reads scratch lines through the L2 that wrote them.
-template <int P, bool NTL>
+//
+// The ragged tail (n not a multiple of 8) lies in the last non-empty shard;
+// trailing shards past it are empty (lo == hi == n) and do nothing, so the
+// tail elements are written by one workgroup only.
+template <int P, bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_rs(InPtrs in, void* scratch, size_t n, size_t S) {
   const unsigned s = blockIdx.x % P;
   const size_t j = blockIdx.x / P;
   const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
   const size_t hi = lo + S < n ? lo + S : n;
-  const size_t v = (lo >> 3) + j * blockDim.x + threadIdx.x;
+  if (lo >= hi) return;
+  const size_t w0 = (lo >> 3) + j * blockDim.x;  // this workgroup's first group
+  const size_t v = w0 + threadIdx.x;
   if (v < (hi >> 3)) {
     u32x4 a[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(static_cast<const u32x4*>(in.p[p]) + v);
-    static_cast<u32x4*>(scratch)[v] = reduce8<P>(a);
+    st16<SP>(static_cast<u32x4*>(scratch) + w0, blockDim.x * 16u, threadIdx.x * 16u, reduce8<P>(a));
   }
   if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
     const size_t i = ((hi >> 3) << 3) + threadIdx.x;
@@ -148,17 +151,19 @@ __global__ __launch_bounds__(kMaxBlock) void k_rs(InPtrs in, void* scratch, size
   }
 }
 
-template <int P, bool NTS>
+template <int P, bool NTL, int SP>
 __global__ __launch_bounds__(kMaxBlock) void k_ag(const void* scratch, OutPtrs out, size_t n, size_t S) {
   const unsigned s = blockIdx.x % P;
   const size_t j = blockIdx.x / P;
   const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
   const size_t hi = lo + S < n ? lo + S : n;
-  const size_t v = (lo >> 3) + j * blockDim.x + threadIdx.x;
+  if (lo >= hi) return;
+  const size_t w0 = (lo >> 3) + j * blockDim.x;
+  const size_t v = w0 + threadIdx.x;
   if (v < (hi >> 3)) {
-    const u32x4 a = static_cast<const u32x4*>(scratch)[v];
+    const u32x4 a = ld4<NTL>(static_cast<const u32x4*>(scratch) + v);
 #pragma unroll
-    for (int p = 0; p < P; ++p) st4<NTS>(static_cast<u32x4*>(out.p[p]) + v, a);
+    for (int p = 0; p < P; ++p) st16<SP>(static_cast<u32x4*>(out.p[p]) + w0, blockDim.x * 16u, threadIdx.x * 16u, a);
   }
   if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
     const size_t i = ((hi >> 3) << 3) + threadIdx.x;
@@ -181,22 +186,19 @@ hipError_t range_v(const Shape& sh, hipStream_t st, const InPtrs& in, const OutP
   if (blocks > 0x7FFFFFFFull || bpc > 0xFFFFFFFFull) return hipErrorInvalidConfiguration;
   const unsigned g = (unsigned)blocks, b = (unsigned)bpc;
   const dim3 blk(sh.block);
-  if (sig.done != nullptr) {
-    if (sh.nt_loads && sh.nt_stores)
-      return launch_k(k_reduce<P, NOUT, V, true, true, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
-    if (sh.nt_loads)
-      return launch_k(k_reduce<P, NOUT, V, true, false, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
-    if (sh.nt_stores)
-      return launch_k(k_reduce<P, NOUT, V, false, true, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
-    return launch_k(k_reduce<P, NOUT, V, false, false, true>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
+  if (sig.done != nullptr) {  // flagged: write-through stores (SC1), NT hint from the shape
+    auto go = [&](auto ntl, auto sp) {
+      return launch_k(k_reduce<P, NOUT, V, decltype(ntl)::value, decltype(sp)::value, true>, g, blk, sh.lds, st,
+                      in, out, e0, e1, chunk, b, sig);
+    };
+    const bool nt = (sh.stores & 1) != 0;
+    if (sh.nt_loads) return nt ? go(std::true_type{}, SPc<3>{}) : go(std::true_type{}, SPc<2>{});
+    return nt ? go(std::false_type{}, SPc<3>{}) : go(std::false_type{}, SPc<2>{});
   }
-  if (sh.nt_loads && sh.nt_stores)
-    return launch_k(k_reduce<P, NOUT, V, true, true, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
-  if (sh.nt_loads)
-    return launch_k(k_reduce<P, NOUT, V, true, false, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
-  if (sh.nt_stores)
-    return launch_k(k_reduce<P, NOUT, V, false, true, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
-  return launch_k(k_reduce<P, NOUT, V, false, false, false>, g, blk, sh.lds, st, in, out, e0, e1, chunk, b, sig);
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_reduce<P, NOUT, V, decltype(ntl)::value, decltype(sp)::value, false>, g, blk, sh.lds, st,
+                    in, out, e0, e1, chunk, b, sig);
+  });
 }
 
 template <int P, int NOUT>
@@ -212,16 +214,18 @@ hipError_t staged_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_
   const Shape& rs = L.shape[kRS];
   const Shape& ag = L.shape[kAG];
   const size_t bps_rs = cdiv(S / 8, (size_t)rs.block), bps_ag = cdiv(S / 8, (size_t)ag.block);
+  // both grids are checked before the first launch
   if (bps_rs * P > 0x7FFFFFFFull || bps_ag * P > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
   const unsigned g_rs = (unsigned)(bps_rs * P), g_ag = (unsigned)(bps_ag * P);
-  hipError_t e = rs.nt_loads
-                     ? launch_k(k_rs<P, true>, g_rs, dim3(rs.block), rs.lds, L.stream, in, scratch, n, S)
-                     : launch_k(k_rs<P, false>, g_rs, dim3(rs.block), rs.lds, L.stream, in, scratch, n, S);
+  hipError_t e = with_policy(rs, [&](auto ntl, auto sp) {
+    return launch_k(k_rs<P, decltype(ntl)::value, decltype(sp)::value>, g_rs, dim3(rs.block), rs.lds, L.stream, in,
+                    scratch, n, S);
+  });
   if (e != hipSuccess) return e;
-  return ag.nt_stores ? launch_k(k_ag<P, true>, g_ag, dim3(ag.block), ag.lds, L.stream,
-                                 (const void*)scratch, out, n, S)
-                      : launch_k(k_ag<P, false>, g_ag, dim3(ag.block), ag.lds, L.stream,
-                                 (const void*)scratch, out, n, S);
+  return with_policy(ag, [&](auto ntl, auto sp) {
+    return launch_k(k_ag<P, decltype(ntl)::value, decltype(sp)::value>, g_ag, dim3(ag.block), ag.lds, L.stream,
+                    (const void*)scratch, out, n, S);
+  });
 }
 
 }  // namespace
@@ -253,6 +257,15 @@ hipError_t launch_2stage_fused(const Launch& L, const InPtrs& in, const OutPtrs&
 hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                                 size_t n, void* scratch) {
   AR_DISPATCH_P(P, (staged_p<PP>(L, in, out, n, scratch)))
+}
+
+// The grid check of range_v, without launching.
+bool chunked_fits(const Launch& L, size_t e0, size_t e1, size_t chunk_elems, int two_stage, bool flags) {
+  const Shape& sh = flags ? L.shape[kUbatchFlags] : (two_stage ? L.shape[kUbatch] : L.shape[kOneshot]);
+  const size_t span = (size_t)(sh.vec == 2 ? 2 : 1) * sh.block * 8;
+  const size_t bpc = cdiv(chunk_elems, span);
+  const size_t nchunks = cdiv(e1 - e0, chunk_elems);
+  return bpc <= 0x7FFFFFFFull && nchunks <= 0x7FFFFFFFull / bpc;
 }
 
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,

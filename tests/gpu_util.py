@@ -1,7 +1,10 @@
 """Helpers for the GPU tests: host <-> device copies of bf16 bit patterns and
-payload words, sampled oracle checks at full size.  No arithmetic of the
-method lives here."""
+payload words, block-wise downloads for the full-size checks, and a thread
+pool that runs an oracle function over slices of a block.  No arithmetic of
+the method lives here."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -68,3 +71,47 @@ def gather_ranks(ins, idx: np.ndarray):
 def gather(t: torch.Tensor, idx: np.ndarray) -> np.ndarray:
     ti = torch.from_numpy(idx.astype(np.int64)).to(DEV)
     return down16(bits16(t)[ti])
+
+
+def blocks(n: int, step: int):
+    """[a, b) ranges of at most `step` covering [0, n)."""
+    for a in range(0, n, step):
+        yield a, min(n, a + step)
+
+
+def down16_range(t: torch.Tensor, a: int, b: int) -> np.ndarray:
+    return down16(bits16(t)[a:b])
+
+
+def down64_range(t: torch.Tensor, a: int, b: int) -> np.ndarray:
+    return down64(t[a:b])
+
+
+def host_threads() -> int:
+    """Threads for the host-side oracle: the cores this process may use,
+    at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+_POOL = None
+
+
+def pmap_slices(fn, arrays, n: int, parts: int | None = None):
+    """fn applied to aligned slices [a, b) of every array in `arrays` (each
+    of length n), split over host threads; returns the list of results in
+    slice order.  The oracle is a ctypes library, which releases the GIL."""
+    global _POOL
+    parts = parts or host_threads()
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=host_threads())
+    step = -(-n // parts)
+    step += (-step) % 8
+    cuts = [(a, min(n, a + step)) for a in range(0, n, step)]
+    futs = [_POOL.submit(fn, [x[a:b] for x in arrays]) for a, b in cuts]
+    return [f.result() for f in futs]
+
+
+def first_mismatch(got: np.ndarray, want: np.ndarray):
+    """(count, first index) of elements where got != want; (0, None) if none."""
+    bad = np.flatnonzero(got != want)
+    return (int(bad.size), int(bad[0])) if bad.size else (0, None)
