@@ -64,6 +64,7 @@ extern "C" {
 #define AR_ERR_ALIAS       -3  /* partial overlap between buffers              */
 #define AR_ERR_UNSUPPORTED -4  /* e.g. recursive doubling with P not 2^k       */
 #define AR_ERR_HIP         -5  /* a HIP runtime call or kernel launch failed   */
+#define AR_ERR_SIZE        -6  /* n beyond the library's static scratch        */
 
 #define AR_MAX_RANKS 8         /* simulated ranks per call: 1..8               */
 
@@ -111,6 +112,26 @@ int ar_reduce_oneshot(const void* const* ins, int P, void* out, size_t n, void* 
  */
 int ar_reduce_2stage(const void* const* ins, void* const* outs, int P, size_t n,
                      void* scratch, void* stream);
+
+/*
+ * Staged two-stage reduce that allocates nothing and takes no workspace: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same result and
+ * kernels as ar_reduce_2stage with a scratch buffer, but the scratch is the
+ * library's own static device array of AR_STATIC_SCRATCH_ELEMS bf16 values
+ * (32 MiB), one per GPU, held from library load until the process ends.
+ *   n      at most AR_STATIC_SCRATCH_ELEMS; a larger n returns AR_ERR_SIZE
+ *          and queues nothing.
+ * Every call on one GPU uses that GPU's one array: calls whose executions
+ * overlap on the same GPU (on different streams, or from different threads)
+ * race on it and give undefined results.  Calls in stream order are safe.
+ * The array keeps the last call's reduced values; nothing in it needs to
+ * start at zero (each call writes every element it later reads).
+ * Errors: as ar_reduce_2stage, plus AR_ERR_SIZE; AR_ERR_HIP if the array's
+ * device address could not be obtained.
+ */
+#define AR_STATIC_SCRATCH_ELEMS 16777216
+int ar_reduce_2stage_static(const void* const* ins, void* const* outs, int P, size_t n, void* stream);
 
 /*
  * Pack bf16 data into fused 8-byte payload words ([NVRAR] Optimizations,

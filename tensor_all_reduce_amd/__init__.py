@@ -19,10 +19,10 @@ from typing import Sequence
 
 __all__ = [
     "ARError", "lib", "lib_path", "ar_status_str", "ar_version", "ar_reduce_oneshot",
-    "ar_reduce_2stage", "ar_pack_fused", "ar_unpack_fused", "ar_rd_schedule",
+    "ar_reduce_2stage", "ar_reduce_2stage_static", "ar_pack_fused", "ar_unpack_fused", "ar_rd_schedule",
     "ar_reduce_ubatch", "ar_err_init", "rd_mailbox_words",
     "AR_OK", "AR_ERR_INVALID", "AR_ERR_ALIGN", "AR_ERR_ALIAS", "AR_ERR_UNSUPPORTED",
-    "AR_ERR_HIP", "AR_MAX_RANKS", "AR_VARIANT_ONESHOT", "AR_VARIANT_2STAGE",
+    "AR_ERR_HIP", "AR_ERR_SIZE", "AR_STATIC_SCRATCH_ELEMS", "AR_MAX_RANKS", "AR_VARIANT_ONESHOT", "AR_VARIANT_2STAGE",
     "AR_RD_STAGED", "AR_RD_FP32_CARRY", "ar_set_launch_shape", "ar_get_launch_shape",
     "AR_KERNEL_ONESHOT", "AR_KERNEL_2STAGE", "AR_KERNEL_UBATCH", "AR_KERNEL_RS", "AR_KERNEL_AG",
     "AR_KERNEL_PACK", "AR_KERNEL_UNPACK", "AR_KERNEL_RD", "AR_KERNEL_RDSTEP", "AR_KERNEL_UNPACK_WAIT",
@@ -40,6 +40,8 @@ AR_ERR_ALIGN = -2
 AR_ERR_ALIAS = -3
 AR_ERR_UNSUPPORTED = -4
 AR_ERR_HIP = -5
+AR_ERR_SIZE = -6
+AR_STATIC_SCRATCH_ELEMS = 16777216
 AR_MAX_RANKS = 8
 AR_VARIANT_ONESHOT = 0
 AR_VARIANT_2STAGE = 1
@@ -102,6 +104,8 @@ def lib():
         L.ar_reduce_2stage.restype = ctypes.c_int
         L.ar_reduce_2stage.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz,
                                        _vp, _vp]
+        L.ar_reduce_2stage_static.restype = ctypes.c_int
+        L.ar_reduce_2stage_static.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int, _sz, _vp]
         L.ar_pack_fused.restype = ctypes.c_int
         L.ar_pack_fused.argtypes = [_vp, _vp, _sz, _u32, _vp]
         L.ar_unpack_fused.restype = ctypes.c_int
@@ -209,6 +213,18 @@ def ar_reduce_2stage(ins: Sequence, outs: Sequence, scratch=None, n: int | None 
     sp = None if scratch is None else _bufs([scratch], 2, "scratch", n)[0]
     _check(lib().ar_reduce_2stage(_ptr_array(ip), _ptr_array(op), len(ip), n, sp, _stream(stream)),
            "ar_reduce_2stage")
+
+
+def ar_reduce_2stage_static(ins: Sequence, outs: Sequence, n: int | None = None, stream=None) -> None:
+    """The staged two-stage reduce through the library's static scratch (no
+    allocation, no workspace argument); n <= AR_STATIC_SCRATCH_ELEMS."""
+    n = ins[0].numel() if n is None else int(n)
+    ip = _bufs(ins, 2, "ins", n)
+    op = _bufs(outs, 2, "outs", n)
+    if len(op) != len(ip):
+        raise ValueError("need one output per rank")
+    _check(lib().ar_reduce_2stage_static(_ptr_array(ip), _ptr_array(op), len(ip), n, _stream(stream)),
+           "ar_reduce_2stage_static")
 
 
 def ar_pack_fused(x, words, seq: int, n: int | None = None, stream=None) -> None:

@@ -86,11 +86,19 @@ static_assert(ar::kOneshot == AR_KERNEL_ONESHOT && ar::k2Stage == AR_KERNEL_2STA
 // their LDS requests resolved for it.  Never modified once published.
 struct Table {
   int cus;
+  void* scratch;  // device address of the static scratch array (nullptr: unavailable)
   ar::Shape shape[ar::kKinds];
 };
 
+// Scratch of ar_reduce_2stage_static.  In host code this name is only a
+// stand-in for the symbol: each device's address of the array comes from
+// hipGetSymbolAddress (stored in DevAttr::scratch / Table::scratch), and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) uint16_t scratch[AR_STATIC_SCRATCH_ELEMS];
+
 struct DevAttr {
   int cus = 0, lds_per_cu = 0, lds_per_block = 0;
+  void* scratch = nullptr;  // this device's address of the static scratch array
 };
 
 std::mutex g_mu;                              // initialisation and shape changes
@@ -133,6 +141,7 @@ const Table* publish_locked(int dev) {
   const DevAttr& d = g_attr[dev];
   Table* t = new Table;
   t->cus = d.cus;
+  t->scratch = d.scratch;
   for (int k = 0; k < ar::kKinds; ++k) {
     ar::Shape s = g_base[k];
     unsigned lds = 0;
@@ -167,13 +176,22 @@ int resolve(ar::Launch* L, void* stream) {
           hipDeviceGetAttribute(&lblk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
           cus <= 0)
         return AR_ERR_HIP;
-      g_attr[dev] = DevAttr{cus, lcu, lblk};
+      // the static scratch array's address on this device (the device is
+      // current here); a failure leaves it unavailable to the one entry
+      // point that needs it and is reported there
+      void* sp = nullptr;
+      if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess) {
+        sp = nullptr;
+        (void)hipGetLastError();
+      }
+      g_attr[dev] = DevAttr{cus, lcu, lblk, sp};
       init_base_locked();
       t = publish_locked(dev);
     }
   }
   L->cus = t->cus;
   L->shape = t->shape;
+  L->scratch = t->scratch;
   L->stream = static_cast<hipStream_t>(stream);
   return AR_OK;
 }
@@ -247,6 +265,7 @@ const char* ar_status_str(int status) {
     case AR_ERR_ALIAS: return "AR_ERR_ALIAS: buffers partially overlap";
     case AR_ERR_UNSUPPORTED: return "AR_ERR_UNSUPPORTED: unsupported configuration";
     case AR_ERR_HIP: return "AR_ERR_HIP: HIP runtime or launch failure";
+    case AR_ERR_SIZE: return "AR_ERR_SIZE: n exceeds AR_STATIC_SCRATCH_ELEMS, the static scratch";
     default: return "AR_ERR_UNKNOWN";
   }
 }
@@ -293,6 +312,28 @@ int ar_reduce_2stage(const void* const* ins, void* const* outs, int P, size_t n,
   if ((rc = resolve(&L, stream))) return rc;
   if (scratch) return hip_status(ar::launch_2stage_staged(L, in, out, P, n, scratch));
   return hip_status(ar::launch_2stage_fused(L, in, out, P, n));
+}
+
+int ar_reduce_2stage_static(const void* const* ins, void* const* outs, int P, size_t n, void* stream) {
+  ar::InPtrs in{};
+  ar::OutPtrs out{};
+  Span si[AR_MAX_RANKS], so[AR_MAX_RANKS];
+  int rc = check_ranks(ins, P, n, &in, si);
+  if (rc) return rc;
+  if (!outs) return AR_ERR_INVALID;
+  for (int p = 0; p < P; ++p) {
+    if (!outs[p]) return AR_ERR_INVALID;
+    if (!aligned16(outs[p])) return AR_ERR_ALIGN;
+    out.p[p] = outs[p];
+    so[p] = span_of(outs[p], n * 2);
+  }
+  if ((rc = check_outputs(si, P, so, P))) return rc;
+  if (n > (size_t)AR_STATIC_SCRATCH_ELEMS) return AR_ERR_SIZE;
+  if (n == 0) return AR_OK;
+  ar::Launch L;
+  if ((rc = resolve(&L, stream))) return rc;
+  if (!L.scratch) return AR_ERR_HIP;
+  return hip_status(ar::launch_2stage_staged(L, in, out, P, n, L.scratch));
 }
 
 int ar_pack_fused(const void* x, uint64_t* words, size_t n, uint32_t seq, void* stream) {

@@ -59,6 +59,7 @@ enum Kind {
 struct Launch {
   int cus;             // compute units on the current device
   const Shape* shape;  // kKinds resolved shapes (an immutable per-device table)
+  void* scratch;       // this device's static scratch array (ar_reduce_2stage_static)
   hipStream_t stream;
 };
 

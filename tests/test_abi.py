@@ -57,7 +57,7 @@ def test_header_compiles_as_c():
 
 def test_status_strings_and_version():
     assert tar.ar_status_str(0) == "AR_OK"
-    for code in (-1, -2, -3, -4, -5):
+    for code in (-1, -2, -3, -4, -5, -6):
         assert tar.ar_status_str(code).startswith("AR_ERR_")
     assert tar.ar_status_str(123) == "AR_ERR_UNKNOWN"
     assert tar.ar_version() >= 10000
@@ -105,6 +105,19 @@ def test_2stage_validation():
     assert L.ar_reduce_2stage(ins, arr(C, C + 4096), 2, 64, C + 8200, None) == tar.AR_ERR_ALIGN
     # in place (outs == ins) is fine
     assert L.ar_reduce_2stage(ins, arr(A, B), 2, 0, None, None) == tar.AR_OK
+
+
+def test_2stage_static_validation():
+    L = tar.lib()
+    ins = arr(A, B)
+    big = tar.AR_STATIC_SCRATCH_ELEMS
+    assert L.ar_reduce_2stage_static(ins, None, 2, 8, None) == tar.AR_ERR_INVALID
+    assert L.ar_reduce_2stage_static(ins, arr(C, C + 16), 2, 64, None) == tar.AR_ERR_ALIAS
+    assert L.ar_reduce_2stage_static(ins, arr(C + 8, C + 4096), 2, 64, None) == tar.AR_ERR_ALIGN
+    # beyond the static scratch: rejected before any device work
+    assert L.ar_reduce_2stage_static(ins, arr(A, B), 2, big + 8, None) == tar.AR_ERR_SIZE
+    assert tar.ar_status_str(tar.AR_ERR_SIZE).startswith("AR_ERR_SIZE")
+    assert L.ar_reduce_2stage_static(ins, arr(A, B), 2, 0, None) == tar.AR_OK
 
 
 def test_pack_unpack_validation():
