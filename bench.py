@@ -3,14 +3,18 @@
 
 One step = one pass of every hot-path call over one batch: P = 8 simulated
 rank buffers of bf16 [16384 x 8192] (the 16k-token prefill hidden state,
-256 MiB per buffer), N(0,1) values drawn on the GPU from a seeded generator:
+256 MiB per buffer), N(0,1) values, and P = 8 buffers of bf16
+[16384 x 16384] (512 MiB per buffer) with log-uniform magnitudes in
+[2^-8, 2^8] and random signs for the ubatch row, all drawn on the GPU from
+seeded generators:
 
   oneshot   ar_reduce_oneshot            reads 8 buffers, writes 1
   2stage    ar_reduce_2stage (fused)     reads 8, writes 8
   pack      ar_pack_fused x 8            bf16 -> fused payload words (seq s)
   rd        ar_rd_schedule (fused, R1)   3 recursive-doubling steps, 8 payloads
   unpack    ar_unpack_fused x 8          payload -> bf16, seq checked (s + 3)
-  ubatch    ar_reduce_ubatch             2 ubatches of 8192 rows, 2 streams, 1 MiB chunks
+  ubatch    ar_reduce_ubatch             [16384 x 16384]: 2 ubatches of 8192 rows,
+                                         2 streams, 1 MiB chunks, two-stage variant
 
 `value` = credited bytes of the step / step time (GB/s, 1e9 B/s); credited
 bytes count each input read once and each output written once (no scratch).
@@ -19,7 +23,7 @@ Inputs are resident in HBM before the timed region.
 Also reported (not part of `value`): per-call latency of one-shot and
 two-stage at 128 KiB / 512 KiB / 2 MiB per buffer (native timing loop, no
 Python in the loop), the staged two-stage at the prefill size, the ubatch
-reduce at its own [16384 x 16384] shape, the waiting unpack (on ready payloads
+reduce's one-shot variant and its two ubatches on one stream, the waiting unpack (on ready payloads
 and as a producer -> consumer handoff), attainable copy bandwidth (a plain
 copy; eight buffers copied side by side: the 8 -> 8 pattern of the
 two-stage, RD and ubatch rows, for the ubatch split over two streams; and
@@ -27,6 +31,7 @@ eight buffers gathered into one by XOR: the one-shot's 8 -> 1 pattern), and
 the CPU oracle on a bounded sample of the same step (`cpu_baseline`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --ab      A/B of launch shapes and store policies (text report)
 """
 from __future__ import annotations
 
@@ -70,6 +75,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the steps, run 3 plain copies of exactly 1 GiB (counter calibration)")
+    ap.add_argument("--ab", action="store_true",
+                    help="instead of the step: A/B of the launch shapes and store policies of the 8 -> 8 "
+                         "and 8 -> 1 kernels and of the ubatch schedule, as a text report")
     return ap.parse_args()
 
 
@@ -83,10 +91,10 @@ def sha256_files(paths):
 
 def load_traffic(row: str, sources, path: str | None = None):
     """HBM bytes per launch of a row's kernel from the committed rocprofv3
-    counter summary (profiles/traffic_prefill_step.txt, "key: value" lines),
+    counter summary (profiles/traffic_bench_step.txt, "key: value" lines),
     if it was taken on the current kernel sources; else None."""
     if path is None:
-        path = os.path.join(ROOT, "profiles", "traffic_prefill_step.txt")
+        path = os.path.join(ROOT, "profiles", "traffic_bench_step.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -181,9 +189,17 @@ def main():
     words = [e64(W) for _ in range(P)]
     rdo = [e64(W) for _ in range(P)]
     ux = [e16(n) for _ in range(P)]
-    ubo = [e16(n) for _ in range(P)]
     err = e64(2)
     s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    # the ubatch row's own batch: [16384 x 16384] per rank, log-uniform magnitudes
+    n5 = UB_ROWS * UB_HIDDEN
+    B5 = 2 * n5
+    uin = [t.view(torch.int16) for t in synth.device_rank_buffers("logmag", P, n5, 5, dev)]
+    ubo = [e16(n5) for _ in range(P)]
+
+    if args.ab:
+        ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0, s1)
+        return 0
 
     rows = ["oneshot", "2stage", "pack", "rd", "unpack", "ubatch"]
     credited = {
@@ -192,11 +208,13 @@ def main():
         "pack": P * (B + 2 * B),
         "rd": P * 2 * B * 2,
         "unpack": P * (2 * B + B),
-        "ubatch": 2 * P * B,
+        "ubatch": 2 * P * B5,
     }
     launches = {"oneshot": 1, "2stage": 1, "pack": P, "rd": 1, "unpack": P, "ubatch": 2}
+    # the ubatch row's two launches run at the same time on two streams
+    concurrent = {"ubatch"}
     kernel_of = {"oneshot": "k_reduce<8,1>", "2stage": "k_reduce<8,8>", "pack": "k_pack",
-                 "rd": "k_rd_fused<8,R1>", "unpack": "k_unpack", "ubatch": "k_reduce<8,8> chunked"}
+                 "rd": "k_rd_fused<8,R1>", "unpack": "k_unpack", "ubatch": "k_reduce<8,8> chunked, x2 concurrent"}
     step_bytes = sum(credited.values())
 
     def run_row(name, seq):
@@ -216,7 +234,7 @@ def main():
         elif name == "ubatch":
             s0.wait_stream(main_s)
             s1.wait_stream(main_s)
-            tar.ar_reduce_ubatch(ins, ubo, ROWS, HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE,
+            tar.ar_reduce_ubatch(uin, ubo, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE,
                                  [s0, s1])
             main_s.wait_stream(s0)
             main_s.wait_stream(s1)
@@ -244,8 +262,16 @@ def main():
     e = err.cpu().numpy().view(np.uint64)
     assert int(e[0]) == 0, "sequence-number mismatches in the bench step"
     # every output of the step agrees with the one-shot result on device
-    for o in outs + ubo:
-        assert torch.equal(o, out1), "two-stage/ubatch output differs from one-shot"
+    for o in outs:
+        assert torch.equal(o, out1), "two-stage output differs from one-shot"
+    # the ubatch row's outputs agree with the fused two-stage of the same batch
+    # (outs of the other batch are reused as scratch for the check)
+    chk = [e16(n5) for _ in range(2)]
+    tar.ar_reduce_oneshot(uin, chk[0])
+    torch.cuda.synchronize()
+    for o in ubo:
+        assert torch.equal(o, chk[0]), "ubatch output differs from the one-shot of its batch"
+    del chk
     ms_per_step = gpu_ms / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     step_ms = sorted(ev[k][0].elapsed_time(ev[k][len(rows)]) for k in range(K))
@@ -258,24 +284,40 @@ def main():
         per_row[r] = {"kernel": kernel_of[r], "launches": launches[r], "ms": round(row_ms[r], 4),
                       "credited_bytes": credited[r], "GBps": round(gbps, 1),
                       "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+    # the dominant row by time; for a row whose launches run concurrently the
+    # rate is the row's bytes over the row's time (both launches together),
+    # otherwise bytes per launch over the mean launch time
     dom = max(rows, key=lambda r: row_ms[r])
-    dom_launch_ms = row_ms[dom] / launches[dom]
-    dom_bytes = credited[dom] / launches[dom]
+    if dom in concurrent:
+        dom_launch_ms, dom_bytes = row_ms[dom], credited[dom]
+    else:
+        dom_launch_ms, dom_bytes = row_ms[dom] / launches[dom], credited[dom] / launches[dom]
     achieved = dom_bytes / (dom_launch_ms * 1e-3) / 1e9
+    traffic = load_traffic(dom, KERNEL_SOURCES)
+    if traffic is not None and dom in concurrent:
+        traffic *= launches[dom]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                "traffic": load_traffic(dom, KERNEL_SOURCES),
-                "kernel": kernel_of[dom], "algorithmic_bytes_per_launch": dom_bytes,
+                "traffic": traffic,
+                "kernel": kernel_of[dom], "row": dom, "algorithmic_bytes_per_launch": dom_bytes,
                 "avg_launch_ms": round(dom_launch_ms, 4)}
+    if dom in concurrent:
+        roofline["launches"] = launches[dom]
+        roofline["note"] = ("the row's launches run concurrently on two streams: achieved = the row's "
+                            "algorithmic bytes / the row's time (both launches together); "
+                            "avg_launch_ms is that row time")
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "P=8 simulated ranks, bf16 [16384 x 8192] per rank (16k-token prefill "
-                               "hidden state, 256 MiB/buffer), N(0,1); step = one-shot + two-stage + "
-                               "pack + recursive doubling + unpack + 2-ubatch chunked reduce",
-                   "P": P, "shape_per_rank": [ROWS, HIDDEN], "accumulate": "f32",
+        "config": {"workload": "P=8 simulated ranks; one-shot + fused two-stage + pack + recursive doubling "
+                               "+ unpack on bf16 [16384 x 8192] per rank (16k-token prefill hidden state, "
+                               "256 MiB/buffer), N(0,1); two-ubatch chunked two-stage reduce on bf16 "
+                               "[16384 x 16384] per rank (512 MiB/buffer, 2 streams, 1 MiB chunks), "
+                               "log-uniform magnitudes in [2^-8, 2^8]",
+                   "P": P, "shape_per_rank": [ROWS, HIDDEN], "ubatch_shape_per_rank": [UB_ROWS, UB_HIDDEN],
+                   "accumulate": "f32",
                    "step_credited_bytes": step_bytes, "parallelism": "none (one GPU)"},
         "roofline": roofline,
         "rows": per_row,
@@ -297,8 +339,8 @@ def main():
         del src, dst
 
     if not args.no_extras:
-        result.update(extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1))
-        del ins, outs, words, rdo, ux, ubo, out1
+        result.update(extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1, uin, ubo))
+        del ins, outs, words, rdo, ux, ubo, out1, uin
         torch.cuda.empty_cache()
         # the same rates against the attainable bandwidth measured in this run
         for r in rows:
@@ -310,14 +352,15 @@ def main():
                        ("ubatch", "copy_8to8_two_streams_GBps")):
             per_row[r]["frac_of_pattern_copy"] = round(per_row[r]["GBps"] / result[ref], 4)
         roofline["frac_of_copy"] = round(achieved / result["copy_GBps"], 4)
-        roofline["frac_of_pattern_copy"] = round(achieved / result["copy_8to8_GBps"], 4)
+        pattern = {"oneshot": "copy_8to1_GBps", "ubatch": "copy_8to8_two_streams_GBps"}.get(dom, "copy_8to8_GBps")
+        roofline["frac_of_pattern_copy"] = round(achieved / result[pattern], 4)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, np)
     print(json.dumps(result), flush=True)
     return 0
 
 
-def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1):
+def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1, uin, ubo):
     vp = ctypes.c_void_p
     sh = main_s.cuda_stream
     res = {}
@@ -399,14 +442,16 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
                 best1, shape1 = gbps, {"nt_stores": nts, "wg_per_cu": wg}
     res["copy_8to1_GBps"] = round(best1, 1)
     res["copy_8to1_shape"] = shape1
-    # the ubatch row's pattern: the same copy split at the middle row, the two
-    # halves on two streams at once (as the two ubatch reduces run), on the
-    # ubatch streams themselves: HIP maps a process's streams onto a few
-    # hardware queues, and two more streams here could put the later
-    # producer / consumer pair on one queue, where they would run in turn
-    h = n // 2
-    halves = [(parr([x[:h] for x in ins]), parr([o[:h] for o in outs])),
-              (parr([x[h:] for x in ins]), parr([o[h:] for o in outs]))]
+    # the ubatch row's pattern: its own [16384 x 16384] buffers copied 8 -> 8
+    # with no arithmetic, split at the middle row, the two halves on two
+    # streams at once (as the two ubatch reduces run), on the ubatch streams
+    # themselves: HIP maps a process's streams onto a few hardware queues, and
+    # two more streams here could put the later producer / consumer pair on
+    # one queue, where they would run in turn
+    n5 = UB_ROWS * UB_HIDDEN
+    h = n5 // 2
+    halves = [(parr([x[:h] for x in uin]), parr([o[:h] for o in ubo])),
+              (parr([x[h:] for x in uin]), parr([o[h:] for o in ubo]))]
 
     def two_streams(vec, wg):
         s0.wait_stream(main_s)
@@ -428,7 +473,7 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
                 two_streams(vec, wg)
             e1.record(main_s)
             torch.cuda.synchronize()
-            gbps = 2 * P * 2 * n * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            gbps = 2 * P * 2 * n5 * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
             if gbps > best2:
                 best2, shape2 = gbps, {"vec": vec, "wg_per_cu": wg}
     res["copy_8to8_two_streams_GBps"] = round(best2, 1)
@@ -680,60 +725,188 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     res.update(wait_receive(tar, blib, torch, dev, main_s, ins, outs, s0, s1))
     res.update(fp8(tar, torch, dev, main_s, ins, outs))
 
-    # ubatch reduce at its own shape: [16384 x 16384] per rank, 2 streams, 1 MiB chunks
-    from tensor_all_reduce_amd import synth
+    # the ubatch reduce's variants at the row's shape: the one-shot variant
+    # (one output, (P + 1) B credited) on two streams, and the two-stage
+    # variant with both ubatches on one stream (no overlap between them)
     m = UB_ROWS * UB_HIDDEN
-    uin = [t.view(torch.int16) for t in synth.device_rank_buffers("logmag", P, m, 5, dev)]
-    uout = [e16(m) for _ in range(P)]
-
-    def ub():
-        s0.wait_stream(main_s)
-        s1.wait_stream(main_s)
-        tar.ar_reduce_ubatch(uin, uout, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE,
-                             [s0, s1])
-        main_s.wait_stream(s0)
-        main_s.wait_stream(s1)
-
-    for _ in range(3):
-        ub()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 10
-    e0.record(main_s)
-    for _ in range(reps):
-        ub()
-    e1.record(main_s)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    gbps = 2 * P * 2 * m / (ms * 1e-3) / 1e9
-    res["ubatch_16384x16384"] = {"ms": round(ms, 4), "GBps_credited": round(gbps, 1),
-                                 "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                                 "streams": 2, "chunk_bytes": CHUNK_BYTES}
-    log(f"ubatch [16384x16384]: {ms:.3f} ms, {gbps:.0f} GB/s")
 
-    # the one-shot variant at the same shape (one output, (P + 1) B credited)
-    def ub1():
-        s0.wait_stream(main_s)
-        s1.wait_stream(main_s)
-        tar.ar_reduce_ubatch(uin, uout[:1], UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_ONESHOT,
-                             [s0, s1])
-        main_s.wait_stream(s0)
-        main_s.wait_stream(s1)
+    def ub_timed(variant, streams, nout):
+        def go():
+            for st in set(streams):
+                st.wait_stream(main_s)
+            tar.ar_reduce_ubatch(uin, ubo[:nout], UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, variant, streams)
+            for st in set(streams):
+                main_s.wait_stream(st)
+        for _ in range(3):
+            go()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(reps):
+            go()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
 
-    for _ in range(3):
-        ub1()
-    e0.record(main_s)
-    for _ in range(reps):
-        ub1()
-    e1.record(main_s)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ms = ub_timed(tar.AR_VARIANT_ONESHOT, [s0, s1], 1)
     gbps = (P + 1) * 2 * m / (ms * 1e-3) / 1e9
     res["ubatch_16384x16384_oneshot"] = {"ms": round(ms, 4), "GBps_credited": round(gbps, 1),
                                          "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
     log(f"ubatch one-shot [16384x16384]: {ms:.3f} ms, {gbps:.0f} GB/s")
-    del uin, uout
+    ms = ub_timed(tar.AR_VARIANT_2STAGE, [s0, s0], P)
+    gbps = 2 * P * 2 * m / (ms * 1e-3) / 1e9
+    res["ubatch_16384x16384_one_stream"] = {"ms": round(ms, 4), "GBps_credited": round(gbps, 1),
+                                            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                                            "note": "both ubatches on one stream, one after the other"}
+    log(f"ubatch [16384x16384] on one stream: {ms:.3f} ms, {gbps:.0f} GB/s")
     torch.cuda.empty_cache()
     return res
+
+
+def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0, s1):
+    """A/B of launch choices on the bench's own buffers, printed as text.
+
+    For the one-shot (8 -> 1), the fused two-stage (8 -> 8), the fused
+    recursive doubling and the two-stream ubatch reduce, every candidate shape
+    (block, vec, nt_loads, stores, wg_per_cu; stores 1 = non-temporal,
+    2 = SC1 write-through, 3 = SC1 + non-temporal) is set with
+    ar_set_launch_shape and timed with HIP events around `reps` calls;
+    candidates are visited in a shuffled order each round and the median over
+    rounds is reported, so slow drift of the device affects all alike.  The
+    one-shot writes its output to the P output buffers in turn: its 256 MiB
+    output fits the 256 MiB last-level cache, and calls that rewrite one
+    buffer leave it there without ever paying its write-back to HBM.  The
+    ubatch schedule is also run with both ubatches on one stream.  Reference
+    rows time plain copies with each kernel's access pattern (no arithmetic).
+    GB/s counts each input read once and each output written once."""
+    import itertools
+    import random
+    import statistics
+
+    n = ROWS * HIDDEN
+    n5 = UB_ROWS * UB_HIDDEN
+    B, B5 = 2 * n, 2 * n5
+    W = n // 2
+    words = [torch.empty(W, dtype=torch.int64, device=dev) for _ in range(P)]
+    rdo = [torch.empty(W, dtype=torch.int64, device=dev) for _ in range(P)]
+    err = torch.empty(2, dtype=torch.int64, device=dev)
+    for r in range(P):
+        tar.ar_pack_fused(ins[r], words[r], 1)
+    tar.ar_err_init(err)
+    vp = ctypes.c_void_p
+
+    def parr(ts):
+        a = (vp * len(ts))()
+        for i, t in enumerate(ts):
+            a[i] = t.data_ptr()
+        return a
+
+    def ubatch(streams):
+        for st in set(streams):
+            st.wait_stream(main_s)
+        tar.ar_reduce_ubatch(uin, ubo, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, streams)
+        for st in set(streams):
+            main_s.wait_stream(st)
+
+    turn = [0]
+
+    def oneshot_rotating():
+        turn[0] += 1
+        tar.ar_reduce_oneshot(ins, outs[turn[0] % P])
+
+    kinds = {
+        "oneshot": (tar.AR_KERNEL_ONESHOT, (P + 1) * B, oneshot_rotating,
+                    list(itertools.product((64, 128), (1,), (1,), (1, 2, 3), (0, 8, 12, 16)))),
+        "2stage": (tar.AR_KERNEL_2STAGE, 2 * P * B, lambda: tar.ar_reduce_2stage(ins, outs),
+                   list(itertools.product((64,), (1, 2), (1,), (1, 2, 3), (4, 5, 6, 8)))),
+        "rd": (tar.AR_KERNEL_RD, 4 * P * B, lambda: tar.ar_rd_schedule(words, rdo, 1, err),
+               list(itertools.product((64,), (1,), (1,), (1, 2, 3), (6, 8, 10)))),
+        "ubatch_two_streams": (tar.AR_KERNEL_UBATCH, 2 * P * B5, lambda: ubatch([s0, s1]),
+                               list(itertools.product((64,), (1,), (1,), (1, 3), (3, 4, 6, 8)))),
+        "ubatch_one_stream": (tar.AR_KERNEL_UBATCH, 2 * P * B5, lambda: ubatch([s0, s0]),
+                              list(itertools.product((64,), (1,), (1,), (1, 3), (3, 4, 6, 8)))),
+    }
+    reps, rounds = 4, 3
+    rng = random.Random(11)
+
+    def time_calls(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(reps):
+            fn()
+        e1.record(main_s)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    print("# A/B of launch shapes on the bench buffers: P=8, bf16 [16384 x 8192] per rank "
+          "([16384 x 16384] for the ubatch rows)")
+    print(f"# command: python bench.py --ab   ({rounds} shuffled rounds x {reps} calls, median per candidate)")
+    print(f"# device: {torch.cuda.get_device_properties(dev).name}, "
+          f"{torch.cuda.get_device_properties(dev).multi_processor_count} CUs")
+    for name, (kind, cred, fn, cands) in kinds.items():
+        default = tar.ar_get_launch_shape(kind)
+        if default not in cands:
+            cands = cands + [default]
+        times = {c: [] for c in cands}
+        for _ in range(rounds):
+            order = cands[:]
+            rng.shuffle(order)
+            for c in order:
+                tar.ar_set_launch_shape(kind, *c)
+                times[c].append(time_calls(fn))
+        tar.ar_set_launch_shape(kind, *default)
+        med = {c: statistics.median(v) for c, v in times.items()}
+        ranked = sorted(cands, key=lambda c: med[c])
+        best = med[ranked[0]]
+        print(f"== {name}: {cred} algorithmic bytes per call, {len(cands)} shapes")
+        print("   block vec ntl stores wg/cu        ms      GB/s  frac-of-8TB/s  vs-best")
+        for c in ranked:
+            gbps = cred / (med[c] * 1e-3) / 1e9
+            tag = "  <- default" if c == default else ""
+            print(f"   {c[0]:5d} {c[1]:3d} {c[2]:3d} {c[3]:6d} {c[4]:5d} {med[c]:9.4f} {gbps:9.1f}  "
+                  f"{gbps / PEAK_HBM_GBPS:13.4f}  {best / med[c]:7.4f}{tag}")
+        sys.stdout.flush()
+        log(f"ab: {name} done")
+    # references: the same access patterns copied with no arithmetic
+    print("== reference copies (no arithmetic), best over the listed shapes")
+
+    def best_of(fn_by_shape, shapes, cred):
+        out = []
+        for sh in shapes:
+            out.append((time_calls(lambda: fn_by_shape(sh)), sh))
+        t, sh = min(out)
+        return cred / (t * 1e-3) / 1e9, sh
+
+    def copy8(sh):
+        if blib.arb_copy_multi(parr(ins), parr(outs), P, B, sh[0], sh[1], main_s.cuda_stream) != 0:
+            raise RuntimeError("arb_copy_multi failed")
+
+    def gather(sh):
+        if blib.arb_gather_xor(parr(ins), P, out1.data_ptr(), B, sh[0], sh[1], main_s.cuda_stream) != 0:
+            raise RuntimeError("arb_gather_xor failed")
+
+    h = n5 // 2
+    halves = [(parr([x[:h] for x in uin]), parr([o[:h] for o in ubo])),
+              (parr([x[h:] for x in uin]), parr([o[h:] for o in ubo]))]
+
+    def copy_two(sh):
+        s0.wait_stream(main_s)
+        s1.wait_stream(main_s)
+        for (pi, po), st in zip(halves, (s0, s1)):
+            if blib.arb_copy_multi(pi, po, P, 2 * h, sh[0], sh[1], st.cuda_stream) != 0:
+                raise RuntimeError("arb_copy_multi failed")
+        main_s.wait_stream(s0)
+        main_s.wait_stream(s1)
+
+    caps = (0, 4, 5, 6, 8)
+    g, sh = best_of(copy8, [(v, w) for v in (1, 2) for w in caps], 2 * P * B)
+    print(f"   8 -> 8 copy [16384 x 8192]             {g:9.1f} GB/s  (vec, wg/cu) = {sh}")
+    g, sh = best_of(gather, [(nt, w) for nt in (0, 1) for w in (0, 8, 12, 16)], (P + 1) * B)
+    print(f"   8 -> 1 XOR gather [16384 x 8192]       {g:9.1f} GB/s  (nt_stores, wg/cu) = {sh}")
+    g, sh = best_of(copy_two, [(v, w) for v in (1, 2) for w in caps], 2 * P * B5)
+    print(f"   8 -> 8 copy [16384 x 16384], 2 streams {g:9.1f} GB/s  (vec, wg/cu) = {sh}")
+    sys.stdout.flush()
 
 
 def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
@@ -1017,16 +1190,19 @@ def cpu_model() -> str:
 
 def cpu_baseline(args, np):
     """The oracle (single-threaded C, as it stands) on a bounded sample of the
-    same step: the first `rows_s` rows of the [16384 x 8192] workload."""
+    same step: the first `rows_s` rows of both batches -- [rows_s x 8192] for
+    the one-shot, two-stage, pack, RD and unpack rows, [rows_s x 16384] split
+    into two ubatches for the ubatch row."""
     import oracle
     from tensor_all_reduce_amd import synth
 
     def gen(rows_s):
-        return [synth.normal(rows_s * HIDDEN, 4, 0, p) for p in range(P)]
+        return ([synth.normal(rows_s * HIDDEN, 4, 0, p) for p in range(P)],
+                [synth.logmag(rows_s * UB_HIDDEN, 5, 0, p) for p in range(P)])
 
-    def step(rows_s, xs=None, barrier=None):
-        m = rows_s * HIDDEN
-        xs = gen(rows_s) if xs is None else xs
+    def step(rows_s, data=None, barrier=None):
+        m, m5 = rows_s * HIDDEN, rows_s * UB_HIDDEN
+        xs, x5 = gen(rows_s) if data is None else data
         if barrier is not None:
             barrier.wait()
         t0 = time.perf_counter()
@@ -1036,10 +1212,10 @@ def cpu_baseline(args, np):
         rw, _ = oracle.rd(ws, 1)
         for w in rw:
             oracle.unpack(w, 4)
-        oracle.reduce_ubatch(xs, rows_s, HIDDEN, 2, None, CHUNK_BYTES // 2, oracle.TWOSTAGE)
+        oracle.reduce_ubatch(x5, rows_s, UB_HIDDEN, 2, None, CHUNK_BYTES // 2, oracle.TWOSTAGE)
         t1 = time.perf_counter()
-        b = 2 * m
-        cred = (P + 1) * b + 2 * P * b + 3 * P * b + 4 * P * b + 3 * P * b + 2 * P * b
+        b, b5 = 2 * m, 2 * m5
+        cred = (P + 1) * b + 2 * P * b + 3 * P * b + 4 * P * b + 3 * P * b + 2 * P * b5
         if barrier is not None:
             return t0, t1, cred
         return t1 - t0, cred
@@ -1059,17 +1235,18 @@ def cpu_baseline(args, np):
         dt, cred = step(rows_s)
     gbps = cred / dt / 1e9
     res = {"value": round(gbps, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"one full step (all six rows) of the oracle on the first {rows_s} of 16384 rows "
-                     f"(P=8, hidden 8192, N(0,1)); {dt:.1f} s on one host core; credited bytes as the GPU step",
+           "sample": f"one full step (all six rows) of the oracle on the first {rows_s} of 16384 rows of both "
+                     f"batches (P=8; hidden 8192 N(0,1), and hidden 16384 log-uniform for the ubatch row); "
+                     f"{dt:.1f} s on one host core; credited bytes as the GPU step",
            "seconds": round(dt, 2), "cpu_model": cpu_model()}
     if args.no_cpu_all_cores:
         return res
-    # the same oracle on all host cores (at most 16): the step's rows split
-    # over threads, each running the unchanged oracle on its own rows (the C
+    # the same oracle on every host core this process may use: one thread
+    # per core, each running the unchanged oracle on its own rows (the C
     # calls release the interpreter lock)
     import concurrent.futures as cf
     import threading
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores = max(1, len(os.sched_getaffinity(0)))
     rows_t = max(2, min(rows_s, ROWS // cores))
     rows_t -= rows_t % 2
     data = gen(rows_t)                     # every thread reduces the same values

@@ -39,7 +39,7 @@ constexpr int kMaxUbatch = 16;
 // with the best worst case over placements, within 1% of the best for
 // separately allocated buffers.
 constexpr ar::Shape kDefaultShape[] = {
-    {64, 1, 1, 2, 16, 0},   // one-shot, 8 -> 1
+    {64, 1, 1, 1, 8, 0},    // one-shot, 8 -> 1
     {64, 1, 1, 2, 6, 0},    // fused two-stage, 8 -> 8
     {64, 1, 1, 3, 6, 0},    // ubatch, 8 -> 8 on two streams
     {64, 1, 1, 2, 10, 0},   // staged reduce-scatter, 8 -> 1

@@ -46,10 +46,13 @@ ROWS = ["oneshot", "2stage", "pack", "rd", "unpack", "ubatch"]
 LAUNCHES = {"oneshot": 1, "2stage": 1, "pack": P, "rd": 1, "unpack": P, "ubatch": 2}
 PREFIX = {"oneshot": "k_reduce", "2stage": "k_reduce", "pack": "k_pack", "err_init": "k_err_init",
           "rd": "k_rd_fused", "unpack": "k_unpack", "ubatch": "k_reduce"}
-# algorithmic bytes per launch, [16384 x 8192] bf16 per rank buffer
+# algorithmic bytes per launch: [16384 x 8192] bf16 per rank buffer, and
+# [16384 x 16384] for the ubatch row (each of its two launches reduces one
+# 8192-row ubatch of every rank: P * B5 / 2 read, P * B5 / 2 written)
 B = 2 * 16384 * 8192
+B5 = 2 * 16384 * 16384
 ALGO = {"oneshot": (P + 1) * B, "2stage": 2 * P * B, "pack": 3 * B, "rd": 4 * P * B,
-        "unpack": 3 * B, "ubatch": P * B}
+        "unpack": 3 * B, "ubatch": P * B5}
 SOURCES = ["tensor_all_reduce_amd/csrc/ar_device.hpp", "tensor_all_reduce_amd/csrc/ar_reduce.hip",
            "tensor_all_reduce_amd/csrc/ar_fused.hip", "tensor_all_reduce_amd/csrc/ar_api.hip"]
 
@@ -103,7 +106,8 @@ def cmd_stats(a):
             if row == "ubatch":
                 lo, hi = span.get(s, (t0, t1))
                 span[s] = (min(lo, t0), max(hi, t1))
-    print(f"# rocprofv3 kernel trace of the bench step: P=8, bf16 [16384 x 8192] per rank")
+    print(f"# rocprofv3 kernel trace of the bench step: P=8, bf16 [16384 x 8192] per rank "
+          f"([16384 x 16384] for the ubatch row)")
     print(f"# command: {a.command}")
     print(f"# {steps} steps traced, first {a.warmup} are warmup; durations in ms per dispatch")
     print(f"# row      launches/step  mean(timed)  median(timed)  mean(all)  algorithmic GB/s per launch")
@@ -197,7 +201,8 @@ def cmd_pmc(a):
                 if row in per[name]:
                     per[name][row].append(float(r["Counter_Value"]))
     names = sorted(per)
-    print("# rocprofv3 --pmc counters of the bench step kernels (P=8, bf16 [16384 x 8192] per rank),")
+    print("# rocprofv3 --pmc counters of the bench step kernels (P=8, bf16 [16384 x 8192] per rank,")
+    print("# [16384 x 16384] for the ubatch row),")
     print("# mean per dispatch over every dispatch of each run")
     for c in a.command:
         print(f"# command: {c}")
@@ -240,7 +245,8 @@ def cmd_traffic(a):
     fetch, fcopy, fname = counters(a.fetch_dir)
     write, wcopy, wname = counters(a.write_dir)
     fs, ws = a.calib_bytes / fcopy, a.calib_bytes / wcopy
-    print("# HBM traffic per launch of the bench step kernels (P=8, bf16 [16384 x 8192] per rank)")
+    print("# HBM traffic per launch of the bench step kernels (P=8, bf16 [16384 x 8192] per rank,")
+    print("# [16384 x 16384] for the ubatch row)")
     print(f"# fetch command: {a.command_fetch}")
     print(f"# write command: {a.command_write}")
     print(f"# counters: {fname} and {wname}, KiB per dispatch, averaged over every dispatch of the run;")
