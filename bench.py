@@ -936,13 +936,14 @@ def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
     timeouts = torch.zeros(1, dtype=torch.int32, device=dev)
     epoch = [0]
 
-    def reduce(flags=False):
+    def reduce(flags=False, bounded=False):
         if flags:
             epoch[0] += 1
             tar.ar_reduce_ubatch_flags(xi, xo, rows, HIDDEN, done, tiles, epoch[0], 1, None, CHUNK_BYTES,
                                        tar.AR_VARIANT_2STAGE, [s0])
         else:
-            tar.ar_reduce_ubatch(xi, xo, rows, HIDDEN, 1, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, [s0])
+            v = tar.AR_VARIANT_2STAGE | (tar.AR_UBATCH_BOUNDED if bounded else 0)
+            tar.ar_reduce_ubatch(xi, xo, rows, HIDDEN, 1, None, CHUNK_BYTES, v, [s0])
 
     def compute(iters):
         if blib.arb_alu(alu_out.data_ptr(), iters, alu_grid, s1.cuda_stream) != 0:
@@ -994,6 +995,15 @@ def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
     ov_g = (t_r + t_g - t_gboth) / min(t_r, t_g)
     log(f"overlap with a bf16 GEMM: reduce {t_r:.3f} ms, {reps_g} x GEMM {gdim}^3 {t_g:.3f} ms, "
         f"both {t_gboth:.3f} ms -> {ov_g:.2f}")
+    # the same with the reduce on its bounded-footprint grid (a persistent
+    # grid on part of the CUs), which leaves the rest of the device to the
+    # GEMM: slower alone, but the pair finishes sooner than either order of
+    # the fastest reduce and the GEMM one after the other
+    t_rb = timed(lambda: reduce(bounded=True))
+    t_gbb = timed(lambda: (reduce(bounded=True), gemm(reps_g)))
+    ov_b = (t_rb + t_g - t_gbb) / min(t_rb, t_g)
+    log(f"overlap with a bf16 GEMM, bounded reduce: reduce {t_rb:.3f} ms, both {t_gbb:.3f} ms -> {ov_b:.2f}; "
+        f"serial with the fastest reduce {t_r + t_g:.3f} ms")
     del ga, gb, gc
     t_rf = timed(lambda: reduce(True))
     t_cons = timed(lambda: consume())           # flags already set: the consumer alone
@@ -1015,10 +1025,16 @@ def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
                             "both_ms": round(t_both, 4), "overlap_fraction": round(ov, 3),
                             "reduce": "two-stage, one ubatch of [8192 x 8192] x 8 ranks, 1 MiB chunks",
                             "compute": f"ALU stand-in, {alu_grid} x 256 lanes, {iters} FMA rounds"},
-            "tbo_overlap_gemm": {"reduce_ms": round(t_r, 4), "gemm_ms": round(t_g, 4),
-                                 "both_ms": round(t_gboth, 4), "overlap_fraction": round(ov_g, 3),
+            "tbo_overlap_gemm": {"gemm_ms": round(t_g, 4),
                                  "gemm": f"{reps_g} x bf16 [{gdim} x {gdim}] x [{gdim} x {gdim}] (torch.mm)",
-                                 "gemm_TFLOPs": round(reps_g * gemm_flop / (t_g * 1e-3) / 1e12, 1)},
+                                 "gemm_TFLOPs": round(reps_g * gemm_flop / (t_g * 1e-3) / 1e12, 1),
+                                 "flat_grid": {"reduce_ms": round(t_r, 4), "both_ms": round(t_gboth, 4),
+                                               "overlap_fraction": round(ov_g, 3)},
+                                 "bounded_grid": {"reduce_ms": round(t_rb, 4), "both_ms": round(t_gbb, 4),
+                                                  "overlap_fraction": round(ov_b, 3),
+                                                  "shape": list(tar.ar_get_launch_shape(tar.AR_KERNEL_UBATCH_BOUNDED))},
+                                 "serial_fastest_ms": round(t_r + t_g, 4),
+                                 "bounded_makespan_over_serial": round(t_gbb / (t_r + t_g), 4)},
             "chunk_pipeline": {"flagged_reduce_ms": round(t_rf, 4), "chunks": nchunks,
                                "copy_consumer": {"alone_ms": round(t_cons, 4),
                                                  "serial_ms": round(t_rf + t_cons, 4),

@@ -71,6 +71,7 @@ extern "C" {
 /* ubatch variants */
 #define AR_VARIANT_ONESHOT  0
 #define AR_VARIANT_2STAGE   1
+#define AR_UBATCH_BOUNDED   256    /* flag, OR-ed into a ubatch variant          */
 
 /* recursive-doubling flags */
 #define AR_RD_STAGED        1  /* one launch per exchange step via a mailbox   */
@@ -138,6 +139,12 @@ int ar_reduce_2stage_static(const void* const* ins, void* const* outs, int P, si
  * "Fused Payloads"): words[j] = (uint64)seq << 32 | x[2j+1] << 16 | x[2j].
  *   x      n bf16 (n must be even: AR_ERR_INVALID otherwise)
  *   words  n/2 uint64, disjoint from x
+ * With the default launch shapes the words are written through past the
+ * compute die's L2 (store policy 3), so an ar_unpack_fused_wait running on
+ * another stream sees each word as soon as it is stored, while the pack is
+ * still running.  With a store policy of 0 or 1 (ar_set_launch_shape) a word
+ * may stay in the producer's L2 until that cache evicts it or the kernel
+ * ends.
  */
 int ar_pack_fused(const void* x, uint64_t* words, size_t n, uint32_t seq, void* stream);
 
@@ -221,7 +228,14 @@ int ar_rd_schedule(const uint64_t* const* in_words, uint64_t* const* out_words, 
  * chunk_bytes of every rank buffer; a chunk is the unit that workgroups are
  * assigned to, and chunks are dispatched in ascending order.
  *   variant  AR_VARIANT_2STAGE: all P outputs; AR_VARIANT_ONESHOT: outs[0]
- *            only (outs[1..] ignored, may be NULL).
+ *            only (outs[1..] ignored, may be NULL).  Either may be OR-ed
+ *            with AR_UBATCH_BOUNDED: each ubatch then runs on a persistent
+ *            grid that holds only part of the device (the
+ *            AR_KERNEL_UBATCH_BOUNDED launch shape: by default one 512-lane
+ *            workgroup on each of half the CUs), walking the same chunks in
+ *            the same order.  It is slower alone but leaves the rest of the
+ *            device to compute queued beside it on another stream, which is
+ *            the point of the two-ubatch overlap.  Results are identical.
  *   chunk_bytes  > 0, a multiple of 16.
  *   streams  host array of n_ubatch hipStream_t (entries may be NULL);
  *            the caller orders them against other work with events.
@@ -287,6 +301,11 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
 #define AR_KERNEL_RDSTEP_SMALL 17  /* ar_rd_schedule staged, n <= AR_SMALL_ELEMS */
 #define AR_KERNEL_PACK_SMALL 18    /* ar_pack_fused, n <= AR_SMALL_ELEMS        */
 #define AR_KERNEL_UNPACK_SMALL 19  /* ar_unpack_fused, n <= AR_SMALL_ELEMS      */
+#define AR_KERNEL_UBATCH_BOUNDED 20 /* ar_reduce_ubatch with AR_UBATCH_BOUNDED:
+                                      block 256, 512 or 1024 lanes; wg_per_cu
+                                      (1..8) is the footprint in eighths of
+                                      the device: cus * wg_per_cu / 8
+                                      workgroups; no LDS is requested    */
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int stores, int wg_per_cu);
 int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* stores,
                         int* wg_per_cu);
@@ -322,8 +341,9 @@ int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* stor
  *                the sum over ubatches of ceil(rows_u * hidden * 2 / chunk_bytes).
  *   epoch        nonzero value published by this call (e.g. a call counter).
  * Errors: as ar_reduce_ubatch, plus AR_ERR_INVALID for epoch == 0, a NULL or
- *         too short array, AR_ERR_ALIGN for arrays not 4-byte aligned, and
- *         AR_ERR_ALIAS if the arrays overlap each other or a data buffer.
+ *         too short array, AR_ERR_ALIGN for arrays not 4-byte aligned,
+ *         AR_ERR_ALIAS if the arrays overlap each other or a data buffer, and
+ *         AR_ERR_UNSUPPORTED for a variant with AR_UBATCH_BOUNDED.
  */
 int ar_reduce_ubatch_flags(const void* const* ins, void* const* outs, int P, size_t rows,
                            size_t hidden, int n_ubatch, const size_t* ubatch_rows,

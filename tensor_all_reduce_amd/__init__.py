@@ -22,14 +22,14 @@ __all__ = [
     "ar_reduce_2stage", "ar_reduce_2stage_static", "ar_pack_fused", "ar_unpack_fused", "ar_rd_schedule",
     "ar_reduce_ubatch", "ar_err_init", "rd_mailbox_words",
     "AR_OK", "AR_ERR_INVALID", "AR_ERR_ALIGN", "AR_ERR_ALIAS", "AR_ERR_UNSUPPORTED",
-    "AR_ERR_HIP", "AR_ERR_SIZE", "AR_STATIC_SCRATCH_ELEMS", "AR_MAX_RANKS", "AR_VARIANT_ONESHOT", "AR_VARIANT_2STAGE",
+    "AR_ERR_HIP", "AR_ERR_SIZE", "AR_STATIC_SCRATCH_ELEMS", "AR_MAX_RANKS", "AR_VARIANT_ONESHOT", "AR_VARIANT_2STAGE", "AR_UBATCH_BOUNDED",
     "AR_RD_STAGED", "AR_RD_FP32_CARRY", "ar_set_launch_shape", "ar_get_launch_shape",
     "AR_KERNEL_ONESHOT", "AR_KERNEL_2STAGE", "AR_KERNEL_UBATCH", "AR_KERNEL_RS", "AR_KERNEL_AG",
     "AR_KERNEL_PACK", "AR_KERNEL_UNPACK", "AR_KERNEL_RD", "AR_KERNEL_RDSTEP", "AR_KERNEL_UNPACK_WAIT",
     "AR_KERNEL_UBATCH_FLAGS", "ar_unpack_fused_wait", "ar_reduce_ubatch_flags", "ubatch_chunk_count",
     "AR_KERNEL_QUANT_FP8", "AR_KERNEL_REDUCE_FP8", "AR_KERNEL_REDUCE_FP8_ALL", "ar_quantize_fp8", "ar_reduce_fp8", "fp8_scale_count",
     "AR_KERNEL_ONESHOT_SMALL", "AR_KERNEL_2STAGE_SMALL", "AR_KERNEL_RD_SMALL", "AR_KERNEL_RDSTEP_SMALL",
-    "AR_KERNEL_PACK_SMALL", "AR_KERNEL_UNPACK_SMALL",
+    "AR_KERNEL_PACK_SMALL", "AR_KERNEL_UNPACK_SMALL", "AR_KERNEL_UBATCH_BOUNDED",
     "AR_SMALL_ELEMS",
     "FP8_BLOCK",
 ]
@@ -45,6 +45,7 @@ AR_STATIC_SCRATCH_ELEMS = 16777216
 AR_MAX_RANKS = 8
 AR_VARIANT_ONESHOT = 0
 AR_VARIANT_2STAGE = 1
+AR_UBATCH_BOUNDED = 256
 AR_RD_STAGED = 1
 AR_RD_FP32_CARRY = 2
 AR_KERNEL_ONESHOT = 0
@@ -67,6 +68,7 @@ AR_KERNEL_RD_SMALL = 16
 AR_KERNEL_RDSTEP_SMALL = 17
 AR_KERNEL_PACK_SMALL = 18
 AR_KERNEL_UNPACK_SMALL = 19
+AR_KERNEL_UBATCH_BOUNDED = 20
 AR_SMALL_ELEMS = 2097152
 FP8_BLOCK = 32                  # elements per power-of-two scale
 

@@ -44,7 +44,8 @@ constexpr ar::Shape kDefaultShape[] = {
     {64, 1, 1, 3, 6, 0},    // ubatch, 8 -> 8 on two streams
     {64, 1, 1, 2, 10, 0},   // staged reduce-scatter, 8 -> 1
     {64, 1, 0, 1, 3, 0},    // staged all-gather, 1 -> 8 (plain loads of scratch)
-    {64, 1, 1, 1, 0, 0},    // pack, 1 -> 2 (vec: 16-byte bf16 groups per lane; 1 = 8 bytes)
+    {64, 1, 1, 3, 0, 0},    // pack, 1 -> 2 (vec: 16-byte bf16 groups per lane; 1 = 8 bytes);
+                            // SC1 stores: a waiting receiver on another XCD sees each word once stored
     {64, 1, 1, 3, 0, 0},    // unpack, 2 -> 1
     {64, 1, 1, 3, 8, 0},    // fused recursive doubling, 8 -> 8
     {64, 1, 1, 2, 16, 0},   // staged recursive-doubling step, 8 -> 8
@@ -57,15 +58,16 @@ constexpr ar::Shape kDefaultShape[] = {
     {128, 1, 0, 1, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
     {64, 1, 0, 1, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
     {64, 1, 0, 0, 0, 0},    // staged RD step, n <= AR_SMALL_ELEMS: plain stores keep the mailbox on chip
-    {256, 1, 0, 1, 0, 0},   // pack, n <= AR_SMALL_ELEMS: plain loads, uncapped
+    {256, 1, 0, 3, 0, 0},   // pack, n <= AR_SMALL_ELEMS: plain loads, uncapped, SC1 stores
     {256, 1, 0, 1, 0, 0},   // unpack, n <= AR_SMALL_ELEMS
+    {512, 1, 1, 1, 4, 0},   // bounded ubatch: 512-lane workgroups on 4/8 of the CUs (wg_per_cu: eighths)
 };
 constexpr const char* kShapeEnv[] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
     "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT",
     "AR_SHAPE_UBATCH_FLAGS", "AR_SHAPE_QUANT_FP8", "AR_SHAPE_REDUCE_FP8", "AR_SHAPE_REDUCE_FP8_ALL",
     "AR_SHAPE_ONESHOT_SMALL", "AR_SHAPE_2STAGE_SMALL", "AR_SHAPE_RD_SMALL", "AR_SHAPE_RDSTEP_SMALL",
-    "AR_SHAPE_PACK_SMALL", "AR_SHAPE_UNPACK_SMALL"};
+    "AR_SHAPE_PACK_SMALL", "AR_SHAPE_UNPACK_SMALL", "AR_SHAPE_UBATCH_BOUNDED"};
 // one default and one override name per kind, in the order of ar.h's kind
 // numbers
 static_assert(sizeof(kDefaultShape) / sizeof(kDefaultShape[0]) == ar::kKinds, "a default shape per kind");
@@ -79,7 +81,7 @@ static_assert(ar::kOneshot == AR_KERNEL_ONESHOT && ar::k2Stage == AR_KERNEL_2STA
                   ar::kOneshotSmall == AR_KERNEL_ONESHOT_SMALL && ar::k2StageSmall == AR_KERNEL_2STAGE_SMALL &&
                   ar::kRDSmall == AR_KERNEL_RD_SMALL && ar::kRDStepSmall == AR_KERNEL_RDSTEP_SMALL &&
                   ar::kPackSmall == AR_KERNEL_PACK_SMALL && ar::kUnpackSmall == AR_KERNEL_UNPACK_SMALL &&
-                  ar::kKinds == AR_KERNEL_UNPACK_SMALL + 1,
+                  ar::kUbatchBounded == AR_KERNEL_UBATCH_BOUNDED && ar::kKinds == AR_KERNEL_UBATCH_BOUNDED + 1,
               "kind numbers match ar.h");
 
 // What one device's calls read: its CU count and the launch shapes with
@@ -110,18 +112,20 @@ DevAttr g_attr[kMaxDevices];                  // guarded by g_mu
 // device for each ar_set_launch_shape call (a tuning knob), ~500 bytes each.
 std::atomic<const Table*> g_table[kMaxDevices];
 
-bool shape_ok(int block, int vec, int ntl, int stores, int wg) {
-  return (block == 64 || block == 128 || block == 256) && vec >= 1 && vec <= 2 && ntl >= 0 &&
-         ntl <= 1 && stores >= 0 && stores <= 3 && wg >= 0 && wg <= 64;
+bool shape_ok(int kind, int block, int vec, int ntl, int stores, int wg) {
+  const bool fields = vec >= 1 && vec <= 2 && ntl >= 0 && ntl <= 1 && stores >= 0 && stores <= 3;
+  if (kind == ar::kUbatchBounded)  // a persistent grid: 256..1024 lanes, wg counts eighths of the CUs
+    return fields && (block == 256 || block == 512 || block == 1024) && wg >= 1 && wg <= 8;
+  return fields && (block == 64 || block == 128 || block == 256) && wg >= 0 && wg <= 64;
 }
 
 // "block,vec,nt_loads,stores,wg_per_cu"; an invalid string keeps the default.
-void parse_shape(const char* name, ar::Shape* s) {
+void parse_shape(int kind, const char* name, ar::Shape* s) {
   const char* e = std::getenv(name);
   if (!e || !*e) return;
   int v[5];
   if (std::sscanf(e, "%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4]) != 5) return;
-  if (!shape_ok(v[0], v[1], v[2], v[3], v[4])) return;
+  if (!shape_ok(kind, v[0], v[1], v[2], v[3], v[4])) return;
   *s = ar::Shape{v[0], v[1], v[2], v[3], v[4], 0};
 }
 
@@ -130,7 +134,7 @@ void init_base_locked() {
   if (g_base_ready) return;
   for (int k = 0; k < ar::kKinds; ++k) {
     g_base[k] = kDefaultShape[k];
-    parse_shape(kShapeEnv[k], &g_base[k]);
+    parse_shape(k, kShapeEnv[k], &g_base[k]);
   }
   g_base_ready = true;
 }
@@ -145,7 +149,7 @@ const Table* publish_locked(int dev) {
   for (int k = 0; k < ar::kKinds; ++k) {
     ar::Shape s = g_base[k];
     unsigned lds = 0;
-    if (s.wg_per_cu > 0 && d.lds_per_cu > 0) {
+    if (s.wg_per_cu > 0 && d.lds_per_cu > 0 && k != ar::kUbatchBounded) {
       lds = ((unsigned)d.lds_per_cu / (unsigned)s.wg_per_cu) & ~255u;
       if (lds > (unsigned)d.lds_per_block) lds = (unsigned)d.lds_per_block;
     }
@@ -490,7 +494,10 @@ namespace {
 int ubatch_impl(const void* const* ins, void* const* outs, int P, size_t rows, size_t hidden,
                 int n_ubatch, const size_t* ubatch_rows, size_t chunk_bytes, int variant,
                 void* const* streams, uint32_t* done, uint32_t* tiles, size_t n_flags, uint32_t epoch) {
+  const bool bounded = (variant & AR_UBATCH_BOUNDED) != 0;
+  variant &= ~AR_UBATCH_BOUNDED;
   if (variant != AR_VARIANT_ONESHOT && variant != AR_VARIANT_2STAGE) return AR_ERR_INVALID;
+  if (bounded && done) return AR_ERR_UNSUPPORTED;
   if (n_ubatch < 1 || n_ubatch > kMaxUbatch || !streams) return AR_ERR_INVALID;
   if (chunk_bytes == 0 || (chunk_bytes & 15u)) return AR_ERR_INVALID;
   if (mul_overflows(rows, hidden)) return AR_ERR_INVALID;
@@ -539,7 +546,8 @@ int ubatch_impl(const void* const* ins, void* const* outs, int P, size_t rows, s
   for (int u = 0; u < n_ubatch; ++u) {
     const size_t e0 = row0 * hidden, e1 = (row0 + split[u]) * hidden;
     row0 += split[u];
-    if (e1 > e0 && !ar::chunked_fits(L, e0, e1, chunk, nout > 1 ? 1 : 0, done != nullptr)) return AR_ERR_INVALID;
+    if (e1 > e0 && !ar::chunked_fits(L, e0, e1, chunk, nout > 1 ? 1 : 0, done != nullptr, bounded))
+      return AR_ERR_INVALID;
   }
   row0 = 0;
   for (int u = 0; u < n_ubatch; ++u) {
@@ -548,7 +556,8 @@ int ubatch_impl(const void* const* ins, void* const* outs, int P, size_t rows, s
     if (e1 == e0) continue;
     L.stream = static_cast<hipStream_t>(streams[u]);
     const ar::ChunkSignal sig{done, done ? tiles : nullptr, epoch, (uint32_t)chunk0};
-    rc = hip_status(ar::launch_chunked(L, in, out, P, e0, e1, chunk, nout > 1 ? 1 : 0, sig));
+    rc = hip_status(bounded ? ar::launch_chunked_bounded(L, in, out, P, e0, e1, chunk, nout > 1 ? 1 : 0)
+                            : ar::launch_chunked(L, in, out, P, e0, e1, chunk, nout > 1 ? 1 : 0, sig));
     if (rc) return rc;
     chunk0 += (e1 - e0 + chunk - 1) / chunk;
   }
@@ -576,7 +585,7 @@ int ar_reduce_ubatch_flags(const void* const* ins, void* const* outs, int P, siz
 }
 
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int stores, int wg_per_cu) {
-  if (kind < 0 || kind >= ar::kKinds || !shape_ok(block, vec, nt_loads, stores, wg_per_cu))
+  if (kind < 0 || kind >= ar::kKinds || !shape_ok(kind, block, vec, nt_loads, stores, wg_per_cu))
     return AR_ERR_INVALID;
   std::lock_guard<std::mutex> lock(g_mu);
   init_base_locked();

@@ -18,6 +18,7 @@ namespace ar {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxBlock = 256;  // largest workgroup the kernels are compiled for
+constexpr int kMaxBlockBounded = 1024;  // ... except the bounded-footprint reduce
 constexpr int kWave = 64;       // CDNA wavefront width
 
 template <bool NT>

@@ -51,6 +51,7 @@ enum Kind {
   kRDStepSmall,  // kRDStep for n <= AR_SMALL_ELEMS
   kPackSmall,    // kPack for n <= AR_SMALL_ELEMS
   kUnpackSmall,  // kUnpack for n <= AR_SMALL_ELEMS
+  kUbatchBounded, // chunked reduce on a persistent grid of a fraction of the CUs
   kKinds
 };
 
@@ -120,9 +121,14 @@ hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                           size_t e0, size_t e1, size_t chunk_elems, int two_stage,
                           const ChunkSignal& sig);
-// Whether launch_chunked's grid for [e0, e1) fits a launch (checked by the
-// API layer before any launch of a multi-launch call).
-bool chunked_fits(const Launch& L, size_t e0, size_t e1, size_t chunk_elems, int two_stage, bool flags);
+// Chunked reduce of [e0, e1) on the bounded persistent grid (kUbatchBounded).
+hipError_t launch_chunked_bounded(const Launch& L, const InPtrs& in, const OutPtrs& out, int P, size_t e0,
+                                  size_t e1, size_t chunk_elems, int two_stage);
+// Whether the grid of launch_chunked (or launch_chunked_bounded) for
+// [e0, e1) fits a launch (checked by the API layer before any launch of a
+// multi-launch call).
+bool chunked_fits(const Launch& L, size_t e0, size_t e1, size_t chunk_elems, int two_stage, bool flags,
+                  bool bounded);
 
 hipError_t launch_quant_fp8(const Launch& L, const InPtrs& xs, const ByteOut& codes,
                             const ByteOut& scales, int P, size_t n);

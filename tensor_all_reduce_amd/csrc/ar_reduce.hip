@@ -52,16 +52,7 @@ namespace ar {
 // acquire-loads done[chunk] == epoch (which invalidates its own L2 and L1
 // copies) sees the whole chunk of every output.
 template <int P, int NOUT, int V, bool NTL, int SP, bool SIG>
-__global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, size_t e0, size_t e1,
-                                                     size_t chunk, unsigned bpc, ChunkSignal sig) {
-  const size_t span = (size_t)V * blockDim.x * 8;
-  const size_t c = blockIdx.x / bpc;
-  const unsigned t = blockIdx.x % bpc;
-  const size_t c0 = e0 + c * chunk;
-  const size_t c1 = c0 + chunk < e1 ? c0 + chunk : e1;
-  const size_t b0 = c0 + (size_t)t * span;
-  if (b0 >= c1) return;
-  const size_t b1 = b0 + span < c1 ? b0 + span : c1;
+__device__ __forceinline__ void reduce_tile(const InPtrs& in, const OutPtrs& out, size_t b0, size_t b1) {
   const size_t vb0 = (b0 + 7) >> 3, vb1 = b1 >> 3;
   static_assert(!SIG || SP >= 2, "completion flags need write-through stores");
 
@@ -101,6 +92,20 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
       else *dst = r;
     }
   }
+}
+
+template <int P, int NOUT, int V, bool NTL, int SP, bool SIG>
+__global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, size_t e0, size_t e1,
+                                                     size_t chunk, unsigned bpc, ChunkSignal sig) {
+  const size_t span = (size_t)V * blockDim.x * 8;
+  const size_t c = blockIdx.x / bpc;
+  const unsigned t = blockIdx.x % bpc;
+  const size_t c0 = e0 + c * chunk;
+  const size_t c1 = c0 + chunk < e1 ? c0 + chunk : e1;
+  const size_t b0 = c0 + (size_t)t * span;
+  if (b0 >= c1) return;
+  const size_t b1 = b0 + span < c1 ? b0 + span : c1;
+  reduce_tile<P, NOUT, V, NTL, SP, SIG>(in, out, b0, b1);
   if constexpr (SIG) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -114,6 +119,32 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
         __hip_atomic_store(sig.done + g, sig.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  }
+}
+
+// Bounded-footprint range reduce: the same tiles, in the same chunk-major
+// order, as k_reduce, but a persistent grid of gridDim.x workgroups walks
+// them (workgroup w takes tiles w, w + G, w + 2G, ...), so the reduce holds
+// only that many workgroup slots -- with one large workgroup per CU, a
+// fraction of the CUs -- and leaves the rest of the device to compute
+// running beside it on another stream (the partner ubatch of [TBO-AR]).  At
+// any moment the grid's tiles form one compact window that advances through
+// the chunks in ascending order.  Every tile is reduced exactly as k_reduce
+// reduces it, so the results are identical.
+template <int P, int NOUT, int V, bool NTL, int SP>
+__global__ __launch_bounds__(kMaxBlockBounded) void k_reduce_bounded(InPtrs in, OutPtrs out, size_t e0,
+                                                                    size_t e1, size_t chunk, unsigned bpc,
+                                                                    size_t ntiles) {
+  const size_t span = (size_t)V * blockDim.x * 8;
+  for (size_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
+    const size_t c = g / bpc;
+    const size_t t = g - c * bpc;
+    const size_t c0 = e0 + c * chunk;
+    const size_t c1 = c0 + chunk < e1 ? c0 + chunk : e1;
+    const size_t b0 = c0 + t * span;
+    if (b0 >= c1) continue;
+    const size_t b1 = b0 + span < c1 ? b0 + span : c1;
+    reduce_tile<P, NOUT, V, NTL, SP, false>(in, out, b0, b1);
   }
 }
 
@@ -201,6 +232,36 @@ hipError_t range_v(const Shape& sh, hipStream_t st, const InPtrs& in, const OutP
   });
 }
 
+// Bounded grid: cus * wg_per_cu / 8 workgroups (wg_per_cu counts eighths of
+// the device), at least one and no more than there are tiles.
+inline size_t bounded_grid(const Shape& sh, int cus, size_t ntiles) {
+  size_t g = (size_t)cus * (size_t)(sh.wg_per_cu > 0 ? sh.wg_per_cu : 8) / 8;
+  if (g < 1) g = 1;
+  return g < ntiles ? g : ntiles;
+}
+
+template <int P, int NOUT, int V>
+hipError_t bounded_v(const Shape& sh, int cus, hipStream_t st, const InPtrs& in, const OutPtrs& out, size_t e0,
+                     size_t e1, size_t chunk) {
+  const size_t span = (size_t)V * sh.block * 8;
+  const size_t bpc = cdiv(chunk, span);
+  const size_t nchunks = cdiv(e1 - e0, chunk);
+  if (bpc > 0xFFFFFFFFull || nchunks > (~(size_t)0) / bpc) return hipErrorInvalidConfiguration;
+  const size_t ntiles = nchunks * bpc;
+  const unsigned g = (unsigned)bounded_grid(sh, cus, ntiles), b = (unsigned)bpc;
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_reduce_bounded<P, NOUT, V, decltype(ntl)::value, decltype(sp)::value>, g, dim3(sh.block), 0,
+                    st, in, out, e0, e1, chunk, b, ntiles);
+  });
+}
+
+template <int P, int NOUT>
+hipError_t bounded_p(const Shape& sh, int cus, hipStream_t st, const InPtrs& in, const OutPtrs& out, size_t e0,
+                     size_t e1, size_t chunk) {
+  if (sh.vec == 2) return bounded_v<P, NOUT, 2>(sh, cus, st, in, out, e0, e1, chunk);
+  return bounded_v<P, NOUT, 1>(sh, cus, st, in, out, e0, e1, chunk);
+}
+
 template <int P, int NOUT>
 hipError_t range_p(const Shape& sh, hipStream_t st, const InPtrs& in, const OutPtrs& out, size_t e0,
                    size_t e1, size_t chunk, const ChunkSignal& sig = ChunkSignal{nullptr, nullptr, 0, 0}) {
@@ -259,13 +320,25 @@ hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs
   AR_DISPATCH_P(P, (staged_p<PP>(L, in, out, n, scratch)))
 }
 
-// The grid check of range_v, without launching.
-bool chunked_fits(const Launch& L, size_t e0, size_t e1, size_t chunk_elems, int two_stage, bool flags) {
-  const Shape& sh = flags ? L.shape[kUbatchFlags] : (two_stage ? L.shape[kUbatch] : L.shape[kOneshot]);
+// The grid check of range_v / bounded_v, without launching.
+bool chunked_fits(const Launch& L, size_t e0, size_t e1, size_t chunk_elems, int two_stage, bool flags,
+                  bool bounded) {
+  const Shape& sh = bounded ? L.shape[kUbatchBounded]
+                            : (flags ? L.shape[kUbatchFlags] : (two_stage ? L.shape[kUbatch] : L.shape[kOneshot]));
   const size_t span = (size_t)(sh.vec == 2 ? 2 : 1) * sh.block * 8;
   const size_t bpc = cdiv(chunk_elems, span);
   const size_t nchunks = cdiv(e1 - e0, chunk_elems);
+  if (bounded) return bpc <= 0xFFFFFFFFull && nchunks <= (~(size_t)0) / bpc;
   return bpc <= 0x7FFFFFFFull && nchunks <= 0x7FFFFFFFull / bpc;
+}
+
+hipError_t launch_chunked_bounded(const Launch& L, const InPtrs& in, const OutPtrs& out, int P, size_t e0,
+                                  size_t e1, size_t chunk_elems, int two_stage) {
+  const Shape& sh = L.shape[kUbatchBounded];
+  if (two_stage) {
+    AR_DISPATCH_P(P, (bounded_p<PP, PP>(sh, L.cus, L.stream, in, out, e0, e1, chunk_elems)))
+  }
+  AR_DISPATCH_P(P, (bounded_p<PP, 1>(sh, L.cus, L.stream, in, out, e0, e1, chunk_elems)))
 }
 
 hipError_t launch_chunked(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,

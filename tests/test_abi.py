@@ -107,6 +107,28 @@ def test_2stage_validation():
     assert L.ar_reduce_2stage(ins, arr(A, B), 2, 0, None, None) == tar.AR_OK
 
 
+def test_bounded_ubatch_shape_and_flags_validation():
+    L = tar.lib()
+    K = tar.AR_KERNEL_UBATCH_BOUNDED
+    default = tar.ar_get_launch_shape(K)
+    assert default[0] in (256, 512, 1024) and 1 <= default[4] <= 8
+    # the bounded kind takes 256..1024 lanes and a footprint of 1..8 eighths
+    assert L.ar_set_launch_shape(K, 1024, 1, 1, 1, 8) == tar.AR_OK
+    assert L.ar_set_launch_shape(K, 512, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(K, 512, 1, 1, 1, 9) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(K, 64, 1, 1, 1, 4) == tar.AR_ERR_INVALID
+    # the other kinds keep their limits
+    assert L.ar_set_launch_shape(tar.AR_KERNEL_UBATCH, 512, 1, 1, 1, 4) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(K, *default) == tar.AR_OK
+    # completion flags have no bounded form: rejected before any device work
+    ins, outs = arr(A, B), arr(C, C + 4096)
+    done, tiles = ctypes.c_void_p(0x40000000), ctypes.c_void_p(0x40001000)
+    rc = L.ar_reduce_ubatch_flags(ins, outs, 2, 4, 8, 1, None, 16, tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED,
+                                  arr(None), done, tiles, 64, 1)
+    assert rc == tar.AR_ERR_UNSUPPORTED
+    assert L.ar_reduce_ubatch(ins, outs, 2, 4, 8, 1, None, 16, 0x200, arr(None)) == tar.AR_ERR_INVALID
+
+
 def test_2stage_static_validation():
     L = tar.lib()
     ins = arr(A, B)

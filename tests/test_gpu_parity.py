@@ -323,6 +323,57 @@ def test_ubatch_many_ubatches_hidden_not_multiple_of_8():
         check_full(o, ref, "ubatch odd hidden")
 
 
+@pytest.mark.parametrize("shape", [(512, 1, 1, 1, 4), (256, 2, 1, 3, 1), (1024, 1, 0, 0, 8), (512, 2, 1, 2, 3)])
+@pytest.mark.parametrize("chunk_bytes", [1 << 20, 4096 + 16])
+def test_ubatch_bounded(shape, chunk_bytes):
+    """The bounded-footprint ubatch reduce (AR_UBATCH_BOUNDED): a persistent
+    grid of a fraction of the CUs walks the chunked tiles.  Several grid
+    shapes (256..1024 lanes, 1/8..8/8 of the CUs, both lane widths, every
+    store policy), ragged chunks, three ubatches, hidden not a multiple of 8,
+    both variants: bit-exact against the oracle."""
+    P, rows, hidden = 8, 512, 8192 + 5
+    n = rows * hidden
+    xs = synth.rank_buffers("logmag", P, n, 5, 2, shape[0], shape[4])
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    outs = [empty16(n) for _ in range(P)]
+    one = [empty16(n)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    default = tar.ar_get_launch_shape(tar.AR_KERNEL_UBATCH_BOUNDED)
+    tar.ar_set_launch_shape(tar.AR_KERNEL_UBATCH_BOUNDED, *shape)
+    try:
+        note(f"ubatch bounded shape={shape} chunk={chunk_bytes}")
+        tar.ar_reduce_ubatch(ins, outs, rows, hidden, 3, [100, 300, 112], chunk_bytes,
+                             tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED, streams)
+        tar.ar_reduce_ubatch(ins, one, rows, hidden, 3, [100, 300, 112], chunk_bytes,
+                             tar.AR_VARIANT_ONESHOT | tar.AR_UBATCH_BOUNDED, streams)
+        torch.cuda.synchronize()
+    finally:
+        tar.ar_set_launch_shape(tar.AR_KERNEL_UBATCH_BOUNDED, *default)
+    for o in outs:
+        check_full(o, ref, f"ubatch bounded {shape} 2stage")
+    check_full(one[0], ref, f"ubatch bounded {shape} oneshot")
+
+
+def test_ubatch_bounded_in_place():
+    """Bounded mode with every output equal to its input."""
+    P, rows, hidden = 4, 96, 4096
+    n = rows * hidden
+    xs = synth.rank_buffers("normal", P, n, 5, 3)
+    ref = oracle.reduce_seq(xs)
+    bufs = [up16(x) for x in xs]
+    s = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in s:
+        st.wait_stream(torch.cuda.current_stream())
+    note("ubatch bounded in place")
+    tar.ar_reduce_ubatch(bufs, bufs, rows, hidden, 2, None, 1 << 16, tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED, s)
+    torch.cuda.synchronize()
+    for b in bufs:
+        check_full(b, ref, "ubatch bounded in place")
+
+
 # ------------------------------------------------------------ concurrency
 
 def test_two_threads_two_streams():
@@ -425,8 +476,9 @@ def test_prefill_2stage_full_size(record_property):
 def test_ubatch_full_size(record_property):
     """P=8 [16384 x 16384] per rank split into two 8192-row ubatches on two
     streams, 1 MiB chunks, log-uniform magnitudes in [2^-8, 2^8] with random
-    signs: every element of all P outputs of the two-stage variant and of
-    the one-shot variant's output against the oracle."""
+    signs: every element of all P outputs of the two-stage variant (flat and
+    bounded-footprint grids) and of the one-shot variant's output against
+    the oracle."""
     P, rows, hidden = 8, 16384, 16384
     n = rows * hidden
     note("ubatch full size: generate")
@@ -440,14 +492,18 @@ def test_ubatch_full_size(record_property):
     tar.ar_reduce_ubatch(ins, outs, rows, hidden, 2, None, 1 << 20, tar.AR_VARIANT_2STAGE, s)
     note("ubatch full size: one-shot variant")
     tar.ar_reduce_ubatch(ins, [one], rows, hidden, 2, None, 1 << 20, tar.AR_VARIANT_ONESHOT, s)
+    bouts = [empty16(n) for _ in range(P)]
+    note("ubatch full size: two-stage variant, bounded footprint")
+    tar.ar_reduce_ubatch(ins, bouts, rows, hidden, 2, None, 1 << 20, tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED, s)
     torch.cuda.synchronize()
     outputs = {f"2stage[{r}]": outs[r] for r in range(P)}
     outputs["oneshot"] = one
+    outputs.update({f"2stage bounded[{r}]": bouts[r] for r in range(P)})
     note("ubatch full size: compare every element with the oracle")
     _compare_full(ins, outputs, n, "ubatch")
     record_property("elements_compared", n * len(outputs))
     print(f"[gpu] ubatch full size: {len(outputs)} outputs x {n} elements equal the oracle")
-    del ins, outs, one
+    del ins, outs, one, bouts
     torch.cuda.empty_cache()
 
 

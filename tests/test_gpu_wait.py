@@ -109,3 +109,57 @@ def test_wait_partial_producer_times_out_exactly():
     torch.cuda.synchronize()
     assert err_host(err) == (W - W // 2, W // 2)
     assert np.array_equal(down16(out)[: n // 2], x[: n // 2])
+
+
+def test_wait_consumes_while_producer_runs(record_property):
+    """The pack writes its payload words through to the device-coherent
+    level as it stores them (its default SC1 store policy), so a waiting
+    unpack running beside it on another stream takes each word as soon as it
+    lands rather than when the pack kernel ends.  A 256 MiB payload is
+    packed on one stream while the waiting unpack runs on another: the
+    consumer finishes well within its own run time after the producer ends
+    (it had already taken most of the words), and its output equals the
+    oracle's unpack.  The lag is measured between an event after the pack
+    and an event after the unpack; the consumer's own run time is measured
+    on payloads already written."""
+    n = 64 << 20                       # 128 MiB of bf16, 256 MiB of payload
+    x = synth.normal(n, 86)
+    src = up16(x)
+    w = torch.empty(n // 2, dtype=torch.int64, device=DEV)
+    out = empty16(n)
+    err = new_err()
+    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # warm both streams and time the consumer alone on ready payloads
+    tar.ar_pack_fused(src, w, 1, stream=prod)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record(cons)
+    tar.ar_unpack_fused_wait(w, out, 1, err, stream=cons)
+    b.record(cons)
+    torch.cuda.synchronize()
+    alone = a.elapsed_time(b)
+    lags, packs = [], []
+    for k in range(3):
+        seq = 10 + k
+        tar.ar_err_init(err, stream=cons)
+        torch.cuda.synchronize()
+        p0, p1, c1 = ev(), ev(), ev()
+        note(f"unpack_wait beside a running pack, seq {seq}")
+        p0.record(prod)
+        tar.ar_pack_fused(src, w, seq, stream=prod)
+        p1.record(prod)
+        tar.ar_unpack_fused_wait(w, out, seq, err, max_spins=1 << 22, stream=cons)
+        c1.record(cons)
+        torch.cuda.synchronize()
+        assert err_host(err) == (0, 2 ** 64 - 1)
+        packs.append(p0.elapsed_time(p1))
+        lags.append(p1.elapsed_time(c1))
+    want, _ = oracle.unpack(oracle.pack(x, 12), 12)
+    assert np.array_equal(down16(out), want)
+    lag = min(lags)
+    print(f"[gpu] pack {min(packs):.3f} ms; waiting unpack alone {alone:.3f} ms; consumer end after producer end "
+          f"{', '.join(f'{v:.3f}' for v in lags)} ms")
+    record_property("consumer_alone_ms", round(alone, 4))
+    record_property("consumer_lag_after_producer_ms", [round(v, 4) for v in lags])
+    assert lag < 0.5 * alone
