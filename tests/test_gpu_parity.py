@@ -172,6 +172,31 @@ def test_canaries_untouched():
         check_full(b[G:G + n], ref, "canary body")
 
 
+@pytest.mark.parametrize("P,n", [(8, 10), (8, 13), (3, 17), (8, 8 * 8 + 5), (7, 1000 * 7 + 3)])
+def test_staged_ragged_tail_canaries(P, n):
+    """The staged two-stage where n is not a multiple of 8 and trailing
+    shards are empty (n = 10 with P = 8 leaves shards 1..7 empty): only the
+    last non-empty shard writes the ragged tail.  Outputs and scratch are
+    carved out of guarded buffers; the guards keep their pattern, and every
+    output, the scratch, and the static-scratch entry point equal the oracle."""
+    G = 256
+    xs = synth.rank_buffers("normal", P, n, 26, n)
+    ref = oracle.reduce_seq(xs)
+    ins = [up16(x) for x in xs]
+    bigs = [torch.full((n + 2 * G,), 0x5A5A, dtype=torch.int16, device=DEV) for _ in range(2 * P)]
+    outs = [b[G:G + n] for b in bigs[:P]]
+    outs2 = [b[G:G + n] for b in bigs[P:]]
+    sbig = torch.full((n + 2 * G,), 0x5A5A, dtype=torch.int16, device=DEV)
+    note(f"staged ragged tail P={P} n={n}")
+    tar.ar_reduce_2stage(ins, outs, scratch=sbig[G:G + n])
+    tar.ar_reduce_2stage_static(ins, outs2)
+    torch.cuda.synchronize()
+    for b in bigs + [sbig]:
+        h = down16(b)
+        assert np.all(h[:G] == np.uint16(0x5A5A)) and np.all(h[G + n:] == np.uint16(0x5A5A))
+        check_full(b[G:G + n], ref, "staged ragged body")
+
+
 def test_n_zero_is_noop():
     t = empty16(16)
     t.fill_(7)
