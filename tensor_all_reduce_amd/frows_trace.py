@@ -1,10 +1,11 @@
 """Profiling target for the kernels beyond the bench step: the fp8 path
 (quantise all 8 ranks, reduce into one output and into all 8), the flagged
 two-stage ubatch reduce (per-chunk completion flags, both ubatches on one
-stream) and the waiting unpack on payloads that already carry the expected
-sequence number, each `reps` times at the prefill shape (P = 8, bf16
-[16384 x 8192] per rank), then three plain copies of exactly 1 GiB that
-calibrate FETCH_SIZE / WRITE_SIZE.  No call here waits on another stream, so
+stream), the same ubatch reduce on its bounded-footprint grid, and the
+waiting unpack on payloads that already carry the expected sequence number,
+each `reps` times at the prefill shape (P = 8, bf16 [16384 x 8192] per
+rank), then three plain copies of exactly 1 GiB that calibrate FETCH_SIZE /
+WRITE_SIZE.  No call here waits on another stream, so
 it can run under counter collection, which serialises kernels.
 
 Usage: python -m tensor_all_reduce_amd.frows_trace [--reps 4]
@@ -61,6 +62,11 @@ def main(argv=None):
     if not bool((done == a.reps).all()) or bool(tiles.any()):
         raise SystemExit("flagged reduce: flags or counters not as expected")
     print("[frows] flagged ubatch done", flush=True)
+    for _ in range(a.reps):
+        tar.ar_reduce_ubatch(ins, outs, rows, hidden, 2, None, 1 << 20,
+                             tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED, [s, s])
+    torch.cuda.synchronize()
+    print("[frows] bounded ubatch done", flush=True)
     del outs
     torch.cuda.empty_cache()
     words = [torch.empty(n // 2, dtype=torch.int64, device=dev) for _ in range(P)]
