@@ -2,8 +2,11 @@
 
 Each case draws the rank count, the element count (tiny, ragged, or a few
 tiles), the value mix (normal, log-uniform, integers, or specials mixed in),
-and the operation's own knobs (chunk size, ubatch split, sequence number,
-output count), then compares every output with the oracle bit for bit.  The
+and the operation's own knobs (chunk size, ubatch split and grid, sequence
+number, output count), then compares every output with the oracle bit for
+bit.  The reduce family runs the one-shot, the fused, staged and
+static-scratch two-stage, and the ubatch reduce on the flat or the bounded
+grid.  The
 seed of a failing case is in the assertion message.  AR_FUZZ_SEEDS=<k> in
 the environment runs k seeds per family.
 """
@@ -70,9 +73,11 @@ def test_fuzz_reduce_family(seed):
     scratch = empty16(max(n, 1))
     outs2 = [empty16(max(n, 1)) for _ in range(P)]
     tar.ar_reduce_2stage(ins, outs2, scratch=scratch, n=n)
+    outs3 = [empty16(max(n, 1)) for _ in range(P)]
+    tar.ar_reduce_2stage_static(ins, outs3, n=n)
     torch.cuda.synchronize()
     eq(down16(out)[:n], ref, f"{tag} oneshot")
-    for o in outs + outs2:
+    for o in outs + outs2 + outs3:
         eq(down16(o)[:n], ref, f"{tag} 2stage")
     # ubatch: a random factorisation of n into rows x hidden and a random split
     if n:
@@ -84,9 +89,11 @@ def test_fuzz_reduce_family(seed):
         split = np.diff(np.concatenate([[0], cuts, [rows]])).astype(int).tolist()
         chunk = 16 * int(rng.integers(1, 300))
         variant = int(rng.integers(0, 2))
+        bounded = bool(rng.integers(0, 2))
         uouts = [empty16(n) for _ in range(P)]
-        note(f"fuzz ubatch {tag} rows={rows} split={split} chunk={chunk} variant={variant}")
-        tar.ar_reduce_ubatch(ins, uouts, rows, hidden, nub, split, chunk, variant)
+        note(f"fuzz ubatch {tag} rows={rows} split={split} chunk={chunk} variant={variant} bounded={bounded}")
+        tar.ar_reduce_ubatch(ins, uouts, rows, hidden, nub, split, chunk,
+                             variant | (tar.AR_UBATCH_BOUNDED if bounded else 0))
         torch.cuda.synchronize()
         for o in (uouts if variant == tar.AR_VARIANT_2STAGE else uouts[:1]):
             eq(down16(o), ref, f"{tag} ubatch")
