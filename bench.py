@@ -847,8 +847,10 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
     2 = SC1 write-through, 3 = SC1 + non-temporal) is set with
     ar_set_launch_shape and timed with HIP events around `reps` calls;
     candidates are visited in a shuffled order each round and the median over
-    rounds is reported, so slow drift of the device affects all alike.  The
-    one-shot writes its output to the P output buffers in turn: its 256 MiB
+    rounds is reported, so slow drift of the device affects all alike.  Last,
+    the bounded ubatch grid's footprint is timed alone and beside a bf16 GEMM
+    on another stream.  The one-shot writes its output to the P output
+    buffers in turn: its 256 MiB
     output fits the 256 MiB last-level cache, and calls that rewrite one
     buffer leave it there without ever paying its write-back to HBM.  The
     ubatch schedule is also run with both ubatches on one stream.  Reference
@@ -891,11 +893,11 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
 
     kinds = {
         "oneshot": (tar.AR_KERNEL_ONESHOT, (P + 1) * B, oneshot_rotating,
-                    list(itertools.product((64, 128), (1,), (1,), (1, 2, 3), (0, 8, 12, 16)))),
+                    list(itertools.product((64, 128), (1,), (1,), (0, 1, 2, 3), (0, 8, 12, 16)))),
         "2stage": (tar.AR_KERNEL_2STAGE, 2 * P * B, lambda: tar.ar_reduce_2stage(ins, outs),
-                   list(itertools.product((64,), (1, 2), (1,), (1, 2, 3), (4, 5, 6, 8)))),
+                   list(itertools.product((64,), (1, 2), (1,), (0, 1, 2, 3), (4, 5, 6, 8)))),
         "rd": (tar.AR_KERNEL_RD, 4 * P * B, lambda: tar.ar_rd_schedule(words, rdo, 1, err),
-               list(itertools.product((64,), (1,), (1,), (1, 2, 3), (6, 8, 10)))),
+               list(itertools.product((64,), (1,), (1,), (0, 1, 2, 3), (6, 8, 10)))),
         "ubatch_two_streams": (tar.AR_KERNEL_UBATCH, 2 * P * B5, lambda: ubatch([s0, s1]),
                                list(itertools.product((64,), (1,), (1,), (1, 3), (3, 4, 6, 8)))),
         "ubatch_one_stream": (tar.AR_KERNEL_UBATCH, 2 * P * B5, lambda: ubatch([s0, s0]),
@@ -982,6 +984,58 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
     g, sh = best_of(copy_two, [(v, w) for v in (1, 2) for w in caps], 2 * P * B5)
     print(f"   8 -> 8 copy [16384 x 16384], 2 streams {g:9.1f} GB/s  (vec, wg/cu) = {sh}")
     sys.stdout.flush()
+
+    # the bounded ubatch grid's footprint, alone and beside a bf16 GEMM on
+    # another stream (one [8192 x 8192] ubatch of the prefill batch, as in
+    # tbo_overlap_gemm); the flat grid for comparison
+    rows_u = ROWS // 2
+    m = rows_u * HIDDEN
+    xi, xo = [x[:m] for x in ins], [o[:m] for o in outs]
+    gdim = 4096
+    ga = torch.randn(gdim, gdim, device=dev, dtype=torch.bfloat16)
+    gb = torch.randn(gdim, gdim, device=dev, dtype=torch.bfloat16)
+    gc = torch.empty(gdim, gdim, device=dev, dtype=torch.bfloat16)
+
+    def pair(reduce_fn, gemms):
+        def step():
+            s0.wait_stream(main_s)
+            s1.wait_stream(main_s)
+            if reduce_fn is not None:
+                reduce_fn()
+            with torch.cuda.stream(s1):
+                for _ in range(gemms):
+                    torch.mm(ga, gb, out=gc)
+            main_s.wait_stream(s0)
+            main_s.wait_stream(s1)
+        return timed_settled(torch, main_s, step, 10)
+
+    def red(v):
+        return lambda: tar.ar_reduce_ubatch(xi, xo, rows_u, HIDDEN, 1, None, CHUNK_BYTES, v, [s0])
+
+    kb = tar.AR_KERNEL_UBATCH_BOUNDED
+    default_b = tar.ar_get_launch_shape(kb)
+    t_g1 = pair(None, 1)
+    t_flat = pair(red(tar.AR_VARIANT_2STAGE), 0)
+    gemms = max(1, round(t_flat / t_g1))
+    t_g = pair(None, gemms)
+    print(f"== bounded ubatch footprint: one [{rows_u} x {HIDDEN}] ubatch (P=8), alone and beside {gemms} x bf16 "
+          f"GEMM {gdim}^3 ({t_g:.4f} ms alone)")
+    print("   grid                                alone_ms  with_gemm_ms  overlap  vs_fastest_serial")
+    both = pair(red(tar.AR_VARIANT_2STAGE), gemms)
+    serial = t_flat + t_g
+    print(f"   flat (ubatch default)               {t_flat:8.4f}  {both:12.4f}  {(t_flat + t_g - both) / min(t_flat, t_g):7.2f}"
+          f"  {both / serial:17.4f}")
+    for block, eighths in ((512, 2), (512, 3), (512, 4), (512, 5), (512, 6), (256, 4), (1024, 4)):
+        tar.ar_set_launch_shape(kb, block, 1, 1, 1, eighths)
+        v = tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED
+        alone = pair(red(v), 0)
+        both = pair(red(v), gemms)
+        tag = "  <- default" if (block, 1, 1, 1, eighths) == default_b else ""
+        print(f"   bounded {block:4d} lanes, {eighths}/8 of the CUs  {alone:8.4f}  {both:12.4f}  "
+              f"{(alone + t_g - both) / min(alone, t_g):7.2f}  {both / serial:17.4f}{tag}")
+        sys.stdout.flush()
+    tar.ar_set_launch_shape(kb, *default_b)
+    log("ab: bounded footprint done")
 
 
 def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
