@@ -752,12 +752,16 @@ def test_graph_capture_replays():
 
 def test_graph_capture_replays_other_calls():
     """The remaining entry points captured in one HIP graph: the staged
-    two-stage (scratch), staged recursive doubling (mailbox), the waiting
-    unpack on payloads the graph itself produced, the two-stream ubatch
-    reduce without and with completion flags (the ubatch streams forked from
+    two-stage (caller scratch, and the library's static scratch -- the
+    no-allocation entry point exists for callers under graph capture),
+    staged recursive doubling (mailbox), the waiting unpack on payloads the
+    graph itself produced, the two-stream ubatch reduce on the flat and the
+    bounded grid and with completion flags (the ubatch streams forked from
     the capture stream and joined back), and the fp8 quantise and reduce.
     Replayed with fresh inputs, cleared outputs and flags, and eager library
-    work between replays; every replay is checked against the oracle."""
+    work between replays (including an eager static-scratch call on other
+    values, which leaves its own values in the shared array); every replay
+    is checked against the oracle."""
     P, rows = 8, 24
     n = rows * HIDDEN
     chunk = 64 * 1024 + 16                     # bytes: chunks end off the row boundaries
@@ -765,7 +769,8 @@ def test_graph_capture_replays_other_calls():
     def i64(k):
         return torch.empty(k, dtype=torch.int64, device=DEV)
     ins = [empty16(n) for _ in range(P)]
-    st_outs, ub_outs, fl_outs, f8_outs = ([empty16(n) for _ in range(P)] for _ in range(4))
+    st_outs, ub_outs, fl_outs, f8_outs, sa_outs, bd_outs, eg_outs = ([empty16(n) for _ in range(P)]
+                                                                     for _ in range(7))
     scratch, xw = empty16(n), empty16(n)
     words, rdo = [i64(n // 2) for _ in range(P)], [i64(n // 2) for _ in range(P)]
     mbox = i64(tar.rd_mailbox_words(P, n))
@@ -780,6 +785,7 @@ def test_graph_capture_replays_other_calls():
     def body():
         tar.ar_err_init(err, stream=side)
         tar.ar_reduce_2stage(ins, st_outs, scratch=scratch, stream=side)
+        tar.ar_reduce_2stage_static(ins, sa_outs, stream=side)
         for r in range(P):
             tar.ar_pack_fused(ins[r], words[r], 21, stream=side)
         tar.ar_rd_schedule(words, rdo, 21, err, mailbox=mbox, flags=tar.AR_RD_STAGED, stream=side)
@@ -789,6 +795,8 @@ def test_graph_capture_replays_other_calls():
         tar.ar_reduce_ubatch(ins, ub_outs, rows, HIDDEN, 2, None, chunk, tar.AR_VARIANT_2STAGE, streams=[s0, s1])
         tar.ar_reduce_ubatch_flags(ins, fl_outs, rows, HIDDEN, done, tiles, 5, 2, None, chunk,
                                    tar.AR_VARIANT_ONESHOT, streams=[s0, s1])
+        tar.ar_reduce_ubatch(ins, bd_outs, rows, HIDDEN, 2, None, chunk,
+                             tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED, streams=[s0, s1])
         side.wait_stream(s0)
         side.wait_stream(s1)
         tar.ar_quantize_fp8(ins, codes, scales, stream=side)
@@ -807,18 +815,19 @@ def test_graph_capture_replays_other_calls():
         xs = synth.rank_buffers("normal", P, n, 61, rep)
         for t, h in zip(ins, xs):
             t.copy_(up16(h))
-        for t in st_outs + ub_outs + fl_outs + f8_outs + [scratch, xw]:
+        for t in st_outs + ub_outs + fl_outs + f8_outs + sa_outs + bd_outs + [scratch, xw]:
             t.zero_()
         done.zero_()
         scratch_out = empty16(n)
         tar.ar_reduce_oneshot(ins[::-1], scratch_out)
+        tar.ar_reduce_2stage_static(ins[::-1], eg_outs)
         torch.cuda.synchronize()
         note(f"graph replay {rep} of the remaining entry points")
         g.replay()
         torch.cuda.synchronize()
         ref = oracle.reduce_seq(xs)
         check_full(scratch, ref, f"replay {rep} staged scratch")
-        for o in st_outs + ub_outs:
+        for o in st_outs + ub_outs + sa_outs + bd_outs:
             check_full(o, ref, f"replay {rep} staged two-stage / ubatch")
         check_full(fl_outs[0], ref, f"replay {rep} flagged ubatch")
         assert bool((done == 5).all()) and not bool(tiles.any()), f"replay {rep}: chunk flags or counters"
@@ -836,3 +845,5 @@ def test_graph_capture_replays_other_calls():
         for o in f8_outs:
             check_full(o, f8, f"replay {rep} fp8 reduce")
         check_full(scratch_out, oracle.reduce_seq(xs[::-1]), "eager between replays")
+        for o in eg_outs:
+            check_full(o, oracle.reduce_seq(xs[::-1]), "eager static-scratch call between replays")
