@@ -847,9 +847,10 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
     2 = SC1 write-through, 3 = SC1 + non-temporal) is set with
     ar_set_launch_shape and timed with HIP events around `reps` calls;
     candidates are visited in a shuffled order each round and the median over
-    rounds is reported, so slow drift of the device affects all alike.  Last,
+    rounds is reported, so slow drift of the device affects all alike.  Then
     the bounded ubatch grid's footprint is timed alone and beside a bf16 GEMM
-    on another stream.  The one-shot writes its output to the P output
+    on another stream, and last the 8 -> 8 kernels over buffer placements
+    (placement_report).  The one-shot writes its output to the P output
     buffers in turn: its 256 MiB
     output fits the 256 MiB last-level cache, and calls that rewrite one
     buffer leave it there without ever paying its write-back to HBM.  The
@@ -1036,6 +1037,85 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
         sys.stdout.flush()
     tar.ar_set_launch_shape(kb, *default_b)
     log("ab: bounded footprint done")
+    del ga, gb, gc
+    placement_report(tar, torch, dev, main_s, s0, s1, ins, outs, uin, ubo, time_calls)
+
+
+def placement_report(tar, torch, dev, main_s, s0, s1, ins, outs, uin, ubo, time_calls):
+    """The 8 -> 8 rate against where the 16 buffers sit relative to one another.
+
+    The P simulated ranks' buffers share one GPU's HBM (with P real ranks each
+    rank reads its own), and the DRAM channel and bank an address maps to
+    depends on its higher address bits: 16 streams whose bases differ only in
+    some of those bits contend for the same banks at the same offset.  The
+    fused two-stage runs on 16 buffers of 256 MiB carved from one pooled
+    allocation at stride S, inputs first then outputs, or alternating; the
+    two-ubatch reduce runs on 16 buffers of 512 MiB at stride 512 MiB + skew.
+    The bench's own separately allocated buffers are the first row of each
+    table.  Pool contents are arbitrary finite bf16 patterns; the rate does
+    not depend on the values."""
+    import random
+    import statistics
+
+    n = ROWS * HIDDEN
+    n5 = UB_ROWS * UB_HIDDEN
+    MiB = 1 << 20
+    strides = (256, 256.25, 258, 260, 264, 288, 384, 512)
+    skews = (0, 0.25, 2, 8, 128)
+    span = max(16 * max(strides) * MiB // 2, 16 * (512 + max(skews)) * MiB // 2)
+    pool = torch.empty(int(span) + n5, dtype=torch.int16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    pool.random_(-16000, 16000, generator=g)
+
+    def carve(stride_mib, count, elems, alternating):
+        e = int(stride_mib * MiB) // 2
+        b = [pool[k * e:k * e + elems] for k in range(2 * count)]
+        return (b[0::2], b[1::2]) if alternating else (b[:count], b[count:])
+
+    def ubatch(i, o, streams):
+        def fn():
+            for st in set(streams):
+                st.wait_stream(main_s)
+            tar.ar_reduce_ubatch(i, o, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, streams)
+            for st in set(streams):
+                main_s.wait_stream(st)
+        return fn
+
+    c4 = {"separate allocations (bench)": lambda: tar.ar_reduce_2stage(ins, outs)}
+    for S in strides:
+        for alt in (False, True):
+            i, o = carve(S, P, n, alt)
+            c4[f"stride {S:g} MiB, {'alternating' if alt else 'inputs then outputs'}"] = (
+                lambda i=i, o=o: tar.ar_reduce_2stage(i, o))
+    c5 = {}
+    for mode, streams in (("two streams", [s0, s1]), ("one stream", [s0, s0])):
+        c5[f"separate allocations (bench), {mode}"] = ubatch(uin, ubo, streams)
+        for sk in skews:
+            i, o = carve(512 + sk, P, n5, False)
+            c5[f"stride 512 MiB + {sk:g} MiB, {mode}"] = ubatch(i, o, streams)
+    rng = random.Random(13)
+    rounds = 3
+    print("== buffer placement: the 8 -> 8 rate against the buffers' relative addresses "
+          f"({rounds} shuffled rounds, median)")
+    for title, cases, cred in (("fused two-stage, P=8, 16 buffers of 256 MiB", c4, 2 * P * 2 * n),
+                               ("two-ubatch reduce, P=8, 16 buffers of 512 MiB", c5, 2 * P * 2 * n5)):
+        times = {k: [] for k in cases}
+        for _ in range(rounds):
+            order = list(cases)
+            rng.shuffle(order)
+            for k in order:
+                times[k].append(time_calls(cases[k]))
+        print(f"   {title}")
+        print("   placement                                              ms      GB/s  frac-of-8TB/s")
+        for k in cases:
+            ms = statistics.median(times[k])
+            gbps = cred / (ms * 1e-3) / 1e9
+            print(f"   {k:50s} {ms:9.4f} {gbps:9.1f}  {gbps / PEAK_HBM_GBPS:13.4f}")
+        sys.stdout.flush()
+    del pool
+    torch.cuda.empty_cache()
+    log("ab: placement done")
 
 
 def overlap(tar, blib, torch, dev, main_s, ins, outs, s0, s1):
