@@ -5,8 +5,10 @@
  * HBM.  The library sums them element by element with binary32 accumulation
  * in a fixed schedule order and writes bf16 results.  Every entry point
  * launches hand-written HIP kernels on the caller's stream and returns at
- * once; nothing here synchronises, allocates or copies between host and
- * device.
+ * once; nothing here synchronises or copies between host and device, and the
+ * library makes no memory allocation of its own, host or device (the tuning
+ * knob ar_set_launch_shape excepted: it allocates a small host table per GPU
+ * in use).
  *
  * Pages cited (titles as printed on the pages):
  *   [TBO-AR] "[DSV4] perf(tbo): overlap pure-TP all_reduce on TBO + Delay TP"
@@ -43,7 +45,7 @@
  * - Thread safety: every entry point may be called concurrently from several
  *   host threads on different streams.  The only global state is one
  *   immutable launch table per device (CU count and launch shapes), built
- *   once under a lock by the first call on that device -- lazy
+ *   in static storage once, under a lock, by the first call on that device -- lazy
  *   initialisation raced by two ubatch threads is the hazard [TBO-AR] review
  *   comments describe -- and read without a lock by every later call.
  */

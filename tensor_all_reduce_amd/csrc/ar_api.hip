@@ -108,8 +108,11 @@ bool g_base_ready = false;                    // guarded by g_mu
 ar::Shape g_base[ar::kKinds];                 // defaults + overrides; guarded by g_mu
 DevAttr g_attr[kMaxDevices];                  // guarded by g_mu
 // Published tables are never freed: a call may still be reading a table that
-// ar_set_launch_shape has replaced.  One table per device, plus one per
-// device for each ar_set_launch_shape call (a tuning knob), ~500 bytes each.
+// ar_set_launch_shape has replaced.  A device's first table is static
+// storage, so no compute entry point allocates memory of any kind; only
+// ar_set_launch_shape (a tuning knob) allocates a replacement table, ~500
+// bytes, per device in use.
+Table g_first_table[kMaxDevices];             // written once, under g_mu, before publication
 std::atomic<const Table*> g_table[kMaxDevices];
 
 bool shape_ok(int kind, int block, int vec, int ntl, int stores, int wg) {
@@ -139,11 +142,12 @@ void init_base_locked() {
   g_base_ready = true;
 }
 
-// Build and publish device `dev`'s table from g_base.  Caller holds g_mu and
-// has filled g_attr[dev].
-const Table* publish_locked(int dev) {
+// Build and publish device `dev`'s table from g_base: the device's first
+// table into its static slot, a replacement on the heap.  Caller holds g_mu
+// and has filled g_attr[dev].
+const Table* publish_locked(int dev, bool first) {
   const DevAttr& d = g_attr[dev];
-  Table* t = new Table;
+  Table* t = first ? &g_first_table[dev] : new Table;
   t->cus = d.cus;
   t->scratch = d.scratch;
   for (int k = 0; k < ar::kKinds; ++k) {
@@ -190,7 +194,7 @@ int resolve(ar::Launch* L, void* stream) {
       }
       g_attr[dev] = DevAttr{cus, lcu, lblk, sp};
       init_base_locked();
-      t = publish_locked(dev);
+      t = publish_locked(dev, true);
     }
   }
   L->cus = t->cus;
@@ -592,7 +596,7 @@ int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int stores, 
   g_base[kind] = ar::Shape{block, vec, nt_loads, stores, wg_per_cu, 0};
   // republish every device already in use; later calls see the new shape
   for (int d = 0; d < kMaxDevices; ++d)
-    if (g_table[d].load(std::memory_order_relaxed)) publish_locked(d);
+    if (g_table[d].load(std::memory_order_relaxed)) publish_locked(d, false);
   return AR_OK;
 }
 
