@@ -6,7 +6,7 @@ and the operation's own knobs (chunk size, ubatch split and grid, sequence
 number, output count), then compares every output with the oracle bit for
 bit.  The reduce family runs the one-shot, the fused, staged and
 static-scratch two-stage, and the ubatch reduce on the flat or the bounded
-grid.  The
+grid; the payload family ends with the plain or the waiting unpack.  The
 seed of a failing case is in the assertion message.  AR_FUZZ_SEEDS=<k> in
 the environment runs k seeds per family.
 """
@@ -108,7 +108,8 @@ def test_fuzz_payload_family(seed):
     seq0 = int(rng.choice([0, 1, 0x7FFFFFFF, 0xFFFFFFFE, 0xFFFFFFFF, int(rng.integers(0, 2 ** 32))]))
     staged = bool(rng.integers(0, 2))
     carry = (not staged) and bool(rng.integers(0, 2))
-    tag = f"seed {seed}: P={P} n={n} {kind} seq0={seq0:#x} staged={staged} carry={carry}"
+    wait = bool(rng.integers(0, 2))
+    tag = f"seed {seed}: P={P} n={n} {kind} seq0={seq0:#x} staged={staged} carry={carry} wait={wait}"
     note(f"fuzz payload {tag}")
     W = n // 2
     words = [torch.empty(max(W, 1), dtype=torch.int64, device=DEV) for _ in range(P)]
@@ -121,7 +122,10 @@ def test_fuzz_payload_family(seed):
     tar.ar_rd_schedule(words, rdo, seq0, err, mailbox=mbox, flags=flags, n=n)
     L = {2: 1, 4: 2, 8: 3}[P]
     out = empty16(max(n, 1))
-    tar.ar_unpack_fused(rdo[P - 1], out, (seq0 + L) & 0xFFFFFFFF, err, n=n)
+    if wait:   # the payload is already written: the waiting unpack must take every word at once
+        tar.ar_unpack_fused_wait(rdo[P - 1], out, (seq0 + L) & 0xFFFFFFFF, err, n=n)
+    else:
+        tar.ar_unpack_fused(rdo[P - 1], out, (seq0 + L) & 0xFFFFFFFF, err, n=n)
     torch.cuda.synchronize()
     ow = [oracle.pack(x, seq0) for x in xs]
     for p in range(P):
