@@ -587,24 +587,29 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
         xi = [x[:m] for x in ins]
         xo = [o[:m] for o in outs]
         sc = e16(m)
+        xb = [x.clone() for x in xi]   # the in-place call's buffers (only timed: their values grow)
         key = f"{2 * m // 1024}KiB"
         lat[key] = {}
-        for which, name in ((0, "oneshot"), (1, "2stage_fused"), (2, "2stage_staged")):
-            us = blib.arb_stream_us(which, parr(xi), parr(xo), P, m, sc.data_ptr(), 5000, sh)
+        for which, name, bi, bo in ((0, "oneshot", xi, xo), (1, "2stage_fused", xi, xo),
+                                    (1, "2stage_fused_inplace", xb, xb), (2, "2stage_staged", xi, xo)):
+            us = blib.arb_stream_us(which, parr(bi), parr(bo), P, m, sc.data_ptr(), 5000, sh)
             p50, p10, p90 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
-            rc = blib.arb_wall_us(which, parr(xi), parr(xo), P, m, sc.data_ptr(), 2000, sh,
+            rc = blib.arb_wall_us(which, parr(bi), parr(bo), P, m, sc.data_ptr(), 2000, sh,
                                   ctypes.byref(p50), ctypes.byref(p10), ctypes.byref(p90))
             if rc != 0:
                 raise RuntimeError(f"arb_wall_us failed: {rc}")
             cred = (P + 1) * 2 * m if which == 0 else 2 * P * 2 * m
-            enq = blib.arb_enqueue_us(which, parr(xi), parr(xo), P, m, sc.data_ptr(), 5000, sh)
+            enq = blib.arb_enqueue_us(which, parr(bi), parr(bo), P, m, sc.data_ptr(), 5000, sh)
             if enq < 0:
                 raise RuntimeError(f"arb_enqueue_us failed: {enq}")
             lat[key][name] = {"stream_us": round(us, 2), "wall_us_p50": round(p50.value, 2),
                               "wall_us_p90": round(p90.value, 2), "host_enqueue_us": round(enq, 2),
                               "GBps_hot": round(cred / (us * 1e-6) / 1e9, 1)}
     # host cost of a launch itself: empty kernels with no, 8 or 192 bytes of
-    # arguments (the library's kernels take about 180 bytes)
+    # arguments.  HIP enqueues a kernel whose argument segment is at most 112
+    # bytes faster; the decode-size one-shot, in-place fused two-stage, pack
+    # and unpack kernels take 28-80 bytes and no hidden arguments, the others
+    # about 300-440 bytes
     lat["empty_kernel_host_enqueue_us"] = {
         k: round(blib.arb_enqueue_us(w, None, None, 0, 0, None, 5000, sh), 2)
         for k, w in (("no_arguments", -1), ("8_byte_argument", -2), ("192_byte_argument", -3))}

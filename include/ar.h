@@ -258,8 +258,8 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
  * `wg_per_cu` workgroups per compute unit (0 = no cap; enforced by
  * requesting unused LDS).  `vec` (1 or 2) sets how much each lane handles:
  *   ONESHOT, 2STAGE, UBATCH, UBATCH_FLAGS, RD, QUANT_FP8 and their _SMALL
- *     kinds: vec 16-byte groups per buffer, each a contiguous span across
- *     the wavefront;
+ *     kinds, 2STAGE_INPLACE_SMALL: vec 16-byte groups per buffer, each a
+ *     contiguous span across the wavefront;
  *   PACK, UNPACK and their _SMALL kinds: 1 -> 8 bytes of bf16 (one 16-byte
  *     payload access) per lane, 2 -> 16 bytes of bf16 (two adjacent payload
  *     accesses);
@@ -273,13 +273,18 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
  * The one-shot, fused two-stage, fused recursive-doubling, staged
  * recursive-doubling-step, pack and unpack kernels have a second kind each
  * (..._SMALL) whose shape applies when a call's element count n is at most
- * AR_SMALL_ELEMS (4 MiB of bf16 per rank: the decode messages).  Such a
- * call moves too
- * little data for the occupancy cap that helps long streams; its time is
- * launch, one memory round trip and the number of workgroup rounds, so its
- * default is uncapped with plain loads, which also keep data that is already
- * on chip there (and, for the staged step, plain stores, which keep each
- * step's mailbox on chip for the next step).
+ * AR_SMALL_ELEMS (4 MiB of bf16 per rank: the decode messages); the fused
+ * two-stage has a third for such calls made in place
+ * (2STAGE_INPLACE_SMALL).  Such a call moves too little data for the
+ * occupancy cap that helps long streams; its time is launch, one memory
+ * round trip and the number of workgroup rounds, so its default is uncapped
+ * with plain loads, which also keep data that is already on chip there (and,
+ * for the staged step, plain stores, which keep each step's mailbox on chip
+ * for the next step).  With one group per lane, the one-shot, in-place fused
+ * two-stage, pack and unpack small kinds launch kernels with a compact
+ * argument segment (28-80 bytes, no hidden arguments), which HIP enqueues
+ * faster: the host's launch cost bounds a decode-size call made outside a
+ * graph.
  */
 #define AR_SMALL_ELEMS 2097152
 #define AR_KERNEL_ONESHOT  0   /* ar_reduce_oneshot                         */
@@ -308,6 +313,11 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
                                       (1..8) is the footprint in eighths of
                                       the device: cus * wg_per_cu / 8
                                       workgroups; no LDS is requested    */
+#define AR_KERNEL_2STAGE_INPLACE_SMALL 21 /* ar_reduce_2stage fused with
+                                      outs[r] == ins[r] for every r,
+                                      n <= AR_SMALL_ELEMS: a read-modify-
+                                      write of the same lines, tuned apart
+                                      from 2STAGE_SMALL                   */
 int ar_set_launch_shape(int kind, int block, int vec, int nt_loads, int stores, int wg_per_cu);
 int ar_get_launch_shape(int kind, int* block, int* vec, int* nt_loads, int* stores,
                         int* wg_per_cu);

@@ -30,6 +30,7 @@ __all__ = [
     "AR_KERNEL_QUANT_FP8", "AR_KERNEL_REDUCE_FP8", "AR_KERNEL_REDUCE_FP8_ALL", "ar_quantize_fp8", "ar_reduce_fp8", "fp8_scale_count",
     "AR_KERNEL_ONESHOT_SMALL", "AR_KERNEL_2STAGE_SMALL", "AR_KERNEL_RD_SMALL", "AR_KERNEL_RDSTEP_SMALL",
     "AR_KERNEL_PACK_SMALL", "AR_KERNEL_UNPACK_SMALL", "AR_KERNEL_UBATCH_BOUNDED",
+    "AR_KERNEL_2STAGE_INPLACE_SMALL",
     "AR_SMALL_ELEMS",
     "FP8_BLOCK",
 ]
@@ -69,6 +70,7 @@ AR_KERNEL_RDSTEP_SMALL = 17
 AR_KERNEL_PACK_SMALL = 18
 AR_KERNEL_UNPACK_SMALL = 19
 AR_KERNEL_UBATCH_BOUNDED = 20
+AR_KERNEL_2STAGE_INPLACE_SMALL = 21
 AR_SMALL_ELEMS = 2097152
 FP8_BLOCK = 32                  # elements per power-of-two scale
 

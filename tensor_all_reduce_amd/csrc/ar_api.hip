@@ -54,20 +54,23 @@ constexpr ar::Shape kDefaultShape[] = {
     {64, 2, 1, 3, 0, 0},    // fp8 quantise, 1 -> 1 + scales, buffer after buffer
     {256, 1, 1, 1, 6, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)
     {256, 1, 1, 3, 3, 0},   // fp8 reduce, P code streams -> P outputs
-    {128, 1, 0, 1, 0, 0},   // one-shot, n <= AR_SMALL_ELEMS: uncapped, plain loads
-    {128, 1, 0, 1, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
-    {64, 1, 0, 1, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
+    {128, 1, 0, 2, 0, 0},   // one-shot, n <= AR_SMALL_ELEMS: uncapped, plain loads, SC1 stores
+    {128, 1, 0, 2, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
+    {64, 1, 0, 2, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
     {64, 1, 0, 0, 0, 0},    // staged RD step, n <= AR_SMALL_ELEMS: plain stores keep the mailbox on chip
     {256, 1, 0, 3, 0, 0},   // pack, n <= AR_SMALL_ELEMS: plain loads, uncapped, SC1 stores
-    {256, 1, 0, 1, 0, 0},   // unpack, n <= AR_SMALL_ELEMS
+    {256, 1, 0, 2, 0, 0},   // unpack, n <= AR_SMALL_ELEMS
     {512, 1, 1, 1, 4, 0},   // bounded ubatch: 512-lane workgroups on 4/8 of the CUs (wg_per_cu: eighths)
+    {128, 1, 1, 1, 0, 0},   // in-place fused two-stage, n <= AR_SMALL_ELEMS: NT loads, so the NT stores
+                            // that rewrite the same lines find them marked streaming
 };
 constexpr const char* kShapeEnv[] = {
     "AR_SHAPE_ONESHOT", "AR_SHAPE_2STAGE", "AR_SHAPE_UBATCH", "AR_SHAPE_RS", "AR_SHAPE_AG",
     "AR_SHAPE_PACK", "AR_SHAPE_UNPACK", "AR_SHAPE_RD", "AR_SHAPE_RDSTEP", "AR_SHAPE_UNPACK_WAIT",
     "AR_SHAPE_UBATCH_FLAGS", "AR_SHAPE_QUANT_FP8", "AR_SHAPE_REDUCE_FP8", "AR_SHAPE_REDUCE_FP8_ALL",
     "AR_SHAPE_ONESHOT_SMALL", "AR_SHAPE_2STAGE_SMALL", "AR_SHAPE_RD_SMALL", "AR_SHAPE_RDSTEP_SMALL",
-    "AR_SHAPE_PACK_SMALL", "AR_SHAPE_UNPACK_SMALL", "AR_SHAPE_UBATCH_BOUNDED"};
+    "AR_SHAPE_PACK_SMALL", "AR_SHAPE_UNPACK_SMALL", "AR_SHAPE_UBATCH_BOUNDED",
+    "AR_SHAPE_2STAGE_INPLACE_SMALL"};
 // one default and one override name per kind, in the order of ar.h's kind
 // numbers
 static_assert(sizeof(kDefaultShape) / sizeof(kDefaultShape[0]) == ar::kKinds, "a default shape per kind");
@@ -81,7 +84,9 @@ static_assert(ar::kOneshot == AR_KERNEL_ONESHOT && ar::k2Stage == AR_KERNEL_2STA
                   ar::kOneshotSmall == AR_KERNEL_ONESHOT_SMALL && ar::k2StageSmall == AR_KERNEL_2STAGE_SMALL &&
                   ar::kRDSmall == AR_KERNEL_RD_SMALL && ar::kRDStepSmall == AR_KERNEL_RDSTEP_SMALL &&
                   ar::kPackSmall == AR_KERNEL_PACK_SMALL && ar::kUnpackSmall == AR_KERNEL_UNPACK_SMALL &&
-                  ar::kUbatchBounded == AR_KERNEL_UBATCH_BOUNDED && ar::kKinds == AR_KERNEL_UBATCH_BOUNDED + 1,
+                  ar::kUbatchBounded == AR_KERNEL_UBATCH_BOUNDED &&
+                  ar::k2StageInplaceSmall == AR_KERNEL_2STAGE_INPLACE_SMALL &&
+                  ar::kKinds == AR_KERNEL_2STAGE_INPLACE_SMALL + 1,
               "kind numbers match ar.h");
 
 // What one device's calls read: its CU count and the launch shapes with

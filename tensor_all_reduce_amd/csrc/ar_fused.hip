@@ -64,16 +64,35 @@ __device__ __forceinline__ void wave_flush(const WaveErr& e, uint64_t* err) {
 // (the launch shape that measured fastest for streaming on MI355X).  The
 // ragged end (the data words past the last whole run) is done by the last
 // workgroup.
+//
+// Pack and unpack take the workgroup size as a template constant BLOCK for
+// small messages (0: read blockDim and gridDim).  The kernel then reads no
+// hidden dispatch arguments, its argument segment is its explicit arguments
+// alone (32 and 40 bytes instead of 288 and 296), and HIP enqueues a kernel
+// whose segment is at most 112 bytes about 0.7 us faster: the cost that
+// bounds a decode-size call issued from the host.  The last workgroup is then
+// computed from n, the same way the launcher sizes the grid.
 
 // Pack: lane v turns data words [WPL*v, WPL*v + WPL) (WPL = 2: 8 bytes of
 // bf16; 4: 16 bytes) into WPL payload words (16 or 32 bytes).  WPL = 2 makes
 // every wavefront store instruction one contiguous 1 KiB: with WPL = 4 each
 // lane stores two adjacent 16-byte groups, so each instruction covers a
 // 2 KiB span half-filled, and that measured 8% slower.
-template <int WPL, bool NTL, int SP>
-__global__ __launch_bounds__(kMaxBlock) void k_pack(const void* x, uint64_t* w, size_t n, uint32_t seq) {
+// Whether this is the grid's last workgroup: from the template constant
+// (grid = max(1, ceil(lanes / BLOCK)), as flat_grid sizes it) or from the
+// dispatch.
+template <int BLOCK>
+__device__ __forceinline__ bool last_group(size_t lanes) {
+  if constexpr (BLOCK > 0) return blockIdx.x == (unsigned)(lanes ? (lanes - 1) / BLOCK : 0);
+  else return blockIdx.x == gridDim.x - 1;
+}
+
+template <int WPL, bool NTL, int SP, int BLOCK>
+__global__ __launch_bounds__(BLOCK > 0 ? BLOCK : kMaxBlock) void k_pack(const void* x, uint64_t* w, size_t n,
+                                                                        uint32_t seq) {
   const size_t nl = (n >> 1) / WPL;
-  const size_t v0 = (size_t)blockIdx.x * blockDim.x;  // the workgroup's first lane
+  const unsigned nthr = BLOCK > 0 ? (unsigned)BLOCK : blockDim.x;
+  const size_t v0 = (size_t)blockIdx.x * nthr;  // the workgroup's first lane
   const size_t v = v0 + threadIdx.x;
   if (v < nl) {
     u32x4* dst = reinterpret_cast<u32x4*>(w);
@@ -81,19 +100,19 @@ __global__ __launch_bounds__(kMaxBlock) void k_pack(const void* x, uint64_t* w, 
       const uint64_t d = ld8<NTL>(static_cast<const uint64_t*>(x) + v);
       u32x4 a;
       a[0] = (uint32_t)d; a[1] = seq; a[2] = (uint32_t)(d >> 32); a[3] = seq;
-      st16<SP>(dst + v0, blockDim.x * 16u, threadIdx.x * 16u, a);
+      st16<SP>(dst + v0, nthr * 16u, threadIdx.x * 16u, a);
     } else {
       const u32x4 d = ld4<NTL>(static_cast<const u32x4*>(x) + v);
       u32x4 a, b;
       a[0] = d[0]; a[1] = seq; a[2] = d[1]; a[3] = seq;
       b[0] = d[2]; b[1] = seq; b[2] = d[3]; b[3] = seq;
-      st16<SP>(dst + 2 * v0, blockDim.x * 32u, threadIdx.x * 32u, a);
-      st16<SP>(dst + 2 * v0, blockDim.x * 32u, threadIdx.x * 32u + 16u, b);
+      st16<SP>(dst + 2 * v0, nthr * 32u, threadIdx.x * 32u, a);
+      st16<SP>(dst + 2 * v0, nthr * 32u, threadIdx.x * 32u + 16u, b);
     }
   }
   // tail: n is even, so fewer than WPL whole data words remain
   const size_t j = nl * WPL + threadIdx.x;
-  if (blockIdx.x == gridDim.x - 1 && j < (n >> 1)) {
+  if (last_group<BLOCK>(nl) && j < (n >> 1)) {
     const uint32_t d = static_cast<const uint32_t*>(x)[j];
     w[j] = ((uint64_t)seq << 32) | (uint64_t)d;
   }
@@ -102,11 +121,12 @@ __global__ __launch_bounds__(kMaxBlock) void k_pack(const void* x, uint64_t* w, 
 // Unpack + validate: lane v reads payload words [WPL*v, WPL*v + WPL) and
 // writes their data words (WPL = 2: one 16-byte load, one 8-byte store, each
 // wavefront instruction contiguous; WPL = 4: two adjacent 16-byte loads).
-template <int WPL, bool NTL, int SP>
-__global__ __launch_bounds__(kMaxBlock) void k_unpack(const uint64_t* w, void* x, size_t n, uint32_t seq,
-                                                     uint64_t* err) {
+template <int WPL, bool NTL, int SP, int BLOCK>
+__global__ __launch_bounds__(BLOCK > 0 ? BLOCK : kMaxBlock) void k_unpack(const uint64_t* w, void* x, size_t n,
+                                                                          uint32_t seq, uint64_t* err) {
   const size_t nl = (n >> 1) / WPL;
-  const size_t v0 = (size_t)blockIdx.x * blockDim.x;
+  const unsigned nthr = BLOCK > 0 ? (unsigned)BLOCK : blockDim.x;
+  const size_t v0 = (size_t)blockIdx.x * nthr;
   const size_t v = v0 + threadIdx.x;
   const bool act = v < nl;
   const u32x4* src = reinterpret_cast<const u32x4*>(w);
@@ -114,14 +134,14 @@ __global__ __launch_bounds__(kMaxBlock) void k_unpack(const uint64_t* w, void* x
   if (act) {
     if constexpr (WPL == 2) {
       a = ld4<NTL>(src + v);
-      st8p<SP>(static_cast<uint64_t*>(x) + v0, blockDim.x * 8u, threadIdx.x * 8u,
+      st8p<SP>(static_cast<uint64_t*>(x) + v0, nthr * 8u, threadIdx.x * 8u,
                (uint64_t)a[0] | ((uint64_t)a[2] << 32));
     } else {
       a = ld4<NTL>(src + 2 * v);
       b = ld4<NTL>(src + 2 * v + 1);
       u32x4 d;
       d[0] = a[0]; d[1] = a[2]; d[2] = b[0]; d[3] = b[2];
-      st16<SP>(static_cast<u32x4*>(x) + v0, blockDim.x * 16u, threadIdx.x * 16u, d);
+      st16<SP>(static_cast<u32x4*>(x) + v0, nthr * 16u, threadIdx.x * 16u, d);
     }
   }
   const bool b0 = a[1] != seq, b1 = a[3] != seq, b2 = b[1] != seq, b3 = b[3] != seq;
@@ -137,7 +157,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_unpack(const uint64_t* w, void* x
   }
   wave_flush(e, err);
   const size_t j = nl * WPL + threadIdx.x;
-  if (blockIdx.x == gridDim.x - 1 && j < (n >> 1)) {
+  if (last_group<BLOCK>(nl) && j < (n >> 1)) {
     const uint64_t wj = w[j];
     static_cast<uint32_t*>(x)[j] = (uint32_t)wj;
     if ((uint32_t)(wj >> 32) != seq) {
@@ -427,41 +447,56 @@ hipError_t rd_fused_p(const Launch& L, const WordIn& in, const WordOut& out, siz
 }  // namespace
 
 template <int WPL>
-hipError_t pack_w(const Shape& sh, hipStream_t st, const void* x, uint64_t* w, size_t n, uint32_t seq) {
+hipError_t pack_w(const Shape& sh, hipStream_t st, const void* x, uint64_t* w, size_t n, uint32_t seq,
+                  bool small) {
   const size_t nl = (n >> 1) / WPL;
   if (!grid_fits(sh, nl)) return hipErrorInvalidConfiguration;
   const unsigned g = flat_grid(sh, nl);
-  const dim3 b(sh.block);
-  return with_policy(sh, [&](auto ntl, auto sp) {
-    return launch_k(k_pack<WPL, decltype(ntl)::value, decltype(sp)::value>, g, b, sh.lds, st, x, w, n, seq);
-  });
+  auto go = [&](auto blk) {
+    return with_policy(sh, [&](auto ntl, auto sp) {
+      return launch_k(k_pack<WPL, decltype(ntl)::value, decltype(sp)::value, decltype(blk)::value>, g,
+                      dim3(sh.block), sh.lds, st, x, w, n, seq);
+    });
+  };
+  if (small && sh.block == 64) return go(SPc<64>{});
+  if (small && sh.block == 128) return go(SPc<128>{});
+  if (small && sh.block == 256) return go(SPc<256>{});
+  return go(SPc<0>{});
 }
 
 template <int WPL>
 hipError_t unpack_w(const Shape& sh, hipStream_t st, const uint64_t* w, void* x, size_t n, uint32_t seq,
-                    uint64_t* d_err) {
+                    uint64_t* d_err, bool small) {
   const size_t nl = (n >> 1) / WPL;
   if (!grid_fits(sh, nl)) return hipErrorInvalidConfiguration;
   const unsigned g = flat_grid(sh, nl);
-  const dim3 b(sh.block);
-  return with_policy(sh, [&](auto ntl, auto sp) {
-    return launch_k(k_unpack<WPL, decltype(ntl)::value, decltype(sp)::value>, g, b, sh.lds, st, w, x, n, seq, d_err);
-  });
+  auto go = [&](auto blk) {
+    return with_policy(sh, [&](auto ntl, auto sp) {
+      return launch_k(k_unpack<WPL, decltype(ntl)::value, decltype(sp)::value, decltype(blk)::value>, g,
+                      dim3(sh.block), sh.lds, st, w, x, n, seq, d_err);
+    });
+  };
+  if (small && sh.block == 64) return go(SPc<64>{});
+  if (small && sh.block == 128) return go(SPc<128>{});
+  if (small && sh.block == 256) return go(SPc<256>{});
+  return go(SPc<0>{});
 }
 
 // For pack and unpack the shape's vec counts 16-byte groups of bf16 per lane:
 // 1 -> 2 data words (8 bytes) per lane, 2 -> 4 data words (16 bytes).
 hipError_t launch_pack(const Launch& L, const void* x, uint64_t* w, size_t n, uint32_t seq) {
-  const Shape& sh = shape_for(L, kPack, kPackSmall, n);
-  if (sh.vec == 2) return pack_w<4>(sh, L.stream, x, w, n, seq);
-  return pack_w<2>(sh, L.stream, x, w, n, seq);
+  const bool small = n <= (size_t)AR_SMALL_ELEMS;
+  const Shape& sh = small ? L.shape[kPackSmall] : L.shape[kPack];
+  if (sh.vec == 2) return pack_w<4>(sh, L.stream, x, w, n, seq, small);
+  return pack_w<2>(sh, L.stream, x, w, n, seq, small);
 }
 
 hipError_t launch_unpack(const Launch& L, const uint64_t* w, void* x, size_t n, uint32_t seq,
                          uint64_t* d_err) {
-  const Shape& sh = shape_for(L, kUnpack, kUnpackSmall, n);
-  if (sh.vec == 2) return unpack_w<4>(sh, L.stream, w, x, n, seq, d_err);
-  return unpack_w<2>(sh, L.stream, w, x, n, seq, d_err);
+  const bool small = n <= (size_t)AR_SMALL_ELEMS;
+  const Shape& sh = small ? L.shape[kUnpackSmall] : L.shape[kUnpack];
+  if (sh.vec == 2) return unpack_w<4>(sh, L.stream, w, x, n, seq, d_err, small);
+  return unpack_w<2>(sh, L.stream, w, x, n, seq, d_err, small);
 }
 
 hipError_t launch_rd_fused(const Launch& L, const WordIn& in, const WordOut& out, int P, size_t n,

@@ -52,6 +52,7 @@ enum Kind {
   kPackSmall,    // kPack for n <= AR_SMALL_ELEMS
   kUnpackSmall,  // kUnpack for n <= AR_SMALL_ELEMS
   kUbatchBounded, // chunked reduce on a persistent grid of a fraction of the CUs
+  k2StageInplaceSmall, // k2StageSmall when every output is its own input
   kKinds
 };
 

@@ -51,15 +51,19 @@ namespace ar {
 // increment follows its workgroup's acknowledged stores, so a consumer that
 // acquire-loads done[chunk] == epoch (which invalidates its own L2 and L1
 // copies) sees the whole chunk of every output.
+//
+// `nthr` is the workgroup size (blockDim.x, or a compile-time constant where
+// the kernel must not read the dispatch's hidden arguments).
 template <int P, int NOUT, int V, bool NTL, int SP, bool SIG>
-__device__ __forceinline__ void reduce_tile(const InPtrs& in, const OutPtrs& out, size_t b0, size_t b1) {
+__device__ __forceinline__ void reduce_tile(const InPtrs& in, const OutPtrs& out, size_t b0, size_t b1,
+                                            unsigned nthr) {
   const size_t vb0 = (b0 + 7) >> 3, vb1 = b1 >> 3;
   static_assert(!SIG || SP >= 2, "completion flags need write-through stores");
 
   u32x4 x[V][P];
 #pragma unroll
   for (int u = 0; u < V; ++u) {
-    const size_t v = vb0 + threadIdx.x + (size_t)u * blockDim.x;
+    const size_t v = vb0 + threadIdx.x + (size_t)u * nthr;
     if (v < vb1) {
 #pragma unroll
       for (int p = 0; p < P; ++p) x[u][p] = ld4<NTL>(static_cast<const u32x4*>(in.p[p]) + v);
@@ -67,7 +71,7 @@ __device__ __forceinline__ void reduce_tile(const InPtrs& in, const OutPtrs& out
   }
 #pragma unroll
   for (int u = 0; u < V; ++u) {
-    const size_t v = vb0 + threadIdx.x + (size_t)u * blockDim.x;
+    const size_t v = vb0 + threadIdx.x + (size_t)u * nthr;
     if (v < vb1) {
       const u32x4 r = reduce8<P>(x[u]);
 #pragma unroll
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(kMaxBlock) void k_reduce(InPtrs in, OutPtrs out, si
   const size_t b0 = c0 + (size_t)t * span;
   if (b0 >= c1) return;
   const size_t b1 = b0 + span < c1 ? b0 + span : c1;
-  reduce_tile<P, NOUT, V, NTL, SP, SIG>(in, out, b0, b1);
+  reduce_tile<P, NOUT, V, NTL, SP, SIG>(in, out, b0, b1, blockDim.x);
   if constexpr (SIG) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -144,8 +148,47 @@ __global__ __launch_bounds__(kMaxBlockBounded) void k_reduce_bounded(InPtrs in, 
     const size_t b0 = c0 + t * span;
     if (b0 >= c1) continue;
     const size_t b1 = b0 + span < c1 ? b0 + span : c1;
-    reduce_tile<P, NOUT, V, NTL, SP, false>(in, out, b0, b1);
+    reduce_tile<P, NOUT, V, NTL, SP, false>(in, out, b0, b1, blockDim.x);
   }
+}
+
+// ----------------------------------------------------------------------------
+// One-shot for small messages (n <= AR_SMALL_ELEMS) with a compact kernel
+// argument segment: the input pointers, the output and n, 80 bytes, and no
+// hidden arguments (the workgroup size is the template constant BLOCK, so the
+// kernel never reads blockDim).  A decode-size one-shot is bound by the
+// host's cost of enqueueing it, and HIP enqueues a kernel whose argument
+// segment is at most 112 bytes about 0.7 us faster than a larger one;
+// k_reduce's segment is 440 bytes (its chunk and signal arguments, then the
+// hidden arguments that reading blockDim brings).  One group per lane; the
+// tiles, and so the results, are k_reduce's with a single chunk.
+template <int P, int BLOCK, bool NTL, int SP>
+__global__ __launch_bounds__(BLOCK) void k_oneshot_small(InPtrs in, void* out, size_t n) {
+  constexpr size_t span = (size_t)BLOCK * 8;
+  const size_t b0 = (size_t)blockIdx.x * span;
+  if (b0 >= n) return;
+  const size_t b1 = b0 + span < n ? b0 + span : n;
+  OutPtrs o{};
+  o.p[0] = out;
+  reduce_tile<P, 1, 1, NTL, SP, false>(in, o, b0, b1, BLOCK);
+}
+
+// In-place fused two-stage for small messages: every output is its own input
+// (the all-reduce's usual form, each rank's result in its own tensor), so
+// the P buffer pointers and n, 72 bytes, are the whole argument segment --
+// under HIP's fast-enqueue size, as for k_oneshot_small.  Each group is read
+// from every buffer by one lane before that lane writes it back to all of
+// them, so reading and writing the same buffers is safe.
+template <int P, int BLOCK, bool NTL, int SP>
+__global__ __launch_bounds__(BLOCK) void k_2stage_small_inplace(OutPtrs io, size_t n) {
+  constexpr size_t span = (size_t)BLOCK * 8;
+  const size_t b0 = (size_t)blockIdx.x * span;
+  if (b0 >= n) return;
+  const size_t b1 = b0 + span < n ? b0 + span : n;
+  InPtrs in;
+#pragma unroll
+  for (int p = 0; p < AR_MAX_RANKS; ++p) in.p[p] = io.p[p];
+  reduce_tile<P, P, 1, NTL, SP, false>(in, io, b0, b1, BLOCK);
 }
 
 // ----------------------------------------------------------------------------
@@ -269,6 +312,57 @@ hipError_t range_p(const Shape& sh, hipStream_t st, const InPtrs& in, const OutP
   return range_v<P, NOUT, 1>(sh, st, in, out, e0, e1, chunk, sig);
 }
 
+template <int P, int BLOCK>
+hipError_t oneshot_small_b(const Shape& sh, hipStream_t st, const InPtrs& in, void* out, size_t n) {
+  const size_t blocks = cdiv(n, (size_t)BLOCK * 8);
+  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_oneshot_small<P, BLOCK, decltype(ntl)::value, decltype(sp)::value>, (unsigned)blocks,
+                    dim3(BLOCK), sh.lds, st, in, out, n);
+  });
+}
+
+// The compact kernel for one group per lane; a shape with two groups per
+// lane takes k_reduce.
+template <int P>
+hipError_t oneshot_small_p(const Shape& sh, hipStream_t st, const InPtrs& in, void* out, size_t n) {
+  if (sh.vec == 1) {
+    if (sh.block == 64) return oneshot_small_b<P, 64>(sh, st, in, out, n);
+    if (sh.block == 128) return oneshot_small_b<P, 128>(sh, st, in, out, n);
+    if (sh.block == 256) return oneshot_small_b<P, 256>(sh, st, in, out, n);
+  }
+  OutPtrs o{};
+  o.p[0] = out;
+  return range_p<P, 1>(sh, st, in, o, 0, n, n);
+}
+
+template <int P, int BLOCK>
+hipError_t inplace_small_b(const Shape& sh, hipStream_t st, const OutPtrs& io, size_t n) {
+  const size_t blocks = cdiv(n, (size_t)BLOCK * 8);
+  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
+  return with_policy(sh, [&](auto ntl, auto sp) {
+    return launch_k(k_2stage_small_inplace<P, BLOCK, decltype(ntl)::value, decltype(sp)::value>, (unsigned)blocks,
+                    dim3(BLOCK), sh.lds, st, io, n);
+  });
+}
+
+// Fused two-stage for small messages.  In place (every output its own
+// input) it takes the in-place kind's shape, and the compact kernel when that
+// shape has one group per lane; otherwise the small kind's shape and
+// k_reduce.
+template <int P>
+hipError_t fused_small_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_t n) {
+  bool inplace = true;
+  for (int p = 0; p < P; ++p) inplace = inplace && out.p[p] == in.p[p];
+  const Shape& sh = inplace ? L.shape[k2StageInplaceSmall] : L.shape[k2StageSmall];
+  if (inplace && sh.vec == 1) {
+    if (sh.block == 64) return inplace_small_b<P, 64>(sh, L.stream, out, n);
+    if (sh.block == 128) return inplace_small_b<P, 128>(sh, L.stream, out, n);
+    if (sh.block == 256) return inplace_small_b<P, 256>(sh, L.stream, out, n);
+  }
+  return range_p<P, P>(sh, L.stream, in, out, 0, n, n);
+}
+
 template <int P>
 hipError_t staged_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_t n, void* scratch) {
   const size_t S = cdiv(cdiv(n, 8), P) * 8;
@@ -305,14 +399,20 @@ hipError_t staged_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_
   }
 
 hipError_t launch_oneshot(const Launch& L, const InPtrs& in, int P, void* out, size_t n) {
+  if (n <= (size_t)AR_SMALL_ELEMS) {
+    AR_DISPATCH_P(P, (oneshot_small_p<PP>(L.shape[kOneshotSmall], L.stream, in, out, n)))
+  }
   OutPtrs o{};
   o.p[0] = out;
-  AR_DISPATCH_P(P, (range_p<PP, 1>(shape_for(L, kOneshot, kOneshotSmall, n), L.stream, in, o, 0, n, n)))
+  AR_DISPATCH_P(P, (range_p<PP, 1>(L.shape[kOneshot], L.stream, in, o, 0, n, n)))
 }
 
 hipError_t launch_2stage_fused(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,
                                size_t n) {
-  AR_DISPATCH_P(P, (range_p<PP, PP>(shape_for(L, k2Stage, k2StageSmall, n), L.stream, in, out, 0, n, n)))
+  if (n <= (size_t)AR_SMALL_ELEMS) {
+    AR_DISPATCH_P(P, (fused_small_p<PP>(L, in, out, n)))
+  }
+  AR_DISPATCH_P(P, (range_p<PP, PP>(L.shape[k2Stage], L.stream, in, out, 0, n, n)))
 }
 
 hipError_t launch_2stage_staged(const Launch& L, const InPtrs& in, const OutPtrs& out, int P,

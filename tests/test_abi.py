@@ -274,13 +274,14 @@ def test_binding_raises_on_error():
 
 def test_launch_shape_roundtrip_and_validation():
     L = tar.lib()
-    for kind in range(20):
+    for kind in [k for k in range(tar.AR_KERNEL_2STAGE_INPLACE_SMALL + 1) if k != tar.AR_KERNEL_UBATCH_BOUNDED]:
         before = tar.ar_get_launch_shape(kind)
         tar.ar_set_launch_shape(kind, 128, 2, 0, 1, 7)
         assert tar.ar_get_launch_shape(kind) == (128, 2, 0, 1, 7)
         tar.ar_set_launch_shape(kind, *before)
         assert tar.ar_get_launch_shape(kind) == before
-    assert L.ar_set_launch_shape(20, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
+    assert L.ar_set_launch_shape(20, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID   # the bounded grid: 256..1024 lanes
+    assert L.ar_set_launch_shape(tar.AR_KERNEL_2STAGE_INPLACE_SMALL + 1, 64, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 96, 1, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 3, 1, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 1, 2, 1, 0) == tar.AR_ERR_INVALID

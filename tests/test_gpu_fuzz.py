@@ -4,9 +4,10 @@ Each case draws the rank count, the element count (tiny, ragged, or a few
 tiles), the value mix (normal, log-uniform, integers, or specials mixed in),
 and the operation's own knobs (chunk size, ubatch split and grid, sequence
 number, output count), then compares every output with the oracle bit for
-bit.  The reduce family runs the one-shot, the fused, staged and
-static-scratch two-stage, and the ubatch reduce on the flat or the bounded
-grid; the payload family ends with the plain or the waiting unpack.  The
+bit.  The reduce family runs the one-shot, the fused (separate outputs and
+in place), staged and static-scratch two-stage, and the ubatch reduce on the
+flat or the bounded grid; the payload family ends with the plain or the
+waiting unpack.  The
 seed of a failing case is in the assertion message.  AR_FUZZ_SEEDS=<k> in
 the environment runs k seeds per family.
 """
@@ -75,9 +76,11 @@ def test_fuzz_reduce_family(seed):
     tar.ar_reduce_2stage(ins, outs2, scratch=scratch, n=n)
     outs3 = [empty16(max(n, 1)) for _ in range(P)]
     tar.ar_reduce_2stage_static(ins, outs3, n=n)
+    bufs = [up16(x) if n else empty16(1) for x in xs]    # fused, in place
+    tar.ar_reduce_2stage(bufs, bufs, n=n)
     torch.cuda.synchronize()
     eq(down16(out)[:n], ref, f"{tag} oneshot")
-    for o in outs + outs2 + outs3:
+    for o in outs + outs2 + outs3 + bufs:
         eq(down16(o)[:n], ref, f"{tag} 2stage")
     # ubatch: a random factorisation of n into rows x hidden and a random split
     if n:

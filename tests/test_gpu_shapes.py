@@ -5,7 +5,8 @@ non-temporal loads / stores, workgroups per CU); each choice is a different
 kernel instantiation or grid.  Here each kind is run under a grid of shapes
 on ragged sizes (tails inside a 16-byte group and inside a tile) and every
 result is compared with the oracle, bit for bit; the default shape is
-restored afterwards.  The one-shot, fused two-stage, fused RD, staged RD,
+restored afterwards (the fused two-stage also in place, which at small sizes
+takes its own compact kernel).  The one-shot, fused two-stage, fused RD, staged RD,
 pack and unpack calls pick their small-message kind at n <= AR_SMALL_ELEMS
 and their large-message kind above it, so those run at one size on each side
 of the threshold.
@@ -59,7 +60,7 @@ def with_shape(kinds, shape, fn):
 
 
 ONESHOT_KINDS = (tar.AR_KERNEL_ONESHOT, tar.AR_KERNEL_ONESHOT_SMALL)
-TWOSTAGE_KINDS = (tar.AR_KERNEL_2STAGE, tar.AR_KERNEL_2STAGE_SMALL)
+TWOSTAGE_KINDS = (tar.AR_KERNEL_2STAGE, tar.AR_KERNEL_2STAGE_SMALL, tar.AR_KERNEL_2STAGE_INPLACE_SMALL)
 RD_KINDS = (tar.AR_KERNEL_RD, tar.AR_KERNEL_RD_SMALL)
 RDSTEP_KINDS = (tar.AR_KERNEL_RDSTEP, tar.AR_KERNEL_RDSTEP_SMALL)
 PACK_KINDS = (tar.AR_KERNEL_PACK, tar.AR_KERNEL_PACK_SMALL)
@@ -85,6 +86,11 @@ def test_reduce_kinds(shape):
         with_shape(TWOSTAGE_KINDS, shape, lambda: tar.ar_reduce_2stage(ins, outs))
         for o in outs:
             eq(down16(o), ref, f"2stage n={n}")
+        note(f"shape {shape}: 2stage fused in place n={n}")
+        bufs = [up16(x) for x in xs]
+        with_shape(TWOSTAGE_KINDS, shape, lambda: tar.ar_reduce_2stage(bufs, bufs))
+        for b in bufs:
+            eq(down16(b), ref, f"2stage in place n={n}")
     ins = [up16(x) for x in XS]
     note(f"shape {shape}: 2stage staged (rs, then ag)")
     for kind in (tar.AR_KERNEL_RS, tar.AR_KERNEL_AG):
