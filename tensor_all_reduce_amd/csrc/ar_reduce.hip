@@ -201,20 +201,25 @@ __global__ __launch_bounds__(BLOCK) void k_2stage_small_inplace(OutPtrs io, size
 // The ragged tail (n not a multiple of 8) lies in the last non-empty shard;
 // trailing shards past it are empty (lo == hi == n) and do nothing, so the
 // tail elements are written by one workgroup only.
-template <int P, bool NTL, int SP>
-__global__ __launch_bounds__(kMaxBlock) void k_rs(InPtrs in, void* scratch, size_t n, size_t S) {
+//
+// The workgroup size is the template constant BLOCK (64, 128 or 256), so the
+// kernels read no hidden dispatch arguments: their argument segments are 88
+// bytes, under the size that HIP enqueues about 0.7 us faster, which is what
+// a decode-size staged call made from the host waits on (two launches).
+template <int P, int BLOCK, bool NTL, int SP>
+__global__ __launch_bounds__(BLOCK) void k_rs(InPtrs in, void* scratch, size_t n, size_t S) {
   const unsigned s = blockIdx.x % P;
   const size_t j = blockIdx.x / P;
   const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
   const size_t hi = lo + S < n ? lo + S : n;
   if (lo >= hi) return;
-  const size_t w0 = (lo >> 3) + j * blockDim.x;  // this workgroup's first group
+  const size_t w0 = (lo >> 3) + j * BLOCK;  // this workgroup's first group
   const size_t v = w0 + threadIdx.x;
   if (v < (hi >> 3)) {
     u32x4 a[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(static_cast<const u32x4*>(in.p[p]) + v);
-    st16<SP>(static_cast<u32x4*>(scratch) + w0, blockDim.x * 16u, threadIdx.x * 16u, reduce8<P>(a));
+    st16<SP>(static_cast<u32x4*>(scratch) + w0, BLOCK * 16u, threadIdx.x * 16u, reduce8<P>(a));
   }
   if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
     const size_t i = ((hi >> 3) << 3) + threadIdx.x;
@@ -225,19 +230,19 @@ __global__ __launch_bounds__(kMaxBlock) void k_rs(InPtrs in, void* scratch, size
   }
 }
 
-template <int P, bool NTL, int SP>
-__global__ __launch_bounds__(kMaxBlock) void k_ag(const void* scratch, OutPtrs out, size_t n, size_t S) {
+template <int P, int BLOCK, bool NTL, int SP>
+__global__ __launch_bounds__(BLOCK) void k_ag(const void* scratch, OutPtrs out, size_t n, size_t S) {
   const unsigned s = blockIdx.x % P;
   const size_t j = blockIdx.x / P;
   const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
   const size_t hi = lo + S < n ? lo + S : n;
   if (lo >= hi) return;
-  const size_t w0 = (lo >> 3) + j * blockDim.x;
+  const size_t w0 = (lo >> 3) + j * BLOCK;
   const size_t v = w0 + threadIdx.x;
   if (v < (hi >> 3)) {
     const u32x4 a = ld4<NTL>(static_cast<const u32x4*>(scratch) + v);
 #pragma unroll
-    for (int p = 0; p < P; ++p) st16<SP>(static_cast<u32x4*>(out.p[p]) + w0, blockDim.x * 16u, threadIdx.x * 16u, a);
+    for (int p = 0; p < P; ++p) st16<SP>(static_cast<u32x4*>(out.p[p]) + w0, BLOCK * 16u, threadIdx.x * 16u, a);
   }
   if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
     const size_t i = ((hi >> 3) << 3) + threadIdx.x;
@@ -372,15 +377,22 @@ hipError_t staged_p(const Launch& L, const InPtrs& in, const OutPtrs& out, size_
   // both grids are checked before the first launch
   if (bps_rs * P > 0x7FFFFFFFull || bps_ag * P > 0x7FFFFFFFull) return hipErrorInvalidConfiguration;
   const unsigned g_rs = (unsigned)(bps_rs * P), g_ag = (unsigned)(bps_ag * P);
-  hipError_t e = with_policy(rs, [&](auto ntl, auto sp) {
-    return launch_k(k_rs<P, decltype(ntl)::value, decltype(sp)::value>, g_rs, dim3(rs.block), rs.lds, L.stream, in,
-                    scratch, n, S);
-  });
+  auto rs_go = [&](auto blk) {
+    return with_policy(rs, [&](auto ntl, auto sp) {
+      return launch_k(k_rs<P, decltype(blk)::value, decltype(ntl)::value, decltype(sp)::value>, g_rs,
+                      dim3(decltype(blk)::value), rs.lds, L.stream, in, scratch, n, S);
+    });
+  };
+  auto ag_go = [&](auto blk) {
+    return with_policy(ag, [&](auto ntl, auto sp) {
+      return launch_k(k_ag<P, decltype(blk)::value, decltype(ntl)::value, decltype(sp)::value>, g_ag,
+                      dim3(decltype(blk)::value), ag.lds, L.stream, (const void*)scratch, out, n, S);
+    });
+  };
+  // the shape table holds only 64-, 128- or 256-lane blocks for these kinds
+  hipError_t e = rs.block == 64 ? rs_go(SPc<64>{}) : rs.block == 128 ? rs_go(SPc<128>{}) : rs_go(SPc<256>{});
   if (e != hipSuccess) return e;
-  return with_policy(ag, [&](auto ntl, auto sp) {
-    return launch_k(k_ag<P, decltype(ntl)::value, decltype(sp)::value>, g_ag, dim3(ag.block), ag.lds, L.stream,
-                    (const void*)scratch, out, n, S);
-  });
+  return ag.block == 64 ? ag_go(SPc<64>{}) : ag.block == 128 ? ag_go(SPc<128>{}) : ag_go(SPc<256>{});
 }
 
 }  // namespace
