@@ -27,6 +27,9 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(b, v, ntl, nts, wg) for b, v, ntl, nts, wg in
           itertools.product((64, 256), (1, 2), (0, 1), (0, 1), (0, 3))]
+# 128-lane workgroups (each a compile-time block size of the small-message and
+# staged kernels) with the two write-through store policies
+SHAPES += [(128, 1, 0, 2, 0), (128, 1, 1, 3, 0), (128, 2, 1, 2, 3), (128, 2, 0, 3, 0)]
 P = 8
 N = 5 * 4096 + 22          # even; not a multiple of 8 or 16
 ROWS, HIDDEN = 11, 1862    # 20482 elements, odd row count and a hidden size not a multiple of 8
