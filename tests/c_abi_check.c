@@ -6,8 +6,9 @@
  * Inputs are small integers (rank p, element i: ((7 i + 13 p) mod 33) - 16,
  * in [-16, 16]), so every partial sum over P = 8 ranks is an integer of
  * magnitude at most 128: exact in binary32 and in bf16 whatever the order of
- * the additions.  Every schedule (one-shot, both two-stage modes, recursive
- * doubling with bf16 or binary32 partials, the two-stream ubatch reduce)
+ * the additions.  Every schedule (one-shot, both two-stage modes, the fused
+ * one in place, the staged one on the static scratch, recursive doubling
+ * with bf16 or binary32 partials, the two-stream ubatch reduce)
  * must therefore return exactly the integer sum, which this program computes
  * on its own with integer arithmetic.  n is ragged (not a multiple of 8) and
  * spans many tiles.
@@ -133,6 +134,27 @@ int c_abi_check(void) {
     }
   }
 
+  /* fused two-stage in place (each rank's result in its own buffer), then the
+     staged two-stage on the library's static scratch */
+  if (!bad) {
+    for (int p = 0; p < P; ++p) HIP(hipMemcpy(outs[p], ins[p], N * 2, hipMemcpyDeviceToDevice));
+    AR(ar_reduce_2stage((const void* const*)outs, outs, P, N, NULL, st));
+    HIP(hipStreamSynchronize(st));
+    for (int p = 0; p < P && !bad; ++p) {
+      HIP(hipMemcpy(got, outs[p], N * 2, hipMemcpyDeviceToHost));
+      bad |= check16("in-place two-stage", got, want, N);
+    }
+  }
+  if (!bad) {
+    for (int p = 0; p < P; ++p) HIP(hipMemset(outs[p], 0, N * 2));
+    AR(ar_reduce_2stage_static((const void* const*)ins, outs, P, N, st));
+    HIP(hipStreamSynchronize(st));
+    for (int p = 0; p < P && !bad; ++p) {
+      HIP(hipMemcpy(got, outs[p], N * 2, hipMemcpyDeviceToHost));
+      bad |= check16("static-scratch two-stage", got, want, N);
+    }
+  }
+
   /* pack -> recursive doubling (fused R1, fused R2, staged) -> unpack */
   const int modes[3] = {0, AR_RD_FP32_CARRY, AR_RD_STAGED};
   for (int k = 0; k < 3 && !bad; ++k) {
@@ -195,8 +217,9 @@ int c_abi_check(void) {
   free(got);
   if (bad) return 1;
   snprintf(g_msg, sizeof g_msg,
-           "c-abi check: one-shot, two-stage (fused, staged), recursive doubling (R1, R2, staged) and the "
-           "two-stream ubatch reduce exact on %d x %zu elements (library version %d)", P, N, ar_version());
+           "c-abi check: one-shot, two-stage (fused, staged, in place, static scratch), recursive doubling "
+           "(R1, R2, staged) and the two-stream ubatch reduce exact on %d x %zu elements (library version %d)",
+           P, N, ar_version());
   return 0;
 }
 
