@@ -110,7 +110,10 @@ int ar_reduce_oneshot(const void* const* ins, int P, void* out, size_t n, void* 
  *                    scratch holds n bf16, disjoint from every other buffer,
  *                    and afterwards holds the reduced values.
  *   outs   host array of P device pointers (n bf16 each); outs[r] may equal
- *          an input exactly; outputs must be pairwise disjoint.
+ *          an input exactly; outputs must be pairwise disjoint.  With
+ *          outs[r] == ins[r] for every r (in place) and n <= AR_SMALL_ELEMS,
+ *          the fused form runs under its own launch shape
+ *          (AR_KERNEL_2STAGE_INPLACE_SMALL); the result is the same.
  * Errors: as ar_reduce_oneshot.
  */
 int ar_reduce_2stage(const void* const* ins, void* const* outs, int P, size_t n,
