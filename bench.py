@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--ab", action="store_true",
                     help="instead of the step: A/B of the launch shapes and store policies of the 8 -> 8 "
                          "and 8 -> 1 kernels and of the ubatch schedule, as a text report")
+    ap.add_argument("--ab-small", action="store_true",
+                    help="instead of the step: A/B of the small-message kinds' launch shapes at the decode "
+                         "sizes, timed inside HIP graphs, as a text report")
     return ap.parse_args()
 
 
@@ -183,6 +186,10 @@ def main():
 
     def e64(m):
         return torch.empty(m, dtype=torch.int64, device=dev)
+
+    if args.ab_small:
+        ab_small_report(tar, torch, synth, dev, main_s)
+        return 0
 
     log(f"device {props.name}, {props.multi_processor_count} CUs; allocating the prefill batch")
     ins = [t.view(torch.int16) for t in synth.device_rank_buffers("normal", P, n, 4, dev)]
@@ -1044,6 +1051,114 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
     log("ab: bounded footprint done")
     del ga, gb, gc
     placement_report(tar, torch, dev, main_s, s0, s1, ins, outs, uin, ubo, time_calls)
+
+
+def ab_small_report(tar, torch, synth, dev, main_s):
+    """A/B of the small-message kinds (n <= AR_SMALL_ELEMS) at the decode sizes.
+
+    Each kind -- one-shot, fused two-stage with separate outputs and in
+    place, pack, unpack, fused RD, staged RD step -- is timed under every
+    (block 64/128/256, plain or non-temporal loads, store policy 0..3) with
+    one group per lane and no cap, at 128 KiB, 512 KiB and 2 MiB per rank
+    (P = 8), inside a HIP graph of 100 calls replayed 20 times, so the host's
+    launch cost does not hide the kernels' differences; three shuffled
+    rounds, median.  Score: the geometric mean over the sizes of the time
+    against the best shape at that size.  The six best shapes and the
+    default are printed per kind."""
+    import math
+    import random
+    import statistics
+
+    side = torch.cuda.Stream()
+    sizes = (8, 32, 128)                       # rows of hidden 8192: 128 KiB, 512 KiB, 2 MiB per rank
+
+    def graph_us(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            fn()
+            side.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(100):
+                    fn()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(main_s)
+        for _ in range(20):
+            g.replay()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / 2000
+
+    data = {}
+    for T in sizes:
+        m = T * HIDDEN
+        xs = [x.view(torch.int16) for x in synth.device_rank_buffers("normal", P, m, 3, dev)]
+        d = {"xs": xs, "outs": [torch.empty(m, dtype=torch.int16, device=dev) for _ in range(P)],
+             "bufs": [x.clone() for x in xs], "x1": torch.empty(m, dtype=torch.int16, device=dev),
+             "words": [torch.empty(m // 2, dtype=torch.int64, device=dev) for _ in range(P)],
+             "rdo": [torch.empty(m // 2, dtype=torch.int64, device=dev) for _ in range(P)],
+             "err": torch.empty(2, dtype=torch.int64, device=dev),
+             "mbox": torch.empty(tar.rd_mailbox_words(P, m), dtype=torch.int64, device=dev)}
+        for r in range(P):
+            tar.ar_pack_fused(xs[r], d["words"][r], 1)
+        tar.ar_err_init(d["err"])
+        data[T] = d
+
+    def call(kind, d):
+        if kind == tar.AR_KERNEL_ONESHOT_SMALL:
+            return lambda: tar.ar_reduce_oneshot(d["xs"], d["outs"][0], stream=side)
+        if kind == tar.AR_KERNEL_2STAGE_SMALL:
+            return lambda: tar.ar_reduce_2stage(d["xs"], d["outs"], stream=side)
+        if kind == tar.AR_KERNEL_2STAGE_INPLACE_SMALL:
+            return lambda: tar.ar_reduce_2stage(d["bufs"], d["bufs"], stream=side)
+        if kind == tar.AR_KERNEL_PACK_SMALL:
+            return lambda: tar.ar_pack_fused(d["xs"][0], d["words"][0], 1, stream=side)
+        if kind == tar.AR_KERNEL_UNPACK_SMALL:
+            return lambda: tar.ar_unpack_fused(d["words"][1], d["x1"], 1, d["err"], stream=side)
+        if kind == tar.AR_KERNEL_RD_SMALL:
+            return lambda: tar.ar_rd_schedule(d["words"], d["rdo"], 1, d["err"], stream=side)
+        return lambda: tar.ar_rd_schedule(d["words"], d["rdo"], 1, d["err"], mailbox=d["mbox"],
+                                          flags=tar.AR_RD_STAGED, stream=side)
+
+    kinds = (("ONESHOT_SMALL", tar.AR_KERNEL_ONESHOT_SMALL), ("2STAGE_SMALL", tar.AR_KERNEL_2STAGE_SMALL),
+             ("2STAGE_INPLACE_SMALL", tar.AR_KERNEL_2STAGE_INPLACE_SMALL), ("PACK_SMALL", tar.AR_KERNEL_PACK_SMALL),
+             ("UNPACK_SMALL", tar.AR_KERNEL_UNPACK_SMALL), ("RD_SMALL", tar.AR_KERNEL_RD_SMALL),
+             ("RDSTEP_SMALL", tar.AR_KERNEL_RDSTEP_SMALL))
+    cands = [(b, 1, l, st, 0) for b in (64, 128, 256) for l in (0, 1) for st in (0, 1, 2, 3)]
+    props = torch.cuda.get_device_properties(dev)
+    print("# A/B of the small-message kinds at the decode sizes: P=8, [T x 8192] per rank, T = 8 / 32 / 128")
+    print("# command: python bench.py --ab-small   (per-call time inside HIP graphs of 100 calls, "
+          "3 shuffled rounds, median)")
+    print(f"# device: {props.name}, {props.multi_processor_count} CUs")
+    print("# score: geometric mean over the sizes of time / best time at that size (1.000 = best everywhere)")
+    rng = random.Random(17)
+    for name, kind in kinds:
+        default = tar.ar_get_launch_shape(kind)
+        cs = cands + ([default] if default not in cands else [])
+        t = {(c, T): [] for c in cs for T in sizes}
+        for _ in range(3):
+            order = list(t)
+            rng.shuffle(order)
+            for c, T in order:
+                tar.ar_set_launch_shape(kind, *c)
+                t[(c, T)].append(graph_us(call(kind, data[T])))
+        tar.ar_set_launch_shape(kind, *default)
+        med = {k: statistics.median(v) for k, v in t.items()}
+        best = {T: min(med[(c, T)] for c in cs) for T in sizes}
+        score = {c: math.exp(sum(math.log(med[(c, T)] / best[T]) for T in sizes) / len(sizes)) for c in cs}
+        ranked = sorted(cs, key=lambda c: score[c])
+        print(f"== {name}: default {default}")
+        print("   block vec ntl stores wg/cu   score    128KiB     512KiB    2048KiB")
+        for c in ranked[:6] + ([default] if default not in ranked[:6] else []):
+            tag = "  <- default" if c == default else ""
+            print(f"   {c[0]:5d} {c[1]:3d} {c[2]:3d} {c[3]:6d} {c[4]:5d}  {score[c]:6.3f}  "
+                  + "  ".join(f"{med[(c, T)]:7.2f}us" for T in sizes) + tag)
+        sys.stdout.flush()
+        log(f"ab-small: {name} done")
 
 
 def placement_report(tar, torch, dev, main_s, s0, s1, ins, outs, uin, ubo, time_calls):
