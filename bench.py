@@ -226,7 +226,7 @@ def main():
                  "rd": "k_rd_fused<8,R1>", "unpack": "k_unpack", "ubatch": "k_reduce<8,8> chunked, x2 concurrent"}
     step_bytes = sum(credited.values())
 
-    def run_row(name, seq):
+    def run_row(name, seq, uev=None):
         if name == "oneshot":
             tar.ar_reduce_oneshot(ins, out1)
         elif name == "2stage":
@@ -241,12 +241,20 @@ def main():
             for r in range(P):
                 tar.ar_unpack_fused(rdo[r], ux[r], seq + 3, err)
         elif name == "ubatch":
+            # the two-stream timing protocol: a start event on stream A (s0),
+            # ordered after the step's earlier rows, that B (s1) waits on; one
+            # ubatch on each; A waits for B's end event and records its own.
+            # The row is timed from A's start event to A's end event.
+            start, end, b_end = uev if uev is not None else [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             s0.wait_stream(main_s)
-            s1.wait_stream(main_s)
+            start.record(s0)
+            s1.wait_event(start)
             tar.ar_reduce_ubatch(uin, ubo, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE,
                                  [s0, s1])
+            b_end.record(s1)
+            s0.wait_event(b_end)
+            end.record(s0)
             main_s.wait_stream(s0)
-            main_s.wait_stream(s1)
 
     # ---------------------------------------------------------------- timed steps
     log(f"warmup {args.warmup} steps")
@@ -256,18 +264,21 @@ def main():
     torch.cuda.synchronize()
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(rows) + 1)] for _ in range(K)]
+    uev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
         ev[k][0].record(main_s)
         for i, r in enumerate(rows):
-            run_row(r, k + 1)
+            run_row(r, k + 1, uev[k])
             ev[k][i + 1].record(main_s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev[0][0].elapsed_time(ev[K - 1][len(rows)])
     row_ms = {r: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)) / K for i, r in enumerate(rows)}
+    # the ubatch row by its own protocol events on stream A (start to end)
+    row_ms["ubatch"] = sum(uev[k][0].elapsed_time(uev[k][1]) for k in range(K)) / K
     e = err.cpu().numpy().view(np.uint64)
     assert int(e[0]) == 0, "sequence-number mismatches in the bench step"
     # every output of the step agrees with the one-shot result on device
@@ -382,28 +393,32 @@ def gates(tar, torch, main_s, ins, outs, uin, ubo, s0, s1):
                        >= 80% of 8 TB/s means <= 671 us per call
       c5_ubatch        P=8 [16384 x 16384], ar_reduce_ubatch, two-stage, two
                        8192-row ubatches on two streams, 1 MiB chunks:
-                       <= 1.342 ms per call
+                       <= 1.342 ms per call; each call by the two-stream
+                       protocol (a start event on stream A that B waits on,
+                       one ubatch on each, A waits for B's end), the
+                       bracket's events on A
       c4_oneshot       ar_reduce_oneshot (no target), writing the P output
                        buffers in turn: its 256 MiB output would otherwise
                        stay in the 256 MiB last-level cache between calls
                        and never pay its write-back"""
-    def bracket(fn, brackets=30, target_ms=100.0):
+    def bracket(fn, brackets=30, target_ms=100.0, st=None):
+        st = main_s if st is None else st          # the stream the bracket's events are recorded on
         for _ in range(20):
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(main_s)
+        e0.record(st)
         for _ in range(10):
             fn()
-        e1.record(main_s)
+        e1.record(st)
         e1.synchronize()
         k = max(10, int(target_ms / max(e0.elapsed_time(e1) / 10, 1e-3)) + 1)
         per = []
         for _ in range(brackets):
-            e0.record(main_s)
+            e0.record(st)
             for _ in range(k):
                 fn()
-            e1.record(main_s)
+            e1.record(st)
             e1.synchronize()
             per.append(e0.elapsed_time(e1) / k * 1e3)
         per.sort()
@@ -416,19 +431,26 @@ def gates(tar, torch, main_s, ins, outs, uin, ubo, s0, s1):
         turn[0] += 1
         tar.ar_reduce_oneshot(ins, outs[turn[0] % P])
 
-    def ubatch():
-        s0.wait_stream(main_s)
-        s1.wait_stream(main_s)
-        tar.ar_reduce_ubatch(uin, ubo, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, [s0, s1])
-        main_s.wait_stream(s0)
-        main_s.wait_stream(s1)
+    # the two-stream timing protocol, per call: a start event on stream A
+    # (s0) that B (s1) waits on, one ubatch on each, A waits for B's end; the
+    # bracket's own events are on A
+    u_start, u_bend = torch.cuda.Event(), torch.cuda.Event()
 
-    cases = (("c4_2stage_fused", lambda: tar.ar_reduce_2stage(ins, outs), 2 * P * 2 * n),
-             ("c5_ubatch", ubatch, 2 * P * 2 * n5),
-             ("c4_oneshot", oneshot, (P + 1) * 2 * n))
+    def ubatch():
+        u_start.record(s0)
+        s1.wait_event(u_start)
+        tar.ar_reduce_ubatch(uin, ubo, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, [s0, s1])
+        u_bend.record(s1)
+        s0.wait_event(u_bend)
+
+    s0.wait_stream(main_s)
+    cases = (("c4_2stage_fused", lambda: tar.ar_reduce_2stage(ins, outs), 2 * P * 2 * n, main_s),
+             ("c5_ubatch", ubatch, 2 * P * 2 * n5, s0),
+             ("c4_oneshot", oneshot, (P + 1) * 2 * n, main_s))
     res = {}
-    for name, fn, cred in cases:
-        med, p10, p90, k = bracket(fn)
+    for name, fn, cred, st in cases:
+        med, p10, p90, k = bracket(fn, st=st)
+        main_s.wait_stream(s0)
         gbps = cred / (med * 1e-6) / 1e9
         res[name] = {"us": round(med, 2), "us_p10": round(p10, 2), "us_p90": round(p90, 2), "calls_per_bracket": k,
                      "brackets": 30, "credited_bytes": cred, "GBps": round(gbps, 1),
@@ -535,29 +557,36 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     halves = [(parr([x[:h] for x in uin]), parr([o[:h] for o in ubo])),
               (parr([x[h:] for x in uin]), parr([o[h:] for o in ubo]))]
 
+    # timed by the same two-stream protocol as the ubatch row: per call a
+    # start event on s0 that s1 waits on, one half on each, s0 waits for s1's
+    # end; the bracket's events on s0
+    c_start, c_bend = torch.cuda.Event(), torch.cuda.Event()
+
     def two_streams(vec, wg):
-        s0.wait_stream(main_s)
-        s1.wait_stream(main_s)
+        c_start.record(s0)
+        s1.wait_event(c_start)
         for (pi, po), st in zip(halves, (s0, s1)):
             if blib.arb_copy_multi(pi, po, P, 2 * h, vec, wg, st.cuda_stream) != 0:
                 raise RuntimeError("arb_copy_multi failed")
-        main_s.wait_stream(s0)
-        main_s.wait_stream(s1)
+        c_bend.record(s1)
+        s0.wait_event(c_bend)
 
     best2, shape2 = 0.0, None
+    s0.wait_stream(main_s)
     for vec in (1, 2):
         for wg in (4, 5, 6, 8):
             for _ in range(2):
                 two_streams(vec, wg)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(main_s)
+            e0.record(s0)
             for _ in range(8):
                 two_streams(vec, wg)
-            e1.record(main_s)
+            e1.record(s0)
             torch.cuda.synchronize()
             gbps = 2 * P * 2 * n5 * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
             if gbps > best2:
                 best2, shape2 = gbps, {"vec": vec, "wg_per_cu": wg}
+    main_s.wait_stream(s0)
     res["copy_8to8_two_streams_GBps"] = round(best2, 1)
     res["copy_8to8_two_streams_shape"] = shape2
     # attainable read bandwidth: read-only sweep of the same 2 GiB
@@ -819,20 +848,29 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     reps = 10
 
     def ub_timed(variant, streams, nout):
+        # the two-stream protocol as in the step (start event on A that B
+        # waits on, A waits for B's end), the bracket's events on A
+        a, b = streams
+        start, b_end = torch.cuda.Event(), torch.cuda.Event()
+
         def go():
-            for st in set(streams):
-                st.wait_stream(main_s)
+            if b is not a:
+                start.record(a)
+                b.wait_event(start)
             tar.ar_reduce_ubatch(uin, ubo[:nout], UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, variant, streams)
-            for st in set(streams):
-                main_s.wait_stream(st)
+            if b is not a:
+                b_end.record(b)
+                a.wait_event(b_end)
+        a.wait_stream(main_s)
         for _ in range(3):
             go()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(main_s)
+        e0.record(a)
         for _ in range(reps):
             go()
-        e1.record(main_s)
+        e1.record(a)
         torch.cuda.synchronize()
+        main_s.wait_stream(a)
         return e0.elapsed_time(e1) / reps
 
     ms = ub_timed(tar.AR_VARIANT_ONESHOT, [s0, s1], 1)
