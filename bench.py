@@ -929,12 +929,20 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
             a[i] = t.data_ptr()
         return a
 
+    # two-stream calls follow the timing protocol: a start event on stream A
+    # (s0) that B waits on, one ubatch on each, A waits for B's end; they are
+    # timed on A (time_calls(fn, s0))
+    u_start, u_bend = torch.cuda.Event(), torch.cuda.Event()
+
     def ubatch(streams):
-        for st in set(streams):
-            st.wait_stream(main_s)
+        a, b = streams
+        if b is not a:
+            u_start.record(a)
+            b.wait_event(u_start)
         tar.ar_reduce_ubatch(uin, ubo, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, streams)
-        for st in set(streams):
-            main_s.wait_stream(st)
+        if b is not a:
+            u_bend.record(b)
+            a.wait_event(u_bend)
 
     turn = [0]
 
@@ -950,21 +958,28 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
         "rd": (tar.AR_KERNEL_RD, 4 * P * B, lambda: tar.ar_rd_schedule(words, rdo, 1, err),
                list(itertools.product((64,), (1,), (1,), (0, 1, 2, 3), (6, 8, 10)))),
         "ubatch_two_streams": (tar.AR_KERNEL_UBATCH, 2 * P * B5, lambda: ubatch([s0, s1]),
-                               list(itertools.product((64,), (1,), (1,), (1, 3), (3, 4, 6, 8)))),
+                               list(itertools.product((64,), (1,), (1,), (1, 3), (3, 4, 6, 8))), s0),
         "ubatch_one_stream": (tar.AR_KERNEL_UBATCH, 2 * P * B5, lambda: ubatch([s0, s0]),
-                              list(itertools.product((64,), (1,), (1,), (1, 3), (3, 4, 6, 8)))),
+                              list(itertools.product((64,), (1,), (1,), (1, 3), (3, 4, 6, 8))), s0),
     }
     reps, rounds = 4, 3
     rng = random.Random(11)
 
-    def time_calls(fn):
+    def time_calls(fn, st=None):
+        # events on `st` (default the launch stream); a stream other than the
+        # launch stream takes over from it, and hands back, outside the timing
+        st = main_s if st is None else st
+        if st is not main_s:
+            st.wait_stream(main_s)
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(main_s)
+        e0.record(st)
         for _ in range(reps):
             fn()
-        e1.record(main_s)
+        e1.record(st)
         e1.synchronize()
+        if st is not main_s:
+            main_s.wait_stream(st)
         return e0.elapsed_time(e1) / reps
 
     print("# A/B of launch shapes on the bench buffers: P=8, bf16 [16384 x 8192] per rank "
@@ -972,7 +987,9 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
     print(f"# command: python bench.py --ab   ({rounds} shuffled rounds x {reps} calls, median per candidate)")
     print(f"# device: {torch.cuda.get_device_properties(dev).name}, "
           f"{torch.cuda.get_device_properties(dev).multi_processor_count} CUs")
-    for name, (kind, cred, fn, cands) in kinds.items():
+    for name, spec in kinds.items():
+        kind, cred, fn, cands = spec[:4]
+        tst = spec[4] if len(spec) > 4 else None
         default = tar.ar_get_launch_shape(kind)
         if default not in cands:
             cands = cands + [default]
@@ -982,7 +999,7 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
             rng.shuffle(order)
             for c in order:
                 tar.ar_set_launch_shape(kind, *c)
-                times[c].append(time_calls(fn))
+                times[c].append(time_calls(fn, tst))
         tar.ar_set_launch_shape(kind, *default)
         med = {c: statistics.median(v) for c, v in times.items()}
         ranked = sorted(cands, key=lambda c: med[c])
@@ -999,10 +1016,10 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
     # references: the same access patterns copied with no arithmetic
     print("== reference copies (no arithmetic), best over the listed shapes")
 
-    def best_of(fn_by_shape, shapes, cred):
+    def best_of(fn_by_shape, shapes, cred, st=None):
         out = []
         for sh in shapes:
-            out.append((time_calls(lambda: fn_by_shape(sh)), sh))
+            out.append((time_calls(lambda: fn_by_shape(sh), st), sh))
         t, sh = min(out)
         return cred / (t * 1e-3) / 1e9, sh
 
@@ -1019,20 +1036,20 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
               (parr([x[h:] for x in uin]), parr([o[h:] for o in ubo]))]
 
     def copy_two(sh):
-        s0.wait_stream(main_s)
-        s1.wait_stream(main_s)
+        u_start.record(s0)
+        s1.wait_event(u_start)
         for (pi, po), st in zip(halves, (s0, s1)):
             if blib.arb_copy_multi(pi, po, P, 2 * h, sh[0], sh[1], st.cuda_stream) != 0:
                 raise RuntimeError("arb_copy_multi failed")
-        main_s.wait_stream(s0)
-        main_s.wait_stream(s1)
+        u_bend.record(s1)
+        s0.wait_event(u_bend)
 
     caps = (0, 4, 5, 6, 8)
     g, sh = best_of(copy8, [(v, w) for v in (1, 2) for w in caps], 2 * P * B)
     print(f"   8 -> 8 copy [16384 x 8192]             {g:9.1f} GB/s  (vec, wg/cu) = {sh}")
     g, sh = best_of(gather, [(nt, w) for nt in (0, 1) for w in (0, 8, 12, 16)], (P + 1) * B)
     print(f"   8 -> 1 XOR gather [16384 x 8192]       {g:9.1f} GB/s  (nt_stores, wg/cu) = {sh}")
-    g, sh = best_of(copy_two, [(v, w) for v in (1, 2) for w in caps], 2 * P * B5)
+    g, sh = best_of(copy_two, [(v, w) for v in (1, 2) for w in caps], 2 * P * B5, s0)
     print(f"   8 -> 8 copy [16384 x 16384], 2 streams {g:9.1f} GB/s  (vec, wg/cu) = {sh}")
     sys.stdout.flush()
 
@@ -1231,13 +1248,20 @@ def placement_report(tar, torch, dev, main_s, s0, s1, ins, outs, uin, ubo, time_
         b = [pool[k * e:k * e + elems] for k in range(2 * count)]
         return (b[0::2], b[1::2]) if alternating else (b[:count], b[count:])
 
+    # two-stream calls by the timing protocol, timed on stream A (s0)
+    u_start, u_bend = torch.cuda.Event(), torch.cuda.Event()
+
     def ubatch(i, o, streams):
+        a, b = streams
+
         def fn():
-            for st in set(streams):
-                st.wait_stream(main_s)
+            if b is not a:
+                u_start.record(a)
+                b.wait_event(u_start)
             tar.ar_reduce_ubatch(i, o, UB_ROWS, UB_HIDDEN, 2, None, CHUNK_BYTES, tar.AR_VARIANT_2STAGE, streams)
-            for st in set(streams):
-                main_s.wait_stream(st)
+            if b is not a:
+                u_bend.record(b)
+                a.wait_event(u_bend)
         return fn
 
     c4 = {"separate allocations (bench)": lambda: tar.ar_reduce_2stage(ins, outs)}
@@ -1256,14 +1280,14 @@ def placement_report(tar, torch, dev, main_s, s0, s1, ins, outs, uin, ubo, time_
     rounds = 3
     print("== buffer placement: the 8 -> 8 rate against the buffers' relative addresses "
           f"({rounds} shuffled rounds, median)")
-    for title, cases, cred in (("fused two-stage, P=8, 16 buffers of 256 MiB", c4, 2 * P * 2 * n),
-                               ("two-ubatch reduce, P=8, 16 buffers of 512 MiB", c5, 2 * P * 2 * n5)):
+    for title, cases, cred, tst in (("fused two-stage, P=8, 16 buffers of 256 MiB", c4, 2 * P * 2 * n, None),
+                                    ("two-ubatch reduce, P=8, 16 buffers of 512 MiB", c5, 2 * P * 2 * n5, s0)):
         times = {k: [] for k in cases}
         for _ in range(rounds):
             order = list(cases)
             rng.shuffle(order)
             for k in order:
-                times[k].append(time_calls(cases[k]))
+                times[k].append(time_calls(cases[k], tst))
         print(f"   {title}")
         print("   placement                                              ms      GB/s  frac-of-8TB/s")
         for k in cases:
