@@ -208,7 +208,8 @@ def ar_reduce_oneshot(ins: Sequence, out, n: int | None = None, stream=None) -> 
 
 def ar_reduce_2stage(ins: Sequence, outs: Sequence, scratch=None, n: int | None = None,
                      stream=None) -> None:
-    """Every outs[r][:n] = the one-shot sum; scratch given -> staged RS/AG."""
+    """Every outs[r][:n] = the one-shot sum; scratch given -> staged RS/AG.
+    outs may be ins itself (in place: each rank's result in its own buffer)."""
     n = ins[0].numel() if n is None else int(n)
     ip = _bufs(ins, 2, "ins", n)
     op = _bufs(outs, 2, "outs", n)
