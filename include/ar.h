@@ -283,11 +283,14 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
  * round trip and the number of workgroup rounds, so its default is uncapped
  * with plain loads, which also keep data that is already on chip there (and,
  * for the staged step, plain stores, which keep each step's mailbox on chip
- * for the next step).  With one group per lane, the one-shot, in-place fused
+ * for the next step).  With one group per lane, the one-shot, fused
  * two-stage, pack and unpack small kinds launch kernels with a compact
  * argument segment (28-80 bytes, no hidden arguments), which HIP enqueues
  * faster: the host's launch cost bounds a decode-size call made outside a
- * graph.
+ * graph.  The fused two-stage with separate outputs passes its buffers as
+ * 32-bit offsets from ins[0] in units of the largest power of two dividing
+ * every difference; a call with a buffer out of that reach (at least
+ * +-32 GiB) takes the general kernel, with the same result.
  */
 #define AR_SMALL_ELEMS 2097152
 #define AR_KERNEL_ONESHOT  0   /* ar_reduce_oneshot                         */

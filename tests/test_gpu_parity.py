@@ -151,6 +151,41 @@ def test_in_place():
     check_full(ins[3], ref, "in-place oneshot")
 
 
+def test_small_2stage_buffer_offsets():
+    """The small fused two-stage with separate outputs passes its buffers to
+    the kernel as signed 32-bit offsets from ins[0], in units of the largest
+    power of two dividing every difference, and takes the general kernel when
+    one does not fit.  All buffers are carved from one 33 GiB allocation, with
+    outs[0] moved: 128 KiB before ins[0] (a negative offset, 128 KiB units),
+    3 GiB plus 16 bytes past it (16-byte units, the smallest the alignment rule
+    allows; still within reach) and 33 GiB plus 16 bytes past it (beyond the
+    +-32 GiB reach of 16-byte units: the general kernel).  Each matches the
+    oracle."""
+    P, n = 8, 3 * 8192 + 5
+    S = 1 << 16                                    # element stride between carved buffers (128 KiB)
+    xs = synth.rank_buffers("normal", P, n, 4, 777)
+    ref = oracle.reduce_seq(xs)
+    near, far = (3 << 30) // 2 + 8, (33 << 30) // 2 + 8   # in elements
+    big = torch.empty(far + n, dtype=torch.int16, device=DEV)
+    try:
+        ins = [big[(1 + p) * S:(1 + p) * S + n] for p in range(P)]
+        for t, x in zip(ins, xs):
+            t.copy_(up16(x))
+        for out0_at, what in ((0, "outs[0] 128 KiB before ins[0]"), (near, "outs[0] 3 GiB + 16 B past ins[0]"),
+                              (far, "outs[0] 33 GiB + 16 B past ins[0]")):
+            outs = [big[out0_at:out0_at + n]] + [big[(1 + P + p) * S:(1 + P + p) * S + n] for p in range(1, P)]
+            for o in outs:
+                o.fill_(0x5A5A)
+            note(f"small two-stage, buffer offsets: {what}")
+            tar.ar_reduce_2stage(ins, outs)
+            torch.cuda.synchronize()
+            for r, o in enumerate(outs):
+                check_full(o, ref, f"{what}: rank {r}")
+    finally:
+        del big
+        torch.cuda.empty_cache()
+
+
 def test_canaries_untouched():
     """Outputs carved out of larger buffers: the guard bytes around them keep
     their pattern, so no kernel writes outside [0, n)."""
