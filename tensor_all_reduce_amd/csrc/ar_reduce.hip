@@ -162,11 +162,16 @@ __global__ __launch_bounds__(kMaxBlockBounded) void k_reduce_bounded(InPtrs in, 
 // k_reduce's segment is 440 bytes (its chunk and signal arguments, then the
 // hidden arguments that reading blockDim brings).  One group per lane; the
 // tiles, and so the results, are k_reduce's with a single chunk.
+//
+// The grid is cdiv(n, 8 * BLOCK), so every workgroup's tile starts below n;
+// the compact kernels have no early exit on b0 >= n (where reduce_tile would
+// touch nothing anyway), so that the compiler loads n and the buffer
+// pointers from the argument segment together instead of one after the
+// other.
 template <int P, int BLOCK, bool NTL, int SP>
 __global__ __launch_bounds__(BLOCK) void k_oneshot_small(InPtrs in, void* out, size_t n) {
   constexpr size_t span = (size_t)BLOCK * 8;
   const size_t b0 = (size_t)blockIdx.x * span;
-  if (b0 >= n) return;
   const size_t b1 = b0 + span < n ? b0 + span : n;
   OutPtrs o{};
   o.p[0] = out;
@@ -183,7 +188,6 @@ template <int P, int BLOCK, bool NTL, int SP>
 __global__ __launch_bounds__(BLOCK) void k_2stage_small_inplace(OutPtrs io, size_t n) {
   constexpr size_t span = (size_t)BLOCK * 8;
   const size_t b0 = (size_t)blockIdx.x * span;
-  if (b0 >= n) return;
   const size_t b1 = b0 + span < n ? b0 + span : n;
   InPtrs in;
 #pragma unroll
@@ -205,7 +209,6 @@ template <int P, int BLOCK, bool NTL, int SP>
 __global__ __launch_bounds__(BLOCK) void k_2stage_small_offs(PtrOffsets po, size_t n) {
   constexpr size_t span = (size_t)BLOCK * 8;
   const size_t b0 = (size_t)blockIdx.x * span;
-  if (b0 >= n) return;
   const size_t b1 = b0 + span < n ? b0 + span : n;
   InPtrs in{};
   OutPtrs out{};
@@ -227,7 +230,10 @@ __global__ __launch_bounds__(BLOCK) void k_2stage_small_offs(PtrOffsets po, size
 //
 // The ragged tail (n not a multiple of 8) lies in the last non-empty shard;
 // trailing shards past it are empty (lo == hi == n) and do nothing, so the
-// tail elements are written by one workgroup only.
+// tail elements are written by one workgroup only.  An empty shard's group
+// range is empty by itself (v >= n / 8), so only the tail write tests
+// lo < hi: with no early exit the compiler loads every argument at once
+// instead of the shard bounds first and the pointers after them.
 //
 // The workgroup size is the template constant BLOCK (64, 128 or 256), so the
 // kernels read no hidden dispatch arguments: their argument segments are 88
@@ -239,7 +245,6 @@ __global__ __launch_bounds__(BLOCK) void k_rs(InPtrs in, void* scratch, size_t n
   const size_t j = blockIdx.x / P;
   const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
   const size_t hi = lo + S < n ? lo + S : n;
-  if (lo >= hi) return;
   const size_t w0 = (lo >> 3) + j * BLOCK;  // this workgroup's first group
   const size_t v = w0 + threadIdx.x;
   if (v < (hi >> 3)) {
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(BLOCK) void k_rs(InPtrs in, void* scratch, size_t n
     for (int p = 0; p < P; ++p) a[p] = ld4<NTL>(static_cast<const u32x4*>(in.p[p]) + v);
     st16<SP>(static_cast<u32x4*>(scratch) + w0, BLOCK * 16u, threadIdx.x * 16u, reduce8<P>(a));
   }
-  if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
+  if (j == 0 && lo < hi && ((hi >> 3) << 3) + threadIdx.x < hi) {
     const size_t i = ((hi >> 3) << 3) + threadIdx.x;
     const uint16_t* in16[P];
 #pragma unroll
@@ -263,7 +268,6 @@ __global__ __launch_bounds__(BLOCK) void k_ag(const void* scratch, OutPtrs out, 
   const size_t j = blockIdx.x / P;
   const size_t lo = (size_t)s * S < n ? (size_t)s * S : n;
   const size_t hi = lo + S < n ? lo + S : n;
-  if (lo >= hi) return;
   const size_t w0 = (lo >> 3) + j * BLOCK;
   const size_t v = w0 + threadIdx.x;
   if (v < (hi >> 3)) {
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(BLOCK) void k_ag(const void* scratch, OutPtrs out, 
 #pragma unroll
     for (int p = 0; p < P; ++p) st16<SP>(static_cast<u32x4*>(out.p[p]) + w0, BLOCK * 16u, threadIdx.x * 16u, a);
   }
-  if (j == 0 && ((hi >> 3) << 3) + threadIdx.x < hi) {
+  if (j == 0 && lo < hi && ((hi >> 3) << 3) + threadIdx.x < hi) {
     const size_t i = ((hi >> 3) << 3) + threadIdx.x;
     const uint16_t r = static_cast<const uint16_t*>(scratch)[i];
 #pragma unroll
