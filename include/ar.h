@@ -283,7 +283,8 @@ int ar_reduce_ubatch(const void* const* ins, void* const* outs, int P, size_t ro
  * round trip and the number of workgroup rounds, so its default is uncapped
  * with plain loads, which also keep data that is already on chip there (and,
  * for the staged step, plain stores, which keep each step's mailbox on chip
- * for the next step).  With one group per lane, the one-shot, fused
+ * for the next step); the in-place kind, which rewrites the lines it has
+ * just read, is fastest with non-temporal loads and stores.  With one group per lane, the one-shot, fused
  * two-stage, pack and unpack small kinds launch kernels with a compact
  * argument segment (28-80 bytes, no hidden arguments), which HIP enqueues
  * faster: the host's launch cost bounds a decode-size call made outside a

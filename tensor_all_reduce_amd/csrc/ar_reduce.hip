@@ -196,9 +196,10 @@ __global__ __launch_bounds__(BLOCK) void k_2stage_small_inplace(OutPtrs io, size
 }
 
 // Fused two-stage for small messages with separate outputs: the 2P - 1
-// buffers other than ins[0] are passed as 32-bit byte offsets from it (the
-// host checks that every one fits), so the argument segment is 80 bytes
-// instead of 16 pointers (128 bytes, over HIP's fast-enqueue size).
+// buffers other than ins[0] are passed as signed 32-bit offsets from it, in
+// units of 2^shift bytes (the host picks the unit and checks that every
+// offset fits), so the argument segment is 80 bytes instead of 2P pointers
+// and n (136 bytes at P = 8, over HIP's fast-enqueue size).
 struct PtrOffsets {
   const char* base;                     // ins[0]
   int32_t off[2 * AR_MAX_RANKS - 1];    // ins[1..P-1], then outs[0..P-1], from base, in units of 1 << shift bytes
