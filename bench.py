@@ -675,8 +675,34 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
         "cores": len(per_core), "fastest_core": fastest,
         "empty_kernel_192_byte_argument": spread(v[0] for v in per_core.values()),
         "oneshot_128KiB": spread(v[1] for v in per_core.values())}
+
+    # the 128 KiB fused two-stage called from Python on the current stream:
+    # through the wrapper, whose checks and marshalling run on every call,
+    # and through a handle from tar.prepare, marshalled once; host time per
+    # call over a loop of calls, and the stream time of the same loop
+    def py_loop(fn, k=3000):
+        for _ in range(300):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        t0 = time.perf_counter()
+        for _ in range(k):
+            fn()
+        t1 = time.perf_counter()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        return round((t1 - t0) / k * 1e6, 2), round(e0.elapsed_time(e1) * 1e3 / k, 2)
+
+    h2 = tar.prepare(tar.ar_reduce_2stage, xi, xo)
+    wh, ws = py_loop(lambda: tar.ar_reduce_2stage(xi, xo))
+    ph, ps = py_loop(h2)
+    lat["python_binding_128KiB_2stage_fused"] = {"wrapper_host_us": wh, "wrapper_stream_us": ws,
+                                                 "prepared_host_us": ph, "prepared_stream_us": ps}
+    del h2
     res["latency"] = lat
-    log("latency measured")
+    log(f"latency measured; from Python at 128 KiB: wrapper {wh} us host / {ws} us stream per call, "
+        f"prepared {ph} / {ps}")
 
     # the same sizes cold: call k uses the (k mod sets)-th disjoint slice of
     # the prefill buffers, at least 1 GiB in all (four times the 256 MiB

@@ -287,3 +287,104 @@ def test_launch_shape_roundtrip_and_validation():
     assert L.ar_set_launch_shape(0, 64, 1, 2, 1, 0) == tar.AR_ERR_INVALID
     assert L.ar_set_launch_shape(0, 64, 1, 1, 1, 65) == tar.AR_ERR_INVALID
     assert L.ar_get_launch_shape(0, None, None, None, None, None) == tar.AR_ERR_INVALID
+
+
+class _FakeDevTensor:
+    """Stands in for a device tensor in the binding's checks (no GPU here)."""
+
+    is_cuda = True
+
+    def __init__(self, ptr: int, n: int, elem_size: int = 2):
+        self._ptr, self._n, self._es = ptr, n, elem_size
+
+    def is_contiguous(self):
+        return True
+
+    def element_size(self):
+        return self._es
+
+    def numel(self):
+        return self._n
+
+    def data_ptr(self):
+        return self._ptr
+
+
+def test_prepare_marshals_once_and_calls_later():
+    import weakref
+
+    n = 4096
+    ins = [_FakeDevTensor(0x10000000 + i * 0x100000, n) for i in range(8)]
+    outs = [_FakeDevTensor(0x20000000 + i * 0x100000, n) for i in range(8)]
+    outs[5] = _FakeDevTensor(0x20000000 + 5 * 0x100000 + 2, n)          # not 16-byte aligned
+    probe = weakref.ref(outs[5])
+    h = tar.prepare(tar.ar_reduce_2stage, ins, outs, stream=0)      # would raise here if it made the call
+    assert isinstance(h, tar.Prepared) and h.name == "ar_reduce_2stage"
+    assert getattr(tar._tls, "capture", None) is None
+    for _ in range(2):
+        with pytest.raises(tar.ARError) as ei:
+            h()
+        assert ei.value.code == tar.AR_ERR_ALIGN
+    del outs
+    assert probe() is not None                     # the handle keeps its buffers alive
+    del h, ei                                      # (the traceback refers to the handle too)
+    assert probe() is None
+
+
+def test_prepare_validates_like_the_wrapper():
+    ins = [_FakeDevTensor(0x10000000 + i * 0x100000, 100) for i in range(8)]
+    outs = [_FakeDevTensor(0x20000000 + i * 0x100000, 99) for i in range(8)]
+    with pytest.raises(ValueError, match="outs"):
+        tar.prepare(tar.ar_reduce_2stage, ins, outs, stream=0)
+    assert getattr(tar._tls, "capture", None) is None
+    with pytest.raises(ValueError, match="one output per rank"):
+        tar.prepare(tar.ar_reduce_2stage, ins, ins[:7], stream=0)
+
+
+def test_prepare_takes_device_calls_only():
+    before = tar.ar_get_launch_shape(tar.AR_KERNEL_ONESHOT)
+    with pytest.raises(ValueError, match="device call"):
+        tar.prepare(tar.ar_set_launch_shape, tar.AR_KERNEL_ONESHOT, 64, 1, 0, 0, 0)
+    assert tar.ar_get_launch_shape(tar.AR_KERNEL_ONESHOT) == before
+    with pytest.raises(ValueError, match="device call"):
+        tar.prepare(print, "x")
+
+
+def test_prepare_every_device_call():
+    """Each device call of the binding prepares (its marshalled arguments
+    match the C signature's count and types) and its handle reaches the C
+    validation, which rejects the misaligned stand-in buffers."""
+    base = [0x30000000]
+
+    def t(n, es=2):
+        base[0] += 0x1000000
+        return _FakeDevTensor(base[0] + 2, n, es)             # every buffer misaligned
+
+    P, n, rows, hidden = 8, 4096, 4, 1024
+    ins, outs = [t(n) for _ in range(P)], [t(n) for _ in range(P)]
+    words, wout = [t(n // 2, 8) for _ in range(P)], [t(n // 2, 8) for _ in range(P)]
+    err, x = t(2, 8), t(n)
+    codes, scales = [t(n, 1) for _ in range(P)], [t(tar.fp8_scale_count(n), 1) for _ in range(P)]
+    nch = tar.ubatch_chunk_count(rows, hidden)
+    calls = [
+        (tar.ar_reduce_oneshot, (ins, outs[0]), {"stream": 0}),
+        (tar.ar_reduce_2stage, (ins, outs), {"stream": 0}),
+        (tar.ar_reduce_2stage, (ins, outs), {"scratch": t(n), "stream": 0}),
+        (tar.ar_reduce_2stage_static, (ins, outs), {"stream": 0}),
+        (tar.ar_pack_fused, (x, words[0], 1), {"stream": 0}),
+        (tar.ar_unpack_fused, (words[0], x, 1, err), {"stream": 0}),
+        (tar.ar_unpack_fused_wait, (words[0], x, 1, err), {"stream": 0}),
+        (tar.ar_rd_schedule, (words, wout, 1, err), {"stream": 0}),
+        (tar.ar_reduce_ubatch, (ins, outs, rows, hidden), {"streams": [0, 0]}),
+        (tar.ar_reduce_ubatch_flags, (ins, outs, rows, hidden, t(nch, 4), t(nch, 4), 1), {"streams": [0, 0]}),
+        (tar.ar_quantize_fp8, (ins, codes, scales), {"stream": 0}),
+        (tar.ar_reduce_fp8, (codes, scales, outs), {"stream": 0}),
+        (tar.ar_err_init, (err,), {"stream": 0}),
+    ]
+    assert {c[0] for c in calls} == tar._PREPARABLE
+    for func, a, k in calls:
+        h = tar.prepare(func, *a, **k)
+        assert h.name == func.__name__
+        with pytest.raises(tar.ARError) as ei:
+            h()
+        assert ei.value.code in (tar.AR_ERR_ALIGN, tar.AR_ERR_INVALID), func.__name__

@@ -186,6 +186,68 @@ def test_small_2stage_buffer_offsets():
         torch.cuda.empty_cache()
 
 
+def test_prepared_calls():
+    """Every hot-path call prepared once (tar.prepare) and then called on two
+    input sets written into the same tensors, one handle on a side stream:
+    each result matches the oracle, so a handle reuses its pointers and reads
+    the buffers' current contents."""
+    P, n = 8, 4 * 8192 + 13
+    n2 = n - 1                                   # payload path: an even element count
+    ins = [empty16(n) for _ in range(P)]
+    bufs = [empty16(n) for _ in range(P)]
+    out1, outs, outs2, scr = empty16(n), [empty16(n) for _ in range(P)], [empty16(n) for _ in range(P)], empty16(n)
+    words = [torch.empty(n2 // 2, dtype=torch.int64, device=DEV) for _ in range(P)]
+    rdo = [torch.empty_like(w) for w in words]
+    x3, err = empty16(n2), torch.empty(2, dtype=torch.int64, device=DEV)
+    codes = [torch.empty(n, dtype=torch.uint8, device=DEV) for _ in range(P)]
+    scales = [torch.empty(tar.fp8_scale_count(n), dtype=torch.uint8, device=DEV) for _ in range(P)]
+    side = torch.cuda.Stream()
+    h = {"oneshot": tar.prepare(tar.ar_reduce_oneshot, ins, out1),
+         "fused": tar.prepare(tar.ar_reduce_2stage, ins, outs, stream=side),
+         "staged": tar.prepare(tar.ar_reduce_2stage, ins, outs2, scratch=scr),
+         "inplace": tar.prepare(tar.ar_reduce_2stage, bufs, bufs),
+         "err": tar.prepare(tar.ar_err_init, err),
+         "pack": [tar.prepare(tar.ar_pack_fused, ins[r], words[r], 9, n=n2) for r in range(P)],
+         "rd": tar.prepare(tar.ar_rd_schedule, words, rdo, 9, err),
+         "unpack": tar.prepare(tar.ar_unpack_fused, rdo[6], x3, 12, err, n=n2),
+         "quant": tar.prepare(tar.ar_quantize_fp8, ins, codes, scales),
+         "fp8": tar.prepare(tar.ar_reduce_fp8, codes, scales, [out1])}
+    for tag in (0, 1):
+        xs = synth.rank_buffers("normal", P, n, 31, tag)
+        ref = oracle.reduce_seq(xs)
+        for t, b, x in zip(ins, bufs, xs):
+            t.copy_(up16(x))
+            b.copy_(up16(x))
+        torch.cuda.synchronize()
+        note(f"prepared calls, input set {tag}")
+        h["oneshot"]()
+        h["staged"]()
+        h["inplace"]()
+        side.wait_stream(torch.cuda.current_stream())
+        h["fused"]()
+        torch.cuda.current_stream().wait_stream(side)
+        h["err"]()
+        for hp in h["pack"]:
+            hp()
+        h["rd"]()
+        h["unpack"]()
+        torch.cuda.synchronize()
+        check_full(out1, ref, f"prepared oneshot, set {tag}")
+        for r in range(P):
+            check_full(outs[r], ref, f"prepared fused, set {tag}, rank {r}")
+            check_full(outs2[r], ref, f"prepared staged, set {tag}, rank {r}")
+            check_full(bufs[r], ref, f"prepared in place, set {tag}, rank {r}")
+        o_words, _ = oracle.rd([oracle.pack(v[:n2], 9) for v in xs], 9)
+        want, _ = oracle.unpack(o_words[6], 12)
+        check_full(x3, want, f"prepared pack/RD/unpack, set {tag}")
+        assert err_host(err)[0] == 0
+        h["quant"]()
+        h["fp8"]()
+        torch.cuda.synchronize()
+        q = [oracle.quant_fp8(v) for v in xs]
+        check_full(out1, oracle.reduce_fp8([c for c, _ in q], [s_ for _, s_ in q]), f"prepared fp8, set {tag}")
+
+
 def test_canaries_untouched():
     """Outputs carved out of larger buffers: the guard bytes around them keep
     their pattern, so no kernel writes outside [0, n)."""
