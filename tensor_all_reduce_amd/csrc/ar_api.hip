@@ -55,7 +55,7 @@ constexpr ar::Shape kDefaultShape[] = {
     {256, 1, 1, 1, 6, 0},   // fp8 reduce, P code streams -> 1 output (vec: 16-byte output groups per lane)
     {256, 1, 1, 3, 3, 0},   // fp8 reduce, P code streams -> P outputs
     {128, 1, 0, 2, 0, 0},   // one-shot, n <= AR_SMALL_ELEMS: uncapped, plain loads, SC1 stores
-    {128, 1, 0, 2, 0, 0},   // fused two-stage, n <= AR_SMALL_ELEMS
+    {64, 1, 0, 2, 0, 0},    // fused two-stage, n <= AR_SMALL_ELEMS (its compact kernel takes buffer offsets)
     {64, 1, 0, 2, 0, 0},    // fused recursive doubling, n <= AR_SMALL_ELEMS
     {64, 1, 0, 0, 0, 0},    // staged RD step, n <= AR_SMALL_ELEMS: plain stores keep the mailbox on chip
     {256, 1, 0, 3, 0, 0},   // pack, n <= AR_SMALL_ELEMS: plain loads, uncapped, SC1 stores
