@@ -847,6 +847,49 @@ def test_graph_capture_replays():
         check_full(scratch_out, oracle.reduce_seq(xs[::-1]), "eager between replays")
 
 
+def test_graph_capture_prepared_calls():
+    """Prepared handles (tar.prepare, stream fixed to the capture stream) for
+    the decode-size one-shot, fused two-stage with separate outputs and in
+    place, captured in one HIP graph; replayed with fresh inputs written into
+    the same buffers and eager wrapper calls between replays, every replay
+    checked against the oracle."""
+    P, n = 8, 16 * HIDDEN + 5
+    ins, bufs = [empty16(n) for _ in range(P)], [empty16(n) for _ in range(P)]
+    out1, outs = empty16(n), [empty16(n) for _ in range(P)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    hs = [tar.prepare(tar.ar_reduce_oneshot, ins, out1, stream=side),
+          tar.prepare(tar.ar_reduce_2stage, ins, outs, stream=side),
+          tar.prepare(tar.ar_reduce_2stage, bufs, bufs, stream=side)]
+    g = torch.cuda.CUDAGraph()
+    note("graph capture of prepared calls")
+    with torch.cuda.stream(side):
+        for h in hs:                             # the library's one-time initialisation, outside the capture
+            h()
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for h in hs:
+                h()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        xs = synth.rank_buffers("normal", P, n, 61, rep)
+        for t, b, x in zip(ins, bufs, xs):
+            t.copy_(up16(x))
+            b.copy_(up16(x))
+        between = empty16(n)
+        tar.ar_reduce_2stage(ins[::-1], [between] + [empty16(n) for _ in range(P - 1)])
+        torch.cuda.synchronize()
+        note(f"prepared graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.reduce_seq(xs)
+        check_full(out1, ref, f"prepared graph replay {rep} oneshot")
+        for r in range(P):
+            check_full(outs[r], ref, f"prepared graph replay {rep} 2stage rank {r}")
+            check_full(bufs[r], ref, f"prepared graph replay {rep} in place rank {r}")
+        check_full(between, oracle.reduce_seq(xs[::-1]), "eager between replays")
+
+
 def test_graph_capture_replays_other_calls():
     """The remaining entry points captured in one HIP graph: the staged
     two-stage (caller scratch, and the library's static scratch -- the
