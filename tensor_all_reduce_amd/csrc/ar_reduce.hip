@@ -24,6 +24,7 @@
 // 20% slower.  Workgroups per CU are capped per kernel (see Shape).
 #include "ar_device.hpp"
 #include "ar_internal.hpp"
+#include "ar_offsets.hpp"
 
 namespace ar {
 
@@ -195,17 +196,9 @@ __global__ __launch_bounds__(BLOCK) void k_2stage_small_inplace(OutPtrs io, size
   reduce_tile<P, P, 1, NTL, SP, false>(in, io, b0, b1, BLOCK);
 }
 
-// Fused two-stage for small messages with separate outputs: the 2P - 1
-// buffers other than ins[0] are passed as signed 32-bit offsets from it, in
-// units of 2^shift bytes (the host picks the unit and checks that every
-// offset fits), so the argument segment is 80 bytes instead of 2P pointers
-// and n (136 bytes at P = 8, over HIP's fast-enqueue size).
-struct PtrOffsets {
-  const char* base;                     // ins[0]
-  int32_t off[2 * AR_MAX_RANKS - 1];    // ins[1..P-1], then outs[0..P-1], from base, in units of 1 << shift bytes
-  uint32_t shift;                       // fills the padding before n: the segment stays at 80 bytes
-};
-
+// Fused two-stage for small messages with separate outputs: ins[0] and the
+// other 2P - 1 buffers as 32-bit offsets from it (PtrOffsets, built on the
+// host by pack_offsets), an 80-byte argument segment instead of 136 bytes.
 template <int P, int BLOCK, bool NTL, int SP>
 __global__ __launch_bounds__(BLOCK) void k_2stage_small_offs(PtrOffsets po, size_t n) {
   constexpr size_t span = (size_t)BLOCK * 8;
@@ -213,12 +206,11 @@ __global__ __launch_bounds__(BLOCK) void k_2stage_small_offs(PtrOffsets po, size
   const size_t b1 = b0 + span < n ? b0 + span : n;
   InPtrs in{};
   OutPtrs out{};
-  const int64_t unit = (int64_t)1 << po.shift;
   in.p[0] = po.base;
 #pragma unroll
-  for (int p = 1; p < P; ++p) in.p[p] = po.base + (int64_t)po.off[p - 1] * unit;
+  for (int p = 1; p < P; ++p) in.p[p] = offset_address(po, p - 1);
 #pragma unroll
-  for (int o = 0; o < P; ++o) out.p[o] = const_cast<char*>(po.base + (int64_t)po.off[P - 1 + o] * unit);
+  for (int o = 0; o < P; ++o) out.p[o] = const_cast<char*>(offset_address(po, P - 1 + o));
   reduce_tile<P, P, 1, NTL, SP, false>(in, out, b0, b1, BLOCK);
 }
 
@@ -393,33 +385,6 @@ hipError_t offs_small_b(const Shape& sh, hipStream_t st, const PtrOffsets& po, s
   });
 }
 
-// Every buffer of the call as a signed 32-bit count of units from ins[0],
-// the unit being the largest power of two (at most 2^30 bytes) that divides
-// every difference: with 16-byte aligned buffers the reach is at least
-// +-32 GiB, and with 512-byte aligned allocations +-1 TiB.  False when some
-// buffer lies farther away.
-template <int P>
-bool pack_offsets(const InPtrs& in, const OutPtrs& out, PtrOffsets* po) {
-  const intptr_t b = reinterpret_cast<intptr_t>(in.p[0]);
-  intptr_t d[2 * AR_MAX_RANKS - 1] = {};
-  uintptr_t bits = 0;
-  for (int i = 1; i < 2 * P; ++i) {
-    const intptr_t a = i < P ? reinterpret_cast<intptr_t>(in.p[i]) : reinterpret_cast<intptr_t>(out.p[i - P]);
-    d[i - 1] = a - b;  // buffers of one device: the difference cannot overflow
-    bits |= static_cast<uintptr_t>(d[i - 1]);
-  }
-  unsigned shift = 0;
-  while (shift < 30 && ((bits >> shift) & 1u) == 0) ++shift;
-  po->base = static_cast<const char*>(in.p[0]);
-  po->shift = shift;
-  for (int i = 0; i < 2 * AR_MAX_RANKS - 1; ++i) {
-    const intptr_t q = d[i] / ((intptr_t)1 << shift);  // exact: 2^shift divides every difference
-    if (q < (intptr_t)INT32_MIN || q > (intptr_t)INT32_MAX) return false;
-    po->off[i] = (int32_t)q;
-  }
-  return true;
-}
-
 // Fused two-stage for small messages, with one group per lane: in place
 // (every output its own input) the in-place kind's shape and its compact
 // kernel; with separate outputs the small kind's shape and, when every
@@ -436,7 +401,12 @@ hipError_t fused_small_p(const Launch& L, const InPtrs& in, const OutPtrs& out, 
     if (sh.block == 256) return inplace_small_b<P, 256>(sh, L.stream, out, n);
   }
   PtrOffsets po;
-  if (!inplace && sh.vec == 1 && pack_offsets<P>(in, out, &po)) {
+  const void* ptrs[2 * AR_MAX_RANKS];
+  for (int p = 0; p < P; ++p) {
+    ptrs[p] = in.p[p];
+    ptrs[P + p] = out.p[p];
+  }
+  if (!inplace && sh.vec == 1 && pack_offsets(ptrs, 2 * P, &po)) {
     if (sh.block == 64) return offs_small_b<P, 64>(sh, L.stream, po, n);
     if (sh.block == 128) return offs_small_b<P, 128>(sh, L.stream, po, n);
     if (sh.block == 256) return offs_small_b<P, 256>(sh, L.stream, po, n);
