@@ -812,20 +812,18 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
         xo = [o[:m] for o in outs]
         key = f"{2 * m // 1024}KiB"
         glat[key] = {}
-        for name in ("oneshot", "2stage_fused"):
+        xb = [x.clone() for x in xi]   # the in-place call's buffers (only timed: their values grow)
+        calls = {"oneshot": lambda: tar.ar_reduce_oneshot(xi, xo[0], stream=side),
+                 "2stage_fused": lambda: tar.ar_reduce_2stage(xi, xo, stream=side),
+                 "2stage_fused_inplace": lambda: tar.ar_reduce_2stage(xb, xb, stream=side)}
+        for name, call in calls.items():
             g = torch.cuda.CUDAGraph()
             with torch.cuda.stream(side):
-                if name == "oneshot":
-                    tar.ar_reduce_oneshot(xi, xo[0], stream=side)
-                else:
-                    tar.ar_reduce_2stage(xi, xo, stream=side)
+                call()
                 side.synchronize()
                 with torch.cuda.graph(g, stream=side):
                     for _ in range(100):
-                        if name == "oneshot":
-                            tar.ar_reduce_oneshot(xi, xo[0], stream=side)
-                        else:
-                            tar.ar_reduce_2stage(xi, xo, stream=side)
+                        call()
             torch.cuda.synchronize()
             for _ in range(3):
                 g.replay()
@@ -838,6 +836,7 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
             torch.cuda.synchronize()
             glat[key][name] = {"us_per_call": round(e0.elapsed_time(e1) * 1e3 / 2000, 2)}
             del g
+        del xb
     # the floor of one graph node on this machine: the same capture of a
     # one-workgroup kernel (torch's fill of 64 floats)
     tiny = torch.zeros(64, dtype=torch.float32, device=dev)
