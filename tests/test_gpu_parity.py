@@ -151,6 +151,35 @@ def test_in_place():
     check_full(ins[3], ref, "in-place oneshot")
 
 
+@pytest.mark.parametrize("n", [3 * 8192 + 5, tar.AR_SMALL_ELEMS + 1001])
+def test_mixed_aliasing(n):
+    """Outputs that are partly the inputs themselves: ranks 0, 2, 4, 6 write
+    into their own input, rank 1 into rank 5's input, ranks 3, 5, 7 into
+    separate buffers (pairwise disjoint outputs, each equal to an input or
+    apart from all).  Fused (the compact offset kernel below
+    AR_SMALL_ELEMS, k_reduce above), staged and static-scratch two-stage;
+    every output matches the oracle."""
+    P = 8
+    xs = synth.rank_buffers("normal", P, n, 6, n)
+    ref = oracle.reduce_seq(xs)
+    for mode in ("fused", "staged", "static"):
+        if mode == "static" and n > tar.AR_STATIC_SCRATCH_ELEMS:
+            continue
+        ins = [up16(x) for x in xs]
+        sep = {r: empty16(n) for r in (3, 5, 7)}
+        outs = [ins[0], ins[5], ins[2], sep[3], ins[4], sep[5], ins[6], sep[7]]
+        note(f"mixed aliasing n={n} {mode}")
+        if mode == "fused":
+            tar.ar_reduce_2stage(ins, outs)
+        elif mode == "staged":
+            tar.ar_reduce_2stage(ins, outs, scratch=empty16(n))
+        else:
+            tar.ar_reduce_2stage_static(ins, outs)
+        torch.cuda.synchronize()
+        for r, o in enumerate(outs):
+            check_full(o, ref, f"mixed aliasing n={n} {mode}: rank {r}")
+
+
 def test_small_2stage_buffer_offsets():
     """The small fused two-stage with separate outputs passes its buffers to
     the kernel as signed 32-bit offsets from ins[0], in units of the largest
