@@ -380,6 +380,35 @@ def test_pack_rd_unpack(P, n, seq0):
         assert err_host(err2) == (int(oe[0]), int(oe[1]))
 
 
+@pytest.mark.parametrize("P,n", [(2, 24590), (4, 24590), (8, 24590), (8, 128 * HIDDEN)])
+def test_rd_outputs_alias_inputs(P, n):
+    """Recursive doubling with out_words equal to in_words: in place, and
+    permuted (rank r's result in rank P-1-r's input).  Fused R1, staged R1
+    (P = 2 in one launch, no mailbox) and fused R2; every output word and
+    the error record match the oracle.  n/2 is odd for the small sizes, so
+    the tail word is handled too."""
+    seq0 = 77
+    xs, owords = _rd_case(P, n, seq0, cfg=34)
+    for flags, carry in ((0, False), (tar.AR_RD_STAGED, False), (tar.AR_RD_FP32_CARRY, True)):
+        ref_w, ref_e = oracle.rd(owords, seq0, carry)
+        for layout in ("in place", "permuted"):
+            words = [up64(w) for w in owords]
+            out = words if layout == "in place" else words[::-1]
+            mb = None
+            if flags & tar.AR_RD_STAGED and P > 2:
+                mb = torch.empty(tar.rd_mailbox_words(P, n), dtype=torch.int64, device=DEV)
+            err = new_err()
+            note(f"rd aliasing P={P} n={n} flags={flags} {layout}")
+            tar.ar_rd_schedule(words, out, seq0, err, mailbox=mb, flags=flags)
+            torch.cuda.synchronize()
+            assert err_host(err) == (int(ref_e[0]), int(ref_e[1])) == (0, 2 ** 64 - 1)
+            for r in range(P):
+                got = down64(out[r])
+                bad = np.nonzero(got != ref_w[r])[0]
+                assert bad.size == 0, (f"{layout} flags={flags} rank {r}: word {bad[0]} "
+                                       f"{got[bad[0]]:#x} vs {ref_w[r][bad[0]]:#x}")
+
+
 @pytest.mark.parametrize("staged", [False, True])
 def test_rd_error_counts(staged):
     """Host-forced faults: corrupted sequence numbers in chosen words of
