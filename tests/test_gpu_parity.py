@@ -537,8 +537,12 @@ def test_ubatch_bounded(shape, chunk_bytes):
     check_full(one[0], ref, f"ubatch bounded {shape} oneshot")
 
 
-def test_ubatch_bounded_in_place():
-    """Bounded mode with every output equal to its input."""
+@pytest.mark.parametrize("mode", ["flat", "bounded", "flags", "oneshot", "mixed"])
+def test_ubatch_outputs_alias_inputs(mode):
+    """The ubatch reduce with outputs that are the inputs: every output its
+    own input on the flat grid, the bounded grid and with completion flags;
+    the one-shot variant writing into one rank's input; and outputs that are
+    partly the inputs (own and another rank's) beside separate buffers."""
     P, rows, hidden = 4, 96, 4096
     n = rows * hidden
     xs = synth.rank_buffers("normal", P, n, 5, 3)
@@ -547,11 +551,33 @@ def test_ubatch_bounded_in_place():
     s = [torch.cuda.Stream(), torch.cuda.Stream()]
     for st in s:
         st.wait_stream(torch.cuda.current_stream())
-    note("ubatch bounded in place")
-    tar.ar_reduce_ubatch(bufs, bufs, rows, hidden, 2, None, 1 << 16, tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED, s)
+    note(f"ubatch outputs alias inputs: {mode}")
+    if mode == "flat":
+        outs = bufs
+        tar.ar_reduce_ubatch(bufs, outs, rows, hidden, 2, None, 1 << 16, tar.AR_VARIANT_2STAGE, s)
+    elif mode == "bounded":
+        outs = bufs
+        tar.ar_reduce_ubatch(bufs, outs, rows, hidden, 2, None, 1 << 16,
+                             tar.AR_VARIANT_2STAGE | tar.AR_UBATCH_BOUNDED, s)
+    elif mode == "flags":
+        outs = bufs
+        nf = tar.ubatch_chunk_count(rows, hidden, 2, None, 1 << 16)
+        done = torch.zeros(nf, dtype=torch.int32, device=DEV)
+        tiles = torch.zeros(nf, dtype=torch.int32, device=DEV)
+        torch.cuda.synchronize()
+        tar.ar_reduce_ubatch_flags(bufs, outs, rows, hidden, done, tiles, 3, 2, None, 1 << 16,
+                                   tar.AR_VARIANT_2STAGE, s)
+    elif mode == "oneshot":
+        outs = [bufs[2]]
+        tar.ar_reduce_ubatch(bufs, outs, rows, hidden, 2, None, 1 << 16, tar.AR_VARIANT_ONESHOT, s)
+    else:
+        outs = [bufs[0], bufs[3], empty16(n), empty16(n)]
+        tar.ar_reduce_ubatch(bufs, outs, rows, hidden, 2, [37, 59], 4096 + 16, tar.AR_VARIANT_2STAGE, s)
     torch.cuda.synchronize()
-    for b in bufs:
-        check_full(b, ref, "ubatch bounded in place")
+    for r, o in enumerate(outs):
+        check_full(o, ref, f"ubatch {mode}: output {r}")
+    if mode == "flags":
+        assert np.all(done.cpu().numpy() == 3) and not tiles.cpu().numpy().any()
 
 
 # ------------------------------------------------------------ concurrency
