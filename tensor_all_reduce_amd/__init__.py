@@ -193,8 +193,7 @@ class Prepared:
             raise TypeError(f"{name}: {len(cargs)} arguments for {len(fn.argtypes)} parameters")
         # plain ints become instances of the declared C types now, which
         # ctypes then passes through as they are (about 0.1 us a call)
-        conv = tuple(a if a is None or isinstance(a, (ctypes._SimpleCData, ctypes.Array)) else t(a)
-                     for a, t in zip(cargs, fn.argtypes))
+        conv = tuple(t(a) if isinstance(a, int) else a for a, t in zip(cargs, fn.argtypes))
         self._fn, self._name, self._args, self._refs = fn, name, conv, refs
 
     @property
