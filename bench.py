@@ -611,9 +611,9 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     m = HIDDEN
     xi = [x[:m] for x in ins[:2]]
     xo = [o[:m] for o in outs[:2]]
-    us = blib.arb_stream_us(0, parr(xi), parr(xo), 2, m, None, 5000, sh)
+    us = blib.arb_stream_us(0, parr(xi), parr(xo), 2, m, None, 10000, sh)
     p50, p10, p90 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
-    if blib.arb_wall_us(0, parr(xi), parr(xo), 2, m, None, 2000, sh, ctypes.byref(p50), ctypes.byref(p10),
+    if blib.arb_wall_us(0, parr(xi), parr(xo), 2, m, None, 10000, sh, ctypes.byref(p50), ctypes.byref(p10),
                         ctypes.byref(p90)) != 0:
         raise RuntimeError("arb_wall_us failed")
     lat["P2_16KiB"] = {"oneshot": {"stream_us": round(us, 2), "wall_us_p50": round(p50.value, 2),
@@ -628,9 +628,9 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
         lat[key] = {}
         for which, name, bi, bo in ((0, "oneshot", xi, xo), (1, "2stage_fused", xi, xo),
                                     (1, "2stage_fused_inplace", xb, xb), (2, "2stage_staged", xi, xo)):
-            us = blib.arb_stream_us(which, parr(bi), parr(bo), P, m, sc.data_ptr(), 5000, sh)
+            us = blib.arb_stream_us(which, parr(bi), parr(bo), P, m, sc.data_ptr(), 10000, sh)
             p50, p10, p90 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
-            rc = blib.arb_wall_us(which, parr(bi), parr(bo), P, m, sc.data_ptr(), 2000, sh,
+            rc = blib.arb_wall_us(which, parr(bi), parr(bo), P, m, sc.data_ptr(), 10000, sh,
                                   ctypes.byref(p50), ctypes.byref(p10), ctypes.byref(p90))
             if rc != 0:
                 raise RuntimeError(f"arb_wall_us failed: {rc}")
