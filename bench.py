@@ -705,12 +705,12 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
         f"prepared {ph} / {ps}")
 
     # the same sizes cold: call k uses the (k mod sets)-th disjoint slice of
-    # the prefill buffers, at least 1 GiB in all (four times the 256 MiB
-    # last-level cache), so every call reads and writes HBM
+    # the prefill buffers, at least 64 sets and at least 1 GiB in all (four
+    # times the 256 MiB last-level cache), so every call reads and writes HBM
     cold = {}
     for T in (8, 32, 128):
         m = T * HIDDEN
-        sets = min(n // m, -(-(1 << 30) // (2 * P * 2 * m)))
+        sets = min(n // m, max(64, -(-(1 << 30) // (2 * P * 2 * m))))
         key = f"{2 * m // 1024}KiB"
         cold[key] = {"sets": sets}
         for which, name in ((0, "oneshot"), (1, "2stage_fused")):
