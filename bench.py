@@ -528,17 +528,20 @@ def extras(args, tar, blib, torch, np, dev, main_s, ins, outs, out1, e16, s0, s1
     res["copy_8to8_shape"] = shape8
     # the one-shot row's pattern: eight 256 MiB buffers read, their XOR
     # written to one output (the one-shot's tiling, no float arithmetic),
-    # best over store kind and the workgroups-per-CU cap
+    # best over store kind and the workgroups-per-CU cap.  The output rotates
+    # over the P output buffers, as the one-shot gate's does: rewriting one
+    # output call after call would leave part of it in the 256 MiB last-level
+    # cache, a write-back the step's one-shot (behind five other rows) pays
     best1, shape1 = 0.0, None
     for nts in (0, 1):
         for wg in (0, 4, 8, 12, 16):
-            for _ in range(2):
-                if blib.arb_gather_xor(parr(ins), P, out1.data_ptr(), 2 * n, nts, wg, sh) != 0:
+            for i in range(2):
+                if blib.arb_gather_xor(parr(ins), P, outs[i % P].data_ptr(), 2 * n, nts, wg, sh) != 0:
                     raise RuntimeError("arb_gather_xor failed")
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(main_s)
-            for _ in range(8):
-                blib.arb_gather_xor(parr(ins), P, out1.data_ptr(), 2 * n, nts, wg, sh)
+            for i in range(8):
+                blib.arb_gather_xor(parr(ins), P, outs[(i + 2) % P].data_ptr(), 2 * n, nts, wg, sh)
             e1.record(main_s)
             torch.cuda.synchronize()
             gbps = (P + 1) * 2 * n * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9
@@ -1052,8 +1055,12 @@ def ab_report(args, tar, blib, torch, dev, main_s, ins, outs, out1, uin, ubo, s0
         if blib.arb_copy_multi(parr(ins), parr(outs), P, B, sh[0], sh[1], main_s.cuda_stream) != 0:
             raise RuntimeError("arb_copy_multi failed")
 
-    def gather(sh):
-        if blib.arb_gather_xor(parr(ins), P, out1.data_ptr(), B, sh[0], sh[1], main_s.cuda_stream) != 0:
+    gturn = [0]
+
+    def gather(sh):   # the output rotates over the P outputs, as the one-shot candidates' do
+        gturn[0] += 1
+        if blib.arb_gather_xor(parr(ins), P, outs[gturn[0] % P].data_ptr(), B, sh[0], sh[1],
+                               main_s.cuda_stream) != 0:
             raise RuntimeError("arb_gather_xor failed")
 
     h = n5 // 2
