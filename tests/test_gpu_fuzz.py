@@ -9,7 +9,8 @@ in place), staged and static-scratch two-stage, and the ubatch reduce on the
 flat or the bounded grid; the payload family ends with the plain or the
 waiting unpack.  The
 seed of a failing case is in the assertion message.  AR_FUZZ_SEEDS=<k> in
-the environment runs k seeds per family.
+the environment runs k seeds per family, and AR_FUZZ_SEED0=<s> starts them
+at s instead of 0 (a soak over cases the default run never draws).
 """
 import os
 
@@ -25,9 +26,11 @@ from gpu_util import DEV, note, up16, down16, up64, down64, empty16, new_err, er
 pytestmark = pytest.mark.gpu
 
 # seeds per family; AR_FUZZ_SEEDS=<k> runs k seeds of every family instead
-# (a longer soak), starting where the default range starts
+# (a longer soak), starting at AR_FUZZ_SEED0 (default 0, where the default
+# range starts)
 _K = os.environ.get("AR_FUZZ_SEEDS")
 N_REDUCE, N_PAYLOAD, N_FP8 = (int(_K),) * 3 if _K else (80, 80, 60)
+S0 = int(os.environ.get("AR_FUZZ_SEED0", "0"))
 
 SPECIALS = np.array([0x7FC0, 0xFFC1, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x807F, 0x7F7F, 0xFF7F, 0x0080],
                     dtype=np.uint16)
@@ -57,7 +60,7 @@ def eq(got, want, msg):
     assert bad.size == 0, f"{msg}: {bad.size} mismatches, first at {bad[0]}: got {got[bad[0]]:#x} want {want[bad[0]]:#x}"
 
 
-@pytest.mark.parametrize("seed", range(N_REDUCE))
+@pytest.mark.parametrize("seed", range(S0, S0 + N_REDUCE))
 def test_fuzz_reduce_family(seed):
     rng = np.random.default_rng([991, seed])
     P = int(rng.integers(1, 9))
@@ -102,7 +105,7 @@ def test_fuzz_reduce_family(seed):
             eq(down16(o), ref, f"{tag} ubatch")
 
 
-@pytest.mark.parametrize("seed", range(N_PAYLOAD))
+@pytest.mark.parametrize("seed", range(S0, S0 + N_PAYLOAD))
 def test_fuzz_payload_family(seed):
     rng = np.random.default_rng([992, seed])
     P = int(rng.choice([2, 4, 8]))
@@ -140,7 +143,7 @@ def test_fuzz_payload_family(seed):
     eq(down16(out)[:n], oracle.unpack(want[P - 1], (seq0 + L) & 0xFFFFFFFF)[0], f"{tag} unpack")
 
 
-@pytest.mark.parametrize("seed", range(N_FP8))
+@pytest.mark.parametrize("seed", range(S0, S0 + N_FP8))
 def test_fuzz_fp8_family(seed):
     rng = np.random.default_rng([993, seed])
     P = int(rng.integers(1, 9))
