@@ -6,6 +6,10 @@ pointers and element counts, torch streams become ``hipStream_t`` handles.
 All arithmetic runs in the HIP kernels of ``libarcore.so``; there is no
 fallback of any kind.  If the library is missing, every call raises.
 
+``prepare(func, *args, **kwargs)`` runs a device call's checks and
+marshalling once and returns a handle that makes the same C-ABI call each
+time it is called: for loops that pass the same buffers on every step.
+
 bf16 buffers may be passed as ``torch.bfloat16`` or ``torch.int16`` /
 ``torch.uint16`` tensors (only the 16-bit patterns matter); payload words as
 ``torch.int64`` / ``torch.uint64`` tensors; error records as a 2-element
